@@ -1,0 +1,135 @@
+"""Acceptance of one speculative window.
+
+Greedy chain: [SD] "Speculative decoding on RDNA", §02: accept the longest
+prefix of drafts equal to the target's argmax; §01 (figure "one speculative
+window" and the text under it): the window then emits the target's own
+choice at the first disagreement, or a bonus token after the last row when
+every draft is accepted, so it always emits at least one token.
+
+Sampled chain: [SD] §03 "Sampled requests: rejection sampling", steps 1-4:
+draft x ~ q; accept with probability min(1, p(x)/q(x)); on rejection emit
+a draw from the residual (p - q)+ renormalised and end the window; if all
+drafts are accepted, draw the bonus from p at the last row.  With a
+point-mass draft q = delta(c) ([SD] §06) the same rule accepts with
+probability p(c) and otherwise draws from p without c.
+
+Greedy tree: [TREE] "Spend the budget on a tree, not a longer guess":
+several continuations sharing a prefix are verified in one pass and the
+longest branch the target agrees with is accepted.
+
+Readings taken:
+  * the accept test is u0 * q(x) < p(x) with u0 in [0, 1), evaluated in
+    fp64 from fp32 probabilities (the product of two fp32 values is exact
+    in fp64), which is acceptance with probability min(1, p/q);
+  * p(x) and q(x) are the total probability the distribution gives token
+    x; a token outside the support has probability 0, so a draft outside
+    p's support is always rejected;
+  * the residual is r_j = max(0, p_j - q(t_j)) over p's support in pool
+    order, in fp64; if its total is 0 the replacement is drawn from p;
+  * row i uses the uniforms u[i][0] (accept test) and u[i][1]
+    (replacement or bonus draw); the bonus uses u[k][1];
+  * argmax ties go to the lowest token id (the pool order), so a row's
+    argmax is the first entry of its pool;
+  * in a tree, row 0 is the root and row 1 + j is node j; the accepted
+    branch is the longest agreeing one, the lowest-numbered end node on a
+    tie.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .policy import draw, draw_weights
+
+
+def accept_greedy_chain(target_argmax, drafts) -> list[int]:
+    out = []
+    k = len(drafts)
+    for i in range(k):
+        d = int(drafts[i])
+        if d == int(target_argmax[i]):
+            out.append(d)
+        else:
+            out.append(int(target_argmax[i]))
+            return out
+    out.append(int(target_argmax[k]))
+    return out
+
+
+def accept_greedy_tree(target_argmax, tokens, parent) -> list[int]:
+    """target_argmax [n+1] (row 0 = root), tokens [n], parent [n] (-1 = root).
+
+    A node agrees with the target when its token equals the argmax of its
+    parent's row and its parent agrees (the root always does).  The
+    accepted branch ends at the deepest agreeing node (lowest node number
+    on a tie); the window emits that branch's tokens, then the argmax of
+    its last row.  ``parent[j] < j`` is required.
+    """
+    n = len(tokens)
+    agrees = [False] * n
+    depth = [0] * n
+    for j in range(n):
+        pj = int(parent[j])
+        parent_row = 0 if pj < 0 else pj + 1
+        parent_ok = True if pj < 0 else agrees[pj]
+        agrees[j] = parent_ok and int(tokens[j]) == int(target_argmax[parent_row])
+        depth[j] = 1 if pj < 0 else depth[pj] + 1
+    best = -1
+    for j in range(n):
+        if agrees[j] and (best < 0 or depth[j] > depth[best]):
+            best = j
+    path = []
+    j = best
+    while j >= 0:
+        path.append(j)
+        j = int(parent[j])
+    path.reverse()
+    out = [int(tokens[j]) for j in path]
+    out.append(int(target_argmax[0 if best < 0 else best + 1]))
+    return out
+
+
+def prob_of(dist, x: int) -> float:
+    """Total probability of token x under a sparse distribution (ids, probs)."""
+    ids, probs = dist
+    s = 0.0
+    for t, p in zip(ids, probs):
+        if int(t) == x:
+            s += float(p)
+    return s
+
+
+def residual_weights(p, q) -> list[float]:
+    """(p - q)+ over p's support, in p's order (fp64)."""
+    ids, probs = p
+    return [max(0.0, float(pj) - prob_of(q, int(t))) for t, pj in zip(ids, probs)]
+
+
+def accept_sampled(p_rows, q_rows, drafts, u) -> list[int]:
+    """One sampled window.
+
+    p_rows: k+1 distributions (ids, fp32 probs) for verify rows 0..k;
+    q_rows: k draft distributions; drafts: k token ids; u: [k+1][2] fp32.
+    """
+    out = []
+    k = len(drafts)
+    for i in range(k):
+        x = int(drafts[i])
+        px = prob_of(p_rows[i], x)
+        qx = prob_of(q_rows[i], x)
+        if float(np.float32(u[i][0])) * qx < px:
+            out.append(x)
+            continue
+        r = residual_weights(p_rows[i], q_rows[i])
+        z = 0.0
+        for w in r:
+            z += w
+        ids = p_rows[i][0]
+        if z > 0.0:
+            out.append(int(ids[draw_weights(r, u[i][1])]))
+        else:
+            out.append(int(ids[draw(p_rows[i][1], u[i][1])]))
+        return out
+    ids, probs = p_rows[k]
+    out.append(int(ids[draw(probs, u[k][1])]))
+    return out

@@ -1,0 +1,244 @@
+"""Pins for the acceptance oracle.
+
+* the worked example of section 01 of "Speculative decoding on RDNA"
+  (golden fixture), and the "at least one token" invariant stated there;
+* an exact enumeration over a grid of uniforms showing the emitted token
+  follows p (section 03: the emitted tokens follow p exactly);
+* the point-mass draft of section 06 (accept with probability p(c), else a
+  draw from p without c);
+* the 200,000-trial chi-square test of section 03, with its control: the
+  same test must fail when the rejection replacement is drawn from p
+  instead of the residual (the mistake is planted in the oracle here, on
+  the CPU);
+* the token tree against a brute-force enumeration of root paths.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle.accept as acc
+from oracle.accept import accept_greedy_chain, accept_greedy_tree, accept_sampled
+from oracle.policy import draw, policy_row
+from stats import chi2_pvalue
+from synth import chain_greedy_case, correlated_logits, logits, tree_greedy_case, uniforms
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_worked_example_window():
+    with open(os.path.join(GOLDEN, "worked_example_window.json")) as f:
+        g = json.load(f)
+    v = g["vocab"]
+    drafts = [v[w] for w in g["drafts"]]
+    argmax = [v[w] for w in g["target_argmax"]]
+    out = accept_greedy_chain(argmax, drafts)
+    assert out == [v[w] for w in g["expected_tokens"]]
+    assert len(out) - 1 == g["expected_accepted"]
+
+
+@pytest.mark.parametrize("k,m", [(3, 0), (3, 3), (15, 0), (15, 3), (15, 7), (15, 15)])
+def test_greedy_chain_planted_lengths(k, m):
+    argmax, drafts = chain_greedy_case(100 + m, k, m)
+    out = accept_greedy_chain(argmax, drafts)
+    assert len(out) == m + 1 and 1 <= len(out) <= k + 1
+    assert out[:m] == list(drafts[:m]) and out[m] == int(argmax[m])
+
+
+def all_root_paths(parent):
+    n = len(parent)
+    paths = []
+    for j in range(n):
+        p, node = [], j
+        while node >= 0:
+            p.append(node)
+            node = int(parent[node])
+        paths.append(p[::-1])
+    return paths
+
+
+def brute_force_tree(argmax, tokens, parent):
+    best = []
+    for path in all_root_paths(parent):
+        rows = [0] + [j + 1 for j in path[:-1]]
+        if all(int(tokens[j]) == int(argmax[r]) for j, r in zip(path, rows)):
+            if len(path) > len(best) or (len(path) == len(best) and path[-1] < best[-1]):
+                best = path
+    last_row = 0 if not best else best[-1] + 1
+    return [int(tokens[j]) for j in best] + [int(argmax[last_row])]
+
+
+@pytest.mark.parametrize("branch,length", [(0, 8), (1, 5), (2, 3), (-1, 0), (1, 1), (2, 8)])
+def test_tree_planted(branch, length):
+    parent, tokens, argmax = tree_greedy_case(300 + 7 * branch + length, 3, 8, branch, length)
+    out = accept_greedy_tree(argmax, tokens, parent)
+    assert out == brute_force_tree(argmax, tokens, parent)
+    assert len(out) == length + 1
+
+
+def test_tree_random_small_vocab_against_brute_force():
+    rng = np.random.default_rng(9)
+    for _ in range(300):
+        n = int(rng.integers(1, 12))
+        parent = np.array([-1 if j == 0 else int(rng.integers(-1, j)) for j in range(n)], dtype=np.int32)
+        tokens = rng.integers(0, 3, n).astype(np.int32)
+        argmax = rng.integers(0, 3, n + 1).astype(np.int32)
+        assert accept_greedy_tree(argmax, tokens, parent) == brute_force_tree(argmax, tokens, parent)
+
+
+def test_tree_chain_equals_greedy_chain():
+    rng = np.random.default_rng(5)
+    for _ in range(100):
+        k = int(rng.integers(1, 16))
+        drafts = rng.integers(0, 3, k).astype(np.int32)
+        argmax = rng.integers(0, 3, k + 1).astype(np.int32)
+        parent = np.arange(-1, k - 1, dtype=np.int32)
+        assert accept_greedy_tree(argmax, drafts, parent) == accept_greedy_chain(argmax, drafts)
+
+
+def dist(ids, probs):
+    return (np.array(ids, dtype=np.int32), np.array(probs, dtype=np.float32))
+
+
+def test_sampled_at_least_one_token_and_bonus_only_after_full_accept():
+    rng = np.random.default_rng(2)
+    for _ in range(500):
+        k = int(rng.integers(1, 6))
+        rows = []
+        for _ in range(k + 1):
+            ids = rng.permutation(6)[: int(rng.integers(1, 6))]
+            w = rng.random(len(ids)) + 0.01
+            rows.append(dist(ids, (w / w.sum()).astype(np.float32)))
+        qrows = []
+        for _ in range(k):
+            ids = rng.permutation(6)[: int(rng.integers(1, 6))]
+            w = rng.random(len(ids)) + 0.01
+            qrows.append(dist(ids, (w / w.sum()).astype(np.float32)))
+        drafts = [int(q[0][draw(q[1], rng.random())]) for q in qrows]
+        u = rng.random((k + 1, 2)).astype(np.float32)
+        out = accept_sampled(rows, qrows, drafts, u)
+        assert 1 <= len(out) <= k + 1
+        assert out[:-1] == drafts[: len(out) - 1]
+
+
+def test_crafted_uniforms_force_accept_and_reject():
+    p = dist([1, 2, 3], [0.5, 0.3, 0.2])
+    q = dist([1, 2, 3], [0.2, 0.6, 0.2])
+    bonus = dist([7], [1.0])
+    # u = 0 accepts whenever p(x) > 0
+    assert accept_sampled([p, bonus], [q], [2], [[0.0, 0.0], [0.0, 0.0]]) == [2, 7]
+    # u = 1 - 2^-24 rejects when p(x) < q(x); the residual (p - q)+ is {1: .3} only
+    assert accept_sampled([p, bonus], [q], [2], [[1 - 2**-24, 0.9], [0, 0]]) == [1]
+    # a draft outside p's support is always rejected
+    assert accept_sampled([p, bonus], [dist([9], [1.0])], [9], [[0.0, 0.0], [0, 0]]) == [1]
+    # p == q: never rejected; zero residual falls back to p
+    assert accept_sampled([p, bonus], [p], [3], [[1 - 2**-24, 0.0], [0, 0]]) == [3, 7]
+
+
+def enumerate_emitted(p, q, grid):
+    """P(first emitted token) by exact enumeration over drafts and a uniform grid."""
+    ids_q, probs_q = q
+    prob = {}
+    weight = 1.0 / (len(grid) * len(grid))
+    bonus = dist([-1], [1.0])
+    for x, qx in zip(ids_q, probs_q):
+        for u0 in grid:
+            for u1 in grid:
+                t = accept_sampled([p, bonus], [q], [int(x)], [[u0, u1], [0.0, 0.0]])[0]
+                prob[t] = prob.get(t, 0.0) + float(qx) * weight
+    return prob
+
+
+def test_exact_enumeration_dyadic():
+    # acceptance ratios 1, 1/2, 1, 0 (token 4 is outside p); residual
+    # (3/8, 0, 0, 1/8) over p's support, CDF boundary 3/4: all multiples of 1/32
+    p = dist([0, 1, 2, 3], [0.5, 0.25, 0.125, 0.125])
+    q = dist([0, 1, 2, 4], [0.125, 0.5, 0.125, 0.25])
+    grid = np.arange(32) / 32
+    prob = enumerate_emitted(p, q, grid)
+    assert prob == {0: 0.5, 1: 0.25, 2: 0.125, 3: 0.125}
+
+
+def test_point_mass_draft_closed_form():
+    # q = delta(c): accept with probability p(c), else draw from p without c
+    p = dist([0, 1, 2, 3], [0.5, 0.25, 0.125, 0.125])
+    bonus = dist([-1], [1.0])
+    q = dist([1], [1.0])
+    grid = np.arange(64) / 64
+    accepted = [len(accept_sampled([p, bonus], [q], [1], [[u, 0.0], [0, 0]])) == 2 for u in grid]
+    assert np.mean(accepted) == 0.25
+    # on rejection the replacement never equals c and follows p without c: (2/3, 0, 1/6, 1/6)
+    reps = [accept_sampled([p, bonus], [q], [1], [[0.999, u], [0, 0]])[0] for u in grid]
+    counts = np.bincount(reps, minlength=4) / len(grid)
+    assert counts[1] == 0.0
+    np.testing.assert_allclose(counts, [2 / 3, 0, 1 / 6, 1 / 6], atol=1 / 64)
+    # with c = 0 every boundary is dyadic and the enumeration gives p exactly
+    q0 = dist([0], [1.0])
+    assert enumerate_emitted(p, q0, np.arange(32) / 32) == {0: 0.5, 1: 0.25, 2: 0.125, 3: 0.125}
+
+
+# ---------------------------------------------------------------- chi-square
+
+
+CFG = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
+
+
+def make_case(rho, seed, k=3, vocab=4096):
+    """Fixed p rows (k+1) and q rows (k) over `vocab`, policy applied to the top-64 pool."""
+    from oracle.topk import topk_rows
+
+    pl = logits(seed, (k + 1, vocab))
+    if rho == "point":
+        q_rows = None
+    else:
+        ql = correlated_logits(pl[:k], rho, seed + 1)
+        qv, qi = topk_rows(ql, 64)
+        q_rows = [policy_row(qv[i], qi[i], **CFG) for i in range(k)]
+    pv, pi = topk_rows(pl, 64)
+    p_rows = [policy_row(pv[i], pi[i], **CFG) for i in range(k + 1)]
+    if q_rows is None:  # point-mass drafts: the second most likely target token
+        q_rows = [dist([int(p_rows[i][0][1])], [1.0]) for i in range(k)]
+    return p_rows, q_rows
+
+
+def run_trials(p_rows, q_rows, n, seed):
+    k = len(q_rows)
+    ud = uniforms(seed, (n, k))
+    u = uniforms(seed + 1, (n, k + 1, 2))
+    out = []
+    for b in range(n):
+        drafts = [int(q_rows[i][0][draw(q_rows[i][1], ud[b, i])]) for i in range(k)]
+        out.append(accept_sampled(p_rows, q_rows, drafts, u[b]))
+    return out
+
+
+def row_pvalues(p_rows, outs):
+    pv = []
+    for i in range(len(p_rows)):
+        toks = [o[i] for o in outs if len(o) > i]
+        pv.append(chi2_pvalue(toks, *p_rows[i]) if len(toks) >= 200 else 1.0)
+    return pv
+
+
+TRIALS = 200_000
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.0, 1.0, "point"])
+def test_chi_square_emitted_tokens_follow_p(rho):
+    p_rows, q_rows = make_case(rho, 1100 + (7 if rho == "point" else int(float(rho) * 10)))
+    outs = run_trials(p_rows, q_rows, TRIALS, 42)
+    pv = row_pvalues(p_rows, outs)
+    assert min(pv) >= 1e-3, pv
+    if rho == 1.0:  # q == p: every draft accepted
+        assert all(len(o) == len(q_rows) + 1 for o in outs)
+
+
+@pytest.mark.parametrize("rho", [0.9, "point"])
+def test_chi_square_control_replacement_from_p_fails(rho, monkeypatch):
+    p_rows, q_rows = make_case(rho, 1100 + (7 if rho == "point" else int(float(rho) * 10)))
+    monkeypatch.setattr(acc, "residual_weights", lambda p, q: [float(x) for x in p[1]])
+    outs = run_trials(p_rows, q_rows, TRIALS, 42)
+    pv = row_pvalues(p_rows, outs)
+    assert pv[0] < 1e-6, pv
