@@ -1,0 +1,388 @@
+"""Benchmark of one speculative-decoding verify window on one MI355X.
+
+A step is one verify pass over the whole hot path:
+  * the projections of a 36-layer 8B-class decoder stack (per layer: q|k|v,
+    o, gate|up and down, bf16 weights stored fused where the projections
+    share an input) for R = k + 1 = 4 rows,
+  * the 151936 x 4096 LM head for the same rows,
+  * the acceptance stage: penalties on the R target rows (window 64,
+    repeat 1.1, presence 1.5, frequency 0.2) and on the draft's 8
+    re-scored candidates per draft row, the top-64 pool, the sampler policy
+    (temperature 0.7, top-k 20, top-p 0.95, min-p 0.05) for p and q, and
+    speculative rejection acceptance with the bonus draw.
+Inputs (synthetic, seeded, N(0, 0.02) bf16 weights, N(0, 1) activations)
+are resident in HBM before timing starts.  `value` is the algorithmic bytes
+of the pass divided by the step time.
+
+Also reported: time per pass of the projections for every R from 1 to 24
+(the knee), the roofline of the projection kernel, batched sampling rows/s
+(vocab 4096, k = 3, 16384 windows each with its own rows), and the oracle
+on the host cores as the CPU baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--rows 4]
+                    [--no-sweep] [--no-cpu-baseline] [--graph]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CFG = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
+PEN = dict(window=64, repeat=1.1, presence=1.5, frequency=0.2)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", type=int, default=4, help="verify rows R = k + 1")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sampling", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--layers", type=int, default=36)
+    return ap.parse_args()
+
+
+class VerifyPass:
+    """All inputs of one verify window, resident on the GPU."""
+
+    def __init__(self, torch, vs, synth, layers, rmax, dev):
+        self.torch, self.vs = torch, vs
+        self.dev = dev
+        self.mats = []  # (W, X[rmax][K], Y[rmax][N])
+        seed = 5000
+        g = torch.Generator(device=dev)
+        for layer in range(layers):
+            for name, (N, K) in synth.LAYER_SHAPES_FUSED.items():
+                W = synth.torch_bf16_weights((N, K), seed, dev)
+                g.manual_seed(seed + 1)
+                X = torch.randn((rmax, K), generator=g, device=dev, dtype=torch.float32)
+                Y = torch.empty((rmax, N), device=dev, dtype=torch.float32)
+                self.mats.append((W, X, Y))
+                seed += 2
+        N, K = synth.LM_HEAD_SHAPE
+        self.head = synth.torch_bf16_weights((N, K), seed, dev)
+        g.manual_seed(seed + 1)
+        self.head_x = torch.randn((rmax, K), generator=g, device=dev, dtype=torch.float32)
+        self.logits = torch.empty((rmax, N), device=dev, dtype=torch.float32)
+        self.vocab = N
+        self._arg_cache = {}
+        torch.cuda.synchronize()
+
+    def bytes_projections(self, R):
+        tot = 0
+        for W, X, Y in self.mats:
+            N, K = W.shape
+            tot += 2 * N * K + 4 * R * (K + N)
+        N, K = self.head.shape
+        tot += 2 * N * K + 4 * R * (K + N)
+        return tot
+
+    def n_launches(self):
+        return len(self.mats) + 1
+
+    def _args(self, R):
+        """C-ABI arguments of every projection launch at R rows (pointers cached)."""
+        if R not in self._arg_cache:
+            out = []
+            for W, X, Y in self.mats + [(self.head, self.head_x, self.logits)]:
+                N, K = W.shape
+                out.append((W.data_ptr(), K, N, K, X.data_ptr(), K, R, Y.data_ptr(), N))
+            self._arg_cache[R] = out
+        return self._arg_cache[R]
+
+    def projections(self, R):
+        """The R-row projections of the stack and the LM head, in pass order."""
+        fn = self.vs.library().verify_gemv_rows
+        stream = self.torch.cuda.current_stream().cuda_stream
+        for a in self._args(R):
+            st = fn(*a, stream)
+            if st != 0:
+                raise RuntimeError(f"verify_gemv_rows failed with status {st}")
+
+    def setup_acceptance(self, synth, R):
+        """History, draft candidates and drafts for a window of k = R - 1 drafts."""
+        torch, vs, dev = self.torch, self.vs, self.dev
+        k = R - 1
+        self.R, self.k = R, k
+        self.projections(R)
+        torch.cuda.synchronize()
+        lg = self.logits[:R].cpu().numpy()
+        hot = np.unique(np.argsort(-lg, axis=1)[:, :64])
+        ctx = synth.penalty_history(6001, self.vocab, 2048, 32, hot)
+        q_ids, q_vals = synth.draft_candidates(6002, lg[:k], 8)
+        self.ctx = torch.from_numpy(ctx).to(dev)
+        self.q_ids = torch.from_numpy(q_ids).to(dev)
+        self.q_raw = torch.from_numpy(q_vals).to(dev)
+        self.q_vals = self.q_raw.clone()
+        self.u = torch.from_numpy(synth.uniforms(6003, (1, R, 2))).to(dev)
+        ud = torch.from_numpy(synth.uniforms(6004, (k, 1))).to(dev)
+        # the drafter's own sequential draws: d_i ~ q_i penalised by H_i
+        drafts = torch.zeros((k,), dtype=torch.int32, device=dev)
+        for i in range(k):
+            # row i's history holds drafts[0, i): penalise a copy of all rows, keep row i
+            allq = self.q_raw.clone()
+            vs.penalize_rows(allq, self.ctx, drafts[:i].contiguous(), ids=self.q_ids,
+                             vocab=self.vocab, **PEN)
+            _, _, _, drawn = vs.sample_policy_rows(allq[i:i + 1].contiguous(),
+                                                   self.q_ids[i:i + 1].contiguous(),
+                                                   u=ud[i], **CFG)
+            drafts[i] = drawn[0]
+        self.drafts = drafts
+        self.ws = torch.empty(vs.topk_rows_workspace_bytes(R, self.vocab, 64), dtype=torch.uint8,
+                              device=dev)
+        self.pool_v = torch.empty((R, 64), device=dev, dtype=torch.float32)
+        self.pool_i = torch.empty((R, 64), device=dev, dtype=torch.int32)
+        self.p_out = (torch.empty((R, 64), dtype=torch.int32, device=dev),
+                      torch.empty((R, 64), dtype=torch.float32, device=dev),
+                      torch.empty((R,), dtype=torch.int32, device=dev), None)
+        self.q_out = (torch.empty((k, 8), dtype=torch.int32, device=dev),
+                      torch.empty((k, 8), dtype=torch.float32, device=dev),
+                      torch.empty((k,), dtype=torch.int32, device=dev), None)
+        self.acc_out = (torch.empty((1, R), dtype=torch.int32, device=dev),
+                        torch.empty((1,), dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+
+    def acceptance(self):
+        vs, R, k = self.vs, self.R, self.k
+        L = self.logits[:R]
+        vs.penalize_rows(L, self.ctx, self.drafts, **PEN)
+        vs.topk_rows(L, 64, self.pool_v, self.pool_i, self.ws)
+        p = vs.sample_policy_rows(self.pool_v, self.pool_i, out=self.p_out, **CFG)
+        self.q_vals.copy_(self.q_raw)  # the draft's re-scored candidates for this window
+        vs.penalize_rows(self.q_vals, self.ctx, self.drafts, ids=self.q_ids, vocab=self.vocab, **PEN)
+        q = vs.sample_policy_rows(self.q_vals, self.q_ids, out=self.q_out, **CFG)
+        vs.spec_accept_rows(vs.ACCEPT_SAMPLED, self.drafts[None, :], p[:3], q[:3], u=self.u,
+                            out=self.acc_out)
+
+    def step(self):
+        self.projections(self.R)
+        self.acceptance()
+
+
+def time_region(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, warmup=1):
+    """Batched acceptance stage, one set of rows per window (config: vocab 4096, k = 3)."""
+    R = k + 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000)
+    p_log = torch.randn((B * R, vocab), generator=g, device=dev) * 3.0
+    q_log = 0.9 * p_log.view(B, R, vocab)[:, :k].reshape(B * k, vocab) + \
+        (1 - 0.81) ** 0.5 * 3.0 * torch.randn((B * k, vocab), generator=g, device=dev)
+    u = torch.rand((B, R, 2), generator=g, device=dev)
+    ud = torch.rand((B * k,), generator=g, device=dev)
+    pv = torch.empty((B * R, 64), device=dev)
+    pi = torch.empty((B * R, 64), dtype=torch.int32, device=dev)
+    qv = torch.empty((B * k, 64), device=dev)
+    qi = torch.empty((B * k, 64), dtype=torch.int32, device=dev)
+    ws_p = torch.empty(max(1, vs.topk_rows_workspace_bytes(B * R, vocab, 64)), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(max(1, vs.topk_rows_workspace_bytes(B * k, vocab, 64)), dtype=torch.uint8, device=dev)
+    p_out = (torch.empty((B * R, 64), dtype=torch.int32, device=dev),
+             torch.empty((B * R, 64), dtype=torch.float32, device=dev),
+             torch.empty((B * R,), dtype=torch.int32, device=dev), None)
+    q_out = (torch.empty((B * k, 64), dtype=torch.int32, device=dev),
+             torch.empty((B * k, 64), dtype=torch.float32, device=dev),
+             torch.empty((B * k,), dtype=torch.int32, device=dev),
+             torch.empty((B * k,), dtype=torch.int32, device=dev))
+    acc = (torch.empty((B, R), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+
+    def run():
+        vs.topk_rows(p_log, 64, pv, pi, ws_p)
+        vs.sample_policy_rows(pv, pi, out=p_out, **CFG)
+        vs.topk_rows(q_log, 64, qv, qi, ws_q)
+        vs.sample_policy_rows(qv, qi, u=ud, out=q_out, **CFG)
+        drafts = q_out[3].view(B, k)
+        vs.spec_accept_rows(vs.ACCEPT_SAMPLED, drafts, p_out[:3], q_out[:3], u=u, out=acc)
+
+    ms = time_region(torch, run, steps, warmup)
+    mean_emitted = float(acc[1].float().mean().item())
+    return {"windows": B, "k": k, "vocab": vocab, "ms": ms,
+            "rows_per_s": B * R / (ms * 1e-3), "windows_per_s": B / (ms * 1e-3),
+            "mean_emitted_per_window": mean_emitted}
+
+
+def cpu_baseline(synth, R, budget_s=20.0):
+    """The oracle (as it stands) on a bounded sample of the same pass, on the host cores."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    shapes = list(synth.LAYER_SHAPES_FUSED.values())
+    done_bytes, spent, mats = 0, 0.0, 0
+    layer = 0
+    while spent < budget_s * 0.7 and layer < 4:
+        for i, (N, K) in enumerate(shapes):
+            w, x = synth.gemv_case(8000 + 10 * layer + i, N, K, R)
+            t0 = time.perf_counter()
+            oracle.gemv.gemv_rows(w, x)
+            spent += time.perf_counter() - t0
+            done_bytes += 2 * N * K + 4 * R * (K + N)
+            mats += 1
+        layer += 1
+    gbs = done_bytes / spent / 1e9
+    # the acceptance stage of one window over the LM-head vocabulary
+    V = synth.VOCAB
+    lg = synth.logits(8100, (R, V))
+    hot = np.unique(np.argsort(-lg, axis=1)[:, :64])
+    ctx = synth.penalty_history(8101, V, 2048, 32, hot)
+    q_ids, q_vals = synth.draft_candidates(8102, lg[:R - 1], 8)
+    drafts = q_ids[:, 0].copy()
+    u = synth.uniforms(8103, (R, 2))
+    t0 = time.perf_counter()
+    oracle.pipeline.acceptance_stage(lg, ctx, drafts, u, q_ids=q_ids, q_vals=q_vals, **PEN, **CFG)
+    acc_s = time.perf_counter() - t0
+    return {"value": gbs, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 projection oracle over {layer} fused 8B-class layers "
+                      f"({mats} matrices, {done_bytes / 1e9:.2f} GB of bf16 weights, R={R}); "
+                      f"acceptance-stage oracle on one window (R={R}, vocab {V}): "
+                      f"{acc_s * 1e3:.0f} ms",
+            "seconds": spent + acc_s,
+            "accept_window_ms": acc_s * 1e3}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the verify step would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import verify_sampling_amd as vs
+
+    vs.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = args.rows
+    rmax = 24
+    log(f"generating weights: {args.layers} layers + LM head")
+    t0 = time.time()
+    vp = VerifyPass(torch, vs, synth, args.layers, rmax, dev)
+    log(f"weights ready in {time.time() - t0:.1f}s")
+    vp.setup_acceptance(synth, R)
+
+    step = vp.step
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                vp.step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            vp.step()
+        step = graph.replay
+
+    ms_step = time_region(torch, step, args.steps, args.warmup)
+    step_bytes = vp.bytes_projections(R)
+    log(f"step: {ms_step:.3f} ms")
+
+    # the projection kernel alone, for the roofline (same stream, HIP events)
+    ms_proj = time_region(torch, lambda: vp.projections(R), args.steps, args.warmup)
+    ms_accept = time_region(torch, vp.acceptance, args.steps, args.warmup)
+    per_launch_ms = ms_proj / vp.n_launches()
+    bytes_per_launch = step_bytes / vp.n_launches()
+    achieved = bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
+
+    sweep = {}
+    if not args.no_sweep:
+        for r in range(1, 25):
+            sweep[r] = time_region(torch, lambda: vp.projections(r), max(3, args.steps // 4), 1)
+        log("sweep done")
+    knee = None
+    if sweep:
+        t1 = sweep[1]
+        knee = next((r for r in sorted(sweep) if sweep[r] > 1.1 * t1), None)
+
+    sampling = None if args.no_sampling else sampling_batch(torch, vs, synth, dev)
+    if sampling:
+        log(f"sampling: {sampling['rows_per_s']:.3e} rows/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(synth, R)
+
+    out = {
+        "metric": "verify-pass HBM GB/s (ms/pass vs rows R=1..24; accepted-token sampling rows/s)",
+        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16xf32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"verify window: {args.layers}-layer 8B-class projection stack "
+                        f"(qkv 6144x4096, o 4096x4096, gate|up 24576x4096, down 4096x12288) "
+                        f"+ LM head 151936x4096 + acceptance stage (penalties W=64, top-64 pool, "
+                        f"T0.7/top-k20/top-p0.95/min-p0.05, rejection accept), R={R}",
+            "rows": R,
+            "layers": args.layers,
+            "bytes_per_pass": step_bytes,
+            "graph": bool(args.graph),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_rows_kernel<1>" if R <= 16 else "gemv_rows_kernel<2>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "launches_per_pass": vp.n_launches(),
+            "avg_launch_us": per_launch_ms * 1e3,
+        },
+        "ms_projections": ms_proj,
+        "ms_acceptance": ms_accept,
+        "verify_tokens_per_s": R / (ms_step * 1e-3),
+        "ms_per_pass_vs_R": {str(r): round(v, 4) for r, v in sweep.items()},
+        "gbs_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9, 1)
+                     for r, v in sweep.items()},
+        "knee_R": knee,
+        "sampling": sampling,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * verify_sampling.h: C ABI of the speculative-decoding verify step on
+ * MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [SD]   "Speculative decoding on RDNA" (hipfire 0.4.1 explainer)
+ *   [TREE] "One RDNA4 verify pass has slack for about two dozen speculative
+ *          tokens"
+ *   [PR]   "feat(dflash): developer-only online draft tuning" (hipfire PR #820)
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no mutable global state; scratch space,
+ *     where needed, is a caller-provided workspace whose size a companion
+ *     *_workspace_bytes() call reports.
+ *   - Every call only enqueues work on `stream` and returns; it never
+ *     synchronises the device.  Outputs are valid once the stream has
+ *     reached the call.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     negative status means nothing was launched and no output was
+ *     touched.  VS_ERR_HIP means the launch itself failed (see
+ *     vs_last_error_detail()).
+ *   - Data are never errors: NaN and +-inf logits follow the documented
+ *     orders, token ids outside [0, vocab) in a history are ignored.
+ *   - Calls on distinct streams with disjoint outputs may run concurrently;
+ *     the library is re-entrant.
+ */
+#ifndef VERIFY_SAMPLING_H
+#define VERIFY_SAMPLING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vs_status {
+  VS_OK = 0,
+  VS_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  VS_ERR_SHAPE = -2,       /* a size or leading dimension is out of range    */
+  VS_ERR_PARAM = -3,       /* a scalar parameter is out of range             */
+  VS_ERR_UNSUPPORTED = -4, /* a valid combination this build does not handle */
+  VS_ERR_WORKSPACE = -5,   /* workspace missing or too small                 */
+  VS_ERR_ALIGN = -6,       /* a pointer or leading dimension is misaligned   */
+  VS_ERR_HIP = -7          /* the HIP runtime reported an error at launch    */
+};
+
+#define VS_ABI_VERSION 1
+#define VS_MAX_ROWS 24     /* verify rows R = k + 1 per projection call      */
+#define VS_POOL 64         /* width of the sampler's candidate pool          */
+#define VS_MAX_WINDOW 4096 /* longest penalty window                         */
+#define VS_MAX_VOCAB 262144
+#define VS_MAX_DRAFTS 63   /* drafts (or tree nodes) per window: rows = k + 1 <= 64 */
+
+/* ABI version of the loaded library (VS_ABI_VERSION at build time). */
+int vs_abi_version(void);
+
+/* Static description of a status code. */
+const char* vs_status_string(int status);
+
+/* Text of the last VS_ERR_HIP on the calling thread ("" if none). */
+const char* vs_last_error_detail(void);
+
+/*
+ * verify_gemv_rows: the multi-row verify projection.
+ *   [SD] §01: one verify pass streams each weight matrix once for the
+ *   current position plus k drafts (R = k + 1 rows); §02: the multi-row
+ *   projections sum in exactly the single-row decode order.
+ *
+ *   Y[r][n] = sum_k W[n][k] * X[r][k],  0 <= r < R, 0 <= n < N,
+ * with bf16 weights, fp32 activations and fp32 accumulation.  Row r of the
+ * result is bit-identical to the result of the same call with R = 1 and
+ * X = row r: the summation order depends only on N and K.
+ *
+ *   W    bf16 bit patterns, row-major [N][ldw] (nn.Linear layout, out x in);
+ *        16-byte aligned, ldw % 8 == 0, ldw >= K.
+ *   X    fp32 [R][ldx]; 16-byte aligned, ldx % 4 == 0, ldx >= K.
+ *   Y    fp32 [R][ldy]; ldy >= N.  Must not overlap W or X.
+ *   N >= 1, 1 <= K with K % 8 == 0, 1 <= R <= VS_MAX_ROWS.
+ */
+int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K,
+                     const float* X, int64_t ldx, int R,
+                     float* Y, int64_t ldy, hipStream_t stream);
+
+/*
+ * penalize_rows: windowed repeat / frequency / presence penalties, in place.
+ *   [SD] §04, figure "the penalty history of verify row i":
+ *     H_i = last W tokens of (prompt || emitted || drafts[0, i)),
+ *   and the draft step proposed for row i is penalised by the same H_i.
+ *
+ * Row i (0 <= i < rows) uses H_i = the last `window` tokens of
+ * (ctx[0, ctx_len) || drafts[0, min(i, n_drafts))).  For each distinct
+ * token t in H_i with count c, on its logit l, in fp32 with one rounding
+ * per step and in this order:
+ *   l = (l > 0) ? l / repeat : l * repeat;   l = l - c * frequency;
+ *   l = l - presence.
+ * Tokens outside [0, vocab) in H_i are ignored.  window == 0 is a no-op.
+ *
+ *   Dense  (ids == NULL): logits [rows][ld] holds the whole vocabulary;
+ *          width == vocab.
+ *   Sparse (ids != NULL): ids [rows][ld] and logits [rows][ld] hold
+ *          `width` candidates per row; each candidate slot whose id occurs
+ *          in H_i is penalised with that id's count.
+ *   ctx     int32 [ctx_len] (may be NULL when ctx_len == 0), the request's
+ *           context so far (only its last `window` tokens are read).
+ *   drafts  int32 [n_drafts] (may be NULL when n_drafts == 0).
+ *   1 <= rows <= 4096, 1 <= width <= ld, 1 <= vocab <= 2^31 - 1,
+ *   0 <= window <= VS_MAX_WINDOW, repeat > 0, all parameters finite.
+ */
+int penalize_rows(float* logits, const int32_t* ids, int64_t ld, int rows, int width,
+                  int vocab, const int32_t* ctx, int ctx_len, const int32_t* drafts,
+                  int n_drafts, int window, float repeat, float presence, float frequency,
+                  hipStream_t stream);
+
+/*
+ * topk_rows: per-row top-K in the sampler's pool order.
+ *   [SD] §03 "how hipfire does it": a 64-wide pool with a fixed tie order;
+ *   [PR] "Code map": batched top-K over draft rows, several workgroups per
+ *   row, byte-identical with ties, NaN and -inf included.
+ *
+ * Order: value descending, then index ascending; every NaN ranks below
+ * -inf; -0 and +0 are equal.  out_vals holds the input's bits unchanged.
+ *   X        fp32 [rows][ldx], V valid entries per row.
+ *   out_vals fp32 [rows][ld_out], out_idx int32 [rows][ld_out]; K entries
+ *            per row are written.
+ *   1 <= rows <= 2^24, 1 <= K <= VS_POOL, K <= V <= VS_MAX_VOCAB, ld_out >= K.
+ *   workspace: device memory of at least topk_rows_workspace_bytes(rows, V, K)
+ *   bytes, 16-byte aligned; its contents need no initialisation and are
+ *   scratch after the call.
+ */
+size_t topk_rows_workspace_bytes(int rows, int V, int K);
+int topk_rows(const float* X, int64_t ldx, int rows, int V, int K,
+              float* out_vals, int32_t* out_idx, int64_t ld_out,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sample_policy_rows: the sampler distribution of each row, optionally
+ * with one inverse-CDF draw.
+ *   [SD] §03 "how hipfire does it": temperature, then top-k (absent means
+ *   20 candidates, 0 means the 64-wide pool), then min-p, then top-p, with
+ *   the same pool, tie order and summation; q is the same policy applied
+ *   to the draft's re-scored candidates.
+ *
+ * Each row holds M candidates (vals fp32, ids int32; ids < 0 are ignored).
+ * They are ordered by (value desc, id asc, NaN last).  temperature <= 0 is
+ * greedy (all mass on the first).  Otherwise, in fp64:
+ *   weights e_j = exp((l_j - l_0) / T) over the first k_eff candidates,
+ *   k_eff = 20 if top_k < 0, 64 if top_k == 0, else min(top_k, 64);
+ *   -inf / NaN logits weigh 0 (if l_0 = +inf, each +inf weighs 1);
+ *   weight-0 candidates are dropped; min-p keeps e_j >= min_p * e_0;
+ *   top-p keeps candidates while the kept mass before them is
+ *   < top_p * (total kept mass), at least one (top_p >= 1 keeps all);
+ *   sums run sequentially in pool order; p_j = e_j / sum, rounded to fp32.
+ *   dist_ids/dist_probs [rows][ld_dist] receive the L kept candidates in
+ *   pool order, entries L..M-1 are set to id -1 and probability 0;
+ *   dist_len [rows] receives L (>= 1 when any id is >= 0, else 0).
+ *   u (fp32 [rows], in [0,1)) and drawn (int32 [rows]) are optional but
+ *   must be given together: drawn[r] = dist_ids[r][j], j the first index
+ *   with u * total < C_j, C_j the sequential fp64 sum of the fp32 probs.
+ *   1 <= M <= VS_POOL, M <= ld, M <= ld_dist, 1 <= rows.
+ */
+int sample_policy_rows(const float* vals, const int32_t* ids, int64_t ld, int rows, int M,
+                       float temperature, int top_k, float top_p, float min_p,
+                       int32_t* dist_ids, float* dist_probs, int32_t* dist_len, int64_t ld_dist,
+                       const float* u, int32_t* drawn, hipStream_t stream);
+
+/*
+ * spec_accept_rows: accept drafts for B windows.
+ *   VS_ACCEPT_GREEDY:      [SD] §02: accept the longest prefix of drafts
+ *                          equal to the target argmax (p_ids[row][0]); emit
+ *                          the argmax at the first mismatch, else the bonus
+ *                          argmax of row k ([SD] §01: >= 1 token).
+ *   VS_ACCEPT_SAMPLED:     [SD] §03 steps 1-4: accept d_i iff
+ *                          u[i][0] * q_i(d_i) < p_i(d_i) (fp64); on
+ *                          rejection emit a draw with u[i][1] from
+ *                          (p_i - q_i)+ over p_i's support (from p_i if
+ *                          that is all zero) and stop; after k acceptances
+ *                          emit a bonus draw from p_k with u[k][1].  A
+ *                          point-mass q = delta(c) gives [SD] §06.
+ *   VS_ACCEPT_GREEDY_TREE: [TREE] "Spend the budget on a tree": node j has
+ *                          token drafts[j] and parent parent[j] (-1 = root,
+ *                          else < j); row 0 is the root, row 1 + j is node
+ *                          j.  A node agrees when its token equals its
+ *                          parent row's argmax and its parent agrees; the
+ *                          deepest agreeing node (lowest number on a tie)
+ *                          ends the accepted branch, whose tokens are
+ *                          emitted followed by that node's row argmax.
+ *
+ *   Distributions are sparse rows (ids int32, probs fp32, len int32) as
+ *   written by sample_policy_rows.  Window b's row i is row
+ *   b * p_win_stride + i of p (p_ld entries per row, p_len[row] valid);
+ *   q likewise with q_win_stride (a stride of 0 shares one set of rows
+ *   among all windows).  p has k + 1 rows per window, q has k.
+ *   drafts  int32 [B][k]   (tree: node tokens)
+ *   parent  int32 [B][k]   (tree mode only, else may be NULL)
+ *   u       fp32 [B][k+1][2] in [0, 1) (sampled mode only)
+ *   q_*, p_probs, p_len may be NULL in the greedy modes.
+ *   out_tokens int32 [B][k+1] (entries past the count are -1),
+ *   out_n      int32 [B], 1 <= out_n[b] <= k + 1.
+ *   1 <= B, 0 <= k <= VS_MAX_DRAFTS, 1 <= p_ld, q_ld <= VS_POOL.
+ */
+enum vs_accept_mode {
+  VS_ACCEPT_SAMPLED = 0,
+  VS_ACCEPT_GREEDY = 1,
+  VS_ACCEPT_GREEDY_TREE = 2
+};
+int spec_accept_rows(int mode, int B, int k,
+                     const int32_t* p_ids, const float* p_probs, const int32_t* p_len,
+                     int p_ld, int64_t p_win_stride,
+                     const int32_t* q_ids, const float* q_probs, const int32_t* q_len,
+                     int q_ld, int64_t q_win_stride,
+                     const int32_t* drafts, const int32_t* parent, const float* u,
+                     int32_t* out_tokens, int32_t* out_n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_SAMPLING_H */

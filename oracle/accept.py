@@ -28,6 +28,8 @@ Readings taken:
     order, in fp64; if its total is 0 the replacement is drawn from p;
   * row i uses the uniforms u[i][0] (accept test) and u[i][1]
     (replacement or bonus draw); the bonus uses u[k][1];
+  * a target row with an empty distribution emits token -1 (not a
+    token; the policy only yields one when every candidate slot is empty);
   * argmax ties go to the lowest token id (the pool order), so a row's
     argmax is the first entry of its pool;
   * in a tree, row 0 is the root and row 1 + j is node j; the accepted
@@ -125,11 +127,13 @@ def accept_sampled(p_rows, q_rows, drafts, u) -> list[int]:
         for w in r:
             z += w
         ids = p_rows[i][0]
-        if z > 0.0:
+        if len(ids) == 0:
+            out.append(-1)
+        elif z > 0.0:
             out.append(int(ids[draw_weights(r, u[i][1])]))
         else:
             out.append(int(ids[draw(p_rows[i][1], u[i][1])]))
         return out
     ids, probs = p_rows[k]
-    out.append(int(ids[draw(probs, u[k][1])]))
+    out.append(int(ids[draw(probs, u[k][1])]) if len(ids) else -1)
     return out

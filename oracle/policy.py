@@ -8,7 +8,8 @@ applied to the draft's re-scored candidates and their exact logits; one
 request-seeded random stream supplies every draw.
 
 Readings taken where the page is silent:
-  * candidates are ordered by value descending, then id ascending, NaN
+  * candidate slots with a negative id are empty and ignored; the rest
+    are ordered by value descending, then id ascending, NaN
     last (the pool order of oracle.topk); for p the candidates are the
     top-64 of the penalised row;
   * temperature 0 is greedy: all mass on the first candidate;
@@ -73,11 +74,17 @@ def weights(vals: list[float], temperature: float) -> list[float]:
 def policy_row(vals, ids, temperature: float, top_k: int, top_p: float, min_p: float):
     """One row's sampling distribution.
 
-    vals: fp32 candidate logits, ids: their token ids (any order, <= 64 used).
-    Returns (ids int32 [L], probs fp32 [L]) in pool order, L >= 1.
+    vals: fp32 candidate logits, ids: their token ids (any order, <= 64
+    used; negative ids are empty slots and are ignored).
+    Returns (ids int32 [L], probs fp32 [L]) in pool order; L >= 1 unless
+    every slot is empty.
     """
     vals = np.asarray(vals, dtype=np.float32)
     ids = np.asarray(ids, dtype=np.int32)
+    real = ids >= 0  # negative ids mark empty candidate slots
+    vals, ids = vals[real], ids[real]
+    if len(ids) == 0:
+        return np.zeros(0, dtype=np.int32), np.zeros(0, dtype=np.float32)
     order = pool_order(vals, ids)
     v = [float(vals[m]) for m in order]
     t = [int(ids[m]) for m in order]

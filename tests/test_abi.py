@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects invalid arguments on the host before anything is launched.
+
+No call here launches a kernel, so this runs without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import verify_sampling_amd as vs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_sampling.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = vs.library()
+    names = declared_functions()
+    assert set(names) == set(vs.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = vs.library()
+    assert lib.vs_abi_version() == 1
+    assert lib.vs_status_string(0) == b"ok"
+    for code in range(-7, 0):
+        assert lib.vs_status_string(code) != b"unknown status"
+    assert lib.vs_last_error_detail() == b""
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def test_gemv_rejects_before_launch():
+    lib = vs.library()
+    assert lib.verify_gemv_rows(None, 8, 4, 8, FAKE, 8, 1, FAKE, 4, None) == -1
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 0, FAKE, 4, None) == -2      # R = 0
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 25, FAKE, 4, None) == -2     # R > 24
+    assert lib.verify_gemv_rows(FAKE, 12, 4, 12, FAKE, 12, 1, FAKE, 4, None) == -2   # K % 8
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 1, FAKE, 3, None) == -2      # ldy < N
+    assert lib.verify_gemv_rows(ctypes.c_void_p(0x100008), 8, 4, 8, FAKE, 8, 1, FAKE, 4, None) == -6
+
+
+def test_topk_rejects_before_launch():
+    lib = vs.library()
+    assert lib.topk_rows(FAKE, 100, 1, 100, 65, FAKE, FAKE, 65, None, 0, None) == -2   # K > 64
+    assert lib.topk_rows(FAKE, 10, 1, 10, 11, FAKE, FAKE, 11, None, 0, None) == -2     # K > V
+    assert lib.topk_rows_workspace_bytes(4, 151936, 64) == 4 * 38 * 64 * 8
+    assert lib.topk_rows_workspace_bytes(4, 4096, 64) == 0
+    assert lib.topk_rows(FAKE, 8192, 1, 8192, 8, FAKE, FAKE, 8, None, 0, None) == -5   # workspace
+
+
+def test_policy_and_penalty_and_accept_reject_before_launch():
+    lib = vs.library()
+    assert lib.sample_policy_rows(FAKE, FAKE, 65, 1, 65, 0.7, 20, 0.9, 0.1, FAKE, FAKE, FAKE, 65,
+                                  None, None, None) == -2
+    assert lib.sample_policy_rows(FAKE, FAKE, 8, 1, 8, float("nan"), 20, 0.9, 0.1, FAKE, FAKE, FAKE,
+                                  8, None, None, None) == -3
+    assert lib.sample_policy_rows(FAKE, FAKE, 8, 1, 8, 0.7, 20, 0.9, 0.1, FAKE, FAKE, FAKE, 8,
+                                  FAKE, None, None) == -1
+    assert lib.penalize_rows(FAKE, None, 100, 1, 100, 100, FAKE, 4, None, 0, 5000, 1.1, 0, 0,
+                             None) == -3   # window
+    assert lib.penalize_rows(FAKE, None, 100, 1, 100, 100, FAKE, 4, None, 0, 64, 0.0, 0, 0,
+                             None) == -3   # repeat <= 0
+    assert lib.penalize_rows(FAKE, None, 100, 1, 99, 100, FAKE, 4, None, 0, 64, 1.1, 0, 0,
+                             None) == -2   # dense width != vocab
+    # nothing to penalise: returns OK without launching
+    assert lib.penalize_rows(FAKE, None, 100, 1, 100, 100, None, 0, None, 0, 64, 1.1, 0, 0,
+                             None) == 0
+    assert lib.spec_accept_rows(3, 1, 1, FAKE, None, None, 4, 2, None, None, None, 1, 1, FAKE,
+                                None, None, FAKE, FAKE, None) == -3
+    assert lib.spec_accept_rows(0, 1, 64, FAKE, FAKE, FAKE, 4, 65, FAKE, FAKE, FAKE, 4, 64, FAKE,
+                                None, FAKE, FAKE, FAKE, None) == -2   # k > 63
+    assert lib.spec_accept_rows(0, 1, 2, FAKE, FAKE, FAKE, 4, 3, FAKE, FAKE, FAKE, 4, 2, FAKE,
+                                None, None, FAKE, FAKE, None) == -1   # sampled needs u
+    assert lib.spec_accept_rows(2, 1, 2, FAKE, None, None, 4, 3, None, None, None, 1, 0, FAKE,
+                                None, None, FAKE, FAKE, None) == -1   # tree needs parent
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(vs, "_lib", None)
+    with pytest.raises(vs.VerifySamplingError):
+        vs.library(str(tmp_path / "missing.so"))

@@ -1,0 +1,171 @@
+"""GPU parity of spec_accept_rows.
+
+Sampled windows follow section 03 of "Speculative decoding on RDNA": tokens
+and counts must equal the oracle's under the same uniforms (both decide in
+fp64 from the same fp32 probabilities, so no near-tie exception is needed
+here), and the GPU's emitted tokens must pass the 200,000-trial chi-square
+test against p.  Greedy chains and trees use planted accept lengths.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import verify_sampling_amd as vs
+from gpu_common import dev, host
+from oracle.accept import accept_greedy_chain, accept_greedy_tree, accept_sampled
+from oracle.policy import draw, policy_row
+from oracle.topk import topk_rows
+from stats import chi2_pvalue
+from synth import (VOCAB, chain_greedy_case, correlated_logits, logits, tree_greedy_case,
+                   uniforms)
+
+pytestmark = pytest.mark.gpu
+CFG = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
+W = 64
+
+
+def pack(rows, width=W):
+    n = len(rows)
+    ids = np.full((n, width), -1, dtype=np.int32)
+    probs = np.zeros((n, width), dtype=np.float32)
+    lens = np.zeros(n, dtype=np.int32)
+    for i, (t, p) in enumerate(rows):
+        ids[i, :len(t)] = t
+        probs[i, :len(p)] = p
+        lens[i] = len(t)
+    return ids, probs, lens
+
+
+def make_case(rho, seed, k=3, vocab=4096):
+    pl = logits(seed, (k + 1, vocab))
+    pv, pi = topk_rows(pl, 64)
+    p_rows = [policy_row(pv[i], pi[i], **CFG) for i in range(k + 1)]
+    if rho == "point":
+        q_rows = [(np.array([p_rows[i][0][1]], dtype=np.int32), np.array([1.0], dtype=np.float32))
+                  for i in range(k)]
+    else:
+        ql = correlated_logits(pl[:k], rho, seed + 1)
+        qv, qi = topk_rows(ql, 64)
+        q_rows = [policy_row(qv[i], qi[i], **CFG) for i in range(k)]
+    return p_rows, q_rows
+
+
+TRIALS = 200_000
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.0, 1.0, "point"])
+def test_sampled_windows_match_oracle_and_follow_p(rho):
+    k = 3
+    p_rows, q_rows = make_case(rho, 1800 + (7 if rho == "point" else int(float(rho) * 10)))
+    ud = uniforms(1810, (TRIALS, k))
+    u = uniforms(1811, (TRIALS, k + 1, 2))
+    drafts = np.array([[int(q_rows[i][0][draw(q_rows[i][1], ud[b, i])]) for i in range(k)]
+                       for b in range(TRIALS)], dtype=np.int32)
+    pi, pp, pln = pack(p_rows)
+    qi, qp, qln = pack(q_rows)
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_SAMPLED, dev(drafts), (dev(pi), dev(pp), dev(pln)),
+                                 (dev(qi), dev(qp), dev(qln)), u=dev(u), p_win_stride=0,
+                                 q_win_stride=0)
+    tok, n = host(tok), host(n)
+    mism = 0
+    for b in range(TRIALS):
+        want = accept_sampled(p_rows, q_rows, drafts[b], u[b])
+        got = list(tok[b, :n[b]])
+        if got != want or (tok[b, n[b]:] != -1).any():
+            mism += 1
+    assert mism == 0, f"{mism} windows differ"
+    for i in range(k + 1):
+        toks = tok[n > i, i]
+        if len(toks) >= 200:
+            assert chi2_pvalue(toks, *p_rows[i]) >= 1e-3, i
+
+
+@pytest.mark.parametrize("m", [0, 3, 7, 15])
+def test_greedy_chain_planted(m):
+    k = 15
+    argmax, drafts = chain_greedy_case(1820 + m, k, m)
+    p_ids = np.full((k + 1, 4), -1, dtype=np.int32)
+    p_ids[:, 0] = argmax
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY, dev(drafts[None, :]), (dev(p_ids), None, None))
+    tok, n = host(tok), host(n)
+    assert list(tok[0, :n[0]]) == accept_greedy_chain(argmax, drafts)
+    assert n[0] == m + 1 and (tok[0, n[0]:] == -1).all()
+
+
+def test_tree_planted_batch():
+    cases = [(0, 8), (1, 5), (2, 3), (-1, 0), (1, 1), (2, 8), (0, 2), (1, 8)]
+    B, n_nodes = len(cases), 24
+    parents = np.zeros((B, n_nodes), dtype=np.int32)
+    tokens = np.zeros((B, n_nodes), dtype=np.int32)
+    p_ids = np.full((B * (n_nodes + 1), 2), -1, dtype=np.int32)
+    want = []
+    for b, (br, ln) in enumerate(cases):
+        par, tk, am = tree_greedy_case(1830 + b, 3, 8, br, ln)
+        parents[b], tokens[b] = par, tk
+        p_ids[b * (n_nodes + 1):(b + 1) * (n_nodes + 1), 0] = am
+        want.append(accept_greedy_tree(am, tk, par))
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY_TREE, dev(tokens), (dev(p_ids), None, None),
+                                 parent=dev(parents))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        assert list(tok[b, :n[b]]) == want[b], b
+        assert n[b] == cases[b][1] + 1
+
+
+def test_tree_random_small_vocab():
+    g = np.random.default_rng(1840)
+    B, k = 2000, 12
+    parents = np.array([[-1 if j == 0 else int(g.integers(-1, j)) for j in range(k)]
+                        for _ in range(B)], dtype=np.int32)
+    tokens = g.integers(0, 3, (B, k)).astype(np.int32)
+    am = g.integers(0, 3, (B, k + 1)).astype(np.int32)
+    p_ids = am.reshape(-1, 1).copy()
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY_TREE, dev(tokens), (dev(p_ids), None, None),
+                                 parent=dev(parents))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        assert list(tok[b, :n[b]]) == accept_greedy_tree(am[b], tokens[b], parents[b]), b
+
+
+def test_greedy_random_chains_and_k0():
+    g = np.random.default_rng(1841)
+    B, k = 3000, 5
+    drafts = g.integers(0, 2, (B, k)).astype(np.int32)
+    am = g.integers(0, 2, (B, k + 1)).astype(np.int32)
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY, dev(drafts), (dev(am.reshape(-1, 1).copy()), None, None))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        assert list(tok[b, :n[b]]) == accept_greedy_chain(am[b], drafts[b])
+    # k = 0: the window is one plain decode step
+    d0 = torch.zeros((4, 0), dtype=torch.int32, device="cuda:0")
+    am0 = np.array([[5], [6], [7], [8]], dtype=np.int32)
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY, d0, (dev(am0), None, None))
+    assert list(host(n)) == [1, 1, 1, 1] and list(host(tok)[:, 0]) == [5, 6, 7, 8]
+
+
+def test_sampled_per_window_distributions():
+    """Distinct p and q rows per window (stride k+1 and k), k = 5, random supports."""
+    g = np.random.default_rng(1842)
+    B, k = 3000, 5
+    p_rows_all, q_rows_all = [], []
+    for _ in range(B * (k + 1)):
+        t = g.permutation(10)[: int(g.integers(1, 8))].astype(np.int32)
+        w = g.random(len(t)) + 0.01
+        p_rows_all.append((t, (w / w.sum()).astype(np.float32)))
+    for _ in range(B * k):
+        t = g.permutation(10)[: int(g.integers(1, 8))].astype(np.int32)
+        w = g.random(len(t)) + 0.01
+        q_rows_all.append((t, (w / w.sum()).astype(np.float32)))
+    drafts = np.array([[int(q_rows_all[b * k + i][0][draw(q_rows_all[b * k + i][1], g.random())])
+                        for i in range(k)] for b in range(B)], dtype=np.int32)
+    u = g.random((B, k + 1, 2)).astype(np.float32)
+    pi, pp, pln = pack(p_rows_all, 8)
+    qi, qp, qln = pack(q_rows_all, 8)
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_SAMPLED, dev(drafts), (dev(pi), dev(pp), dev(pln)),
+                                 (dev(qi), dev(qp), dev(qln)), u=dev(u))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        want = accept_sampled(p_rows_all[b * (k + 1):(b + 1) * (k + 1)],
+                              q_rows_all[b * k:(b + 1) * k], drafts[b], u[b])
+        assert list(tok[b, :n[b]]) == want, b

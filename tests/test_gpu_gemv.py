@@ -1,0 +1,120 @@
+"""GPU parity of verify_gemv_rows against the fp64 oracle.
+
+Tolerance: |y_gpu - y_ref| <= 1e-4 * sum_k |w*x| per element.  Row identity:
+row r of an R-row call equals the 1-row call on X[r] bit for bit ("the
+multi-row projections sum in exactly the single-row decode order", section
+02 of "Speculative decoding on RDNA").
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import verify_sampling_amd as vs
+from gpu_common import dev, host
+from oracle.gemv import gemv_rows
+from synth import LAYER_SHAPES, LAYER_SHAPES_FUSED, LM_HEAD_SHAPE, gemv_case, torch_bf16_weights
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def check(y, w_bits, x, rows=None):
+    ref, s = gemv_rows(w_bits, x, rows=rows)
+    yy = y if rows is None else y[:, rows]
+    err = np.abs(yy.astype(np.float64) - ref)
+    bad = err > TOL * s
+    assert not bad.any(), f"{bad.sum()} elements out of tolerance, worst {err.max()}"
+    return float((err / np.maximum(s, 1e-300)).max())
+
+
+@pytest.mark.parametrize("N,K,R", [(1024, 1024, 1), (1024, 1024, 2), (1024, 1024, 4),
+                                   (1024, 1024, 8), (1000, 1000, 1), (1000, 1000, 3),
+                                   (1000, 1000, 16), (1000, 1000, 17), (1000, 1000, 24),
+                                   (1, 8, 1), (17, 40, 24), (33, 4104, 5), (5, 12296, 24)])
+def test_parity_small_and_ragged(N, K, R):
+    w, x = gemv_case(1000 + N + K + R, N, K, R)
+    y = host(vs.verify_gemv_rows(dev(w), dev(x)))
+    check(y, w, x)
+
+
+@pytest.mark.parametrize("N,K", [(1024, 1024), (1000, 1000), (4096, 4096), (1024, 12288)])
+def test_rows_bit_identical_to_single_row(N, K):
+    w, x = gemv_case(2000 + N + K, N, K, 24)
+    W, X = dev(w), dev(x)
+    single = np.stack([host(vs.verify_gemv_rows(W, X[r:r + 1]))[0] for r in range(24)])
+    for R in range(1, 25):
+        y = host(vs.verify_gemv_rows(W, X[:R].contiguous()))
+        assert np.array_equal(y.view(np.uint32), single[:R].view(np.uint32)), f"R={R}"
+
+
+def test_layer_projections_r4_and_r1():
+    """One 8B-class layer's seven projections at R = 4, checked in full, plus R = 1."""
+    for i, (name, (N, K)) in enumerate(LAYER_SHAPES.items()):
+        w, x = gemv_case(1200 + i, N, K, 4)
+        W, X = dev(w), dev(x)
+        y4 = host(vs.verify_gemv_rows(W, X))
+        check(y4, w, x)
+        for r in range(4):
+            y1 = host(vs.verify_gemv_rows(W, X[r:r + 1]))
+            assert np.array_equal(y1[0].view(np.uint32), y4[r].view(np.uint32)), (name, r)
+
+
+def sampled_rows(N, n, seed):
+    g = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([g.choice(N, size=min(n, N), replace=False),
+                                     np.arange(max(0, N - 40), N)]))
+    return rows
+
+
+def test_lm_head_r4_sampled_rows():
+    N, K = LM_HEAD_SHAPE
+    W = torch_bf16_weights((N, K), 1300, "cuda:0")
+    x = np.random.default_rng(1301).standard_normal((4, K)).astype(np.float32)
+    y = host(vs.verify_gemv_rows(W, dev(x)))
+    rows = sampled_rows(N, 3000, 1302)
+    w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
+    ref, s = gemv_rows(w_rows, x)
+    err = np.abs(y[:, rows].astype(np.float64) - ref)
+    assert (err <= TOL * s).all()
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8, 16, 24])
+def test_stack_layer_shapes_sampled_rows(R):
+    """The fused shapes streamed in the 36-layer pass (qkv, o, gate|up, down)."""
+    for i, (name, (N, K)) in enumerate(LAYER_SHAPES_FUSED.items()):
+        W = torch_bf16_weights((N, K), 1400 + i, "cuda:0")
+        x = np.random.default_rng(1410 + i).standard_normal((R, K)).astype(np.float32)
+        X = dev(x)
+        y = host(vs.verify_gemv_rows(W, X))
+        rows = sampled_rows(N, 1500, 1420 + i)
+        w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
+        ref, s = gemv_rows(w_rows, x)
+        err = np.abs(y[:, rows].astype(np.float64) - ref)
+        assert (err <= TOL * s).all(), name
+        y1 = host(vs.verify_gemv_rows(W, X[R - 1:R]))
+        assert np.array_equal(y1[0].view(np.uint32), y[R - 1].view(np.uint32)), name
+
+
+def test_repeat_runs_are_bitwise_equal():
+    w, x = gemv_case(1500, 4096, 4096, 8)
+    W, X = dev(w), dev(x)
+    a = host(vs.verify_gemv_rows(W, X))
+    for _ in range(3):
+        assert np.array_equal(host(vs.verify_gemv_rows(W, X)).view(np.uint32), a.view(np.uint32))
+
+
+def test_strided_operands():
+    """Leading dimensions larger than the row length (views into wider buffers)."""
+    w, x = gemv_case(1600, 300, 264, 5)
+    wide_w = np.zeros((300, 272), dtype=np.uint16)
+    wide_w[:, :264] = w
+    wide_x = np.zeros((5, 268), dtype=np.float32)
+    wide_x[:, :264] = x
+    W = dev(wide_w)[:, :264]
+    X = dev(wide_x)[:, :264]
+    Y = torch.full((5, 310), -7.0, device="cuda:0")
+    vs.verify_gemv_rows(W, X, Y[:, :300])
+    y = host(Y)
+    check(y[:, :300], w, x)
+    assert (y[:, 300:] == -7.0).all()

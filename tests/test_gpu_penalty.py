@@ -1,0 +1,75 @@
+"""GPU parity of penalize_rows: bit identity with the fp32 oracle.
+
+Histories follow the figure "the penalty history of verify row i" in section
+04 of "Speculative decoding on RDNA"; the LM-head case uses a 2048-token
+prompt plus 32 emitted tokens with a quarter of the positions drawn from the
+rows' highest-logit tokens, so the penalties actually reach the pool.
+"""
+
+import numpy as np
+import pytest
+
+import verify_sampling_amd as vs
+from gpu_common import dev, host
+from oracle.penalty import penalize_dense, penalize_sparse
+from synth import VOCAB, draft_candidates, logits, penalty_history
+
+pytestmark = pytest.mark.gpu
+P = dict(repeat=1.1, presence=1.5, frequency=0.2)
+
+
+def hot_tokens(x, n=64):
+    return np.unique(np.argsort(-x, axis=1)[:, :n])
+
+
+def run_dense(x, ctx, drafts, window, **p):
+    t = dev(x)
+    vs.penalize_rows(t, dev(ctx), dev(drafts), window=window, **p)
+    return host(t)
+
+
+def test_lm_head_rows_dense():
+    x = logits(1600, (4, VOCAB))
+    ctx = penalty_history(1601, VOCAB, 2048, 32, hot_tokens(x))
+    drafts = np.argsort(-x[:3], axis=1)[:, 1].astype(np.int32)
+    got = run_dense(x, ctx, drafts, 64, **P)
+    want = penalize_dense(x, ctx, drafts, 64, **P)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert (got != x).sum() > 4 * 20  # the window touched many logits
+
+
+def test_draft_candidates_sparse():
+    x = logits(1602, (4, VOCAB))
+    ctx = penalty_history(1603, VOCAB, 2048, 32, hot_tokens(x))
+    ids, vals = draft_candidates(1604, x[:3], 8)
+    drafts = ids[:, 0].copy()
+    t = dev(vals)
+    vs.penalize_rows(t, dev(ctx), dev(drafts), window=64, ids=dev(ids), vocab=VOCAB, **P)
+    want = penalize_sparse(ids, vals, ctx, drafts, 64, **P)
+    assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("ctx_len,n_drafts,window,rows", [
+    (0, 3, 64, 4), (10, 3, 64, 4), (5000, 0, 4096, 2), (100, 5, 3, 7), (64, 2, 1, 3),
+    (300, 10, 200, 12)])
+def test_windows_and_edges(ctx_len, n_drafts, window, rows):
+    V = 3000
+    g = np.random.default_rng(ctx_len + 7 * window + rows)
+    x = logits(1605 + rows, (rows, V))
+    x[:, :50] = 0.0
+    x[:, 50:60] = -0.0
+    ctx = g.integers(-5, V + 5, ctx_len).astype(np.int32)   # some ids out of range
+    ctx[::3] = g.integers(0, 40, len(ctx[::3]))               # repeats
+    drafts = g.integers(0, 60, n_drafts).astype(np.int32)
+    got = run_dense(x, ctx, drafts, window, **P)
+    want = penalize_dense(x, ctx, drafts, window, **P)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_window_zero_and_neutral_are_noops():
+    x = logits(1606, (3, 2000))
+    ctx = np.arange(100, dtype=np.int32)
+    d = np.array([1, 2], dtype=np.int32)
+    assert np.array_equal(run_dense(x, ctx, d, 0, **P).view(np.uint32), x.view(np.uint32))
+    neutral = dict(repeat=1.0, presence=0.0, frequency=0.0)
+    assert np.array_equal(run_dense(x, ctx, d, 64, **neutral).view(np.uint32), x.view(np.uint32))

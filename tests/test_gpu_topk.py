@@ -1,0 +1,80 @@
+"""GPU parity of topk_rows: byte identity with the oracle's pool order.
+
+Planted ties straddling rank K, 1-ulp neighbours, duplicated maxima, NaN,
+-inf and +-0 follow the byte-identity gate described under "Code map" of
+"feat(dflash): developer-only online draft tuning".
+"""
+
+import numpy as np
+import pytest
+
+import verify_sampling_amd as vs
+from gpu_common import dev, host
+from oracle.topk import topk_rows
+from synth import VOCAB, logits, topk_planted_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def compare(x, K):
+    vals, idx = vs.topk_rows(dev(x), K)
+    gv, gi = host(vals), host(idx)
+    ov, oi = topk_rows(x, K)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv.view(np.uint32), ov.view(np.uint32))
+
+
+def test_draft_rows_top16_planted():
+    compare(topk_planted_rows(1500, rows=15, vocab=VOCAB, K=16), 16)
+
+
+def test_pool_top64_target_rows():
+    compare(logits(1501, (4, VOCAB)), 64)
+
+
+def test_argmax_k1():
+    compare(topk_planted_rows(1502, rows=6, vocab=VOCAB, K=1), 1)
+
+
+@pytest.mark.parametrize("V,K", [(64, 64), (100, 1), (100, 16), (4096, 64), (4097, 64),
+                                 (8191, 7), (12289, 64), (262144, 64)])
+def test_sizes_and_ragged_chunks(V, K):
+    x = logits(1503 + V + K, (3, V))
+    x[1, :] = np.float32(0.5)           # all equal: lowest indices
+    x[2, : V // 2] = np.nan             # half NaN, the rest ordinary
+    compare(x, K)
+
+
+def test_special_rows():
+    V = 5000
+    x = logits(1504, (5, V))
+    x[0, :] = -np.inf
+    x[1, :] = np.nan
+    x[2, :] = -0.0
+    x[2, ::7] = 0.0
+    x[3, :] = np.inf
+    x[3, 10] = np.nan
+    x[4, ::3] = -np.inf
+    compare(x, 64)
+
+
+def test_strided_input_and_output():
+    x = logits(1505, (3, 9000))
+    wide = np.full((3, 9100), 99.0, dtype=np.float32)
+    wide[:, :9000] = x
+    X = dev(wide)[:, :9000]
+    import torch
+    ov = torch.zeros((3, 80), dtype=torch.float32, device="cuda:0")
+    oi = torch.zeros((3, 80), dtype=torch.int32, device="cuda:0")
+    vs.topk_rows(X, 64, ov[:, :64], oi[:, :64])
+    rv, ri = topk_rows(x, 64)
+    assert np.array_equal(host(oi)[:, :64], ri)
+    assert (host(oi)[:, 64:] == 0).all()
+
+
+def test_repeat_runs_are_identical():
+    x = topk_planted_rows(1506, rows=15, vocab=VOCAB, K=16)
+    X = dev(x)
+    a = host(vs.topk_rows(X, 16)[1])
+    for _ in range(3):
+        assert np.array_equal(host(vs.topk_rows(X, 16)[1]), a)

@@ -1,0 +1,90 @@
+// penalize_rows: the per-row penalty prepass, in place.
+//
+// "Speculative decoding on RDNA", §04 (figure "the penalty history of verify
+// row i"): row i is penalised against H_i = last W tokens of (prompt ||
+// emitted || drafts[0, i)); the draft step for row i uses the same H_i.
+//
+// One workgroup per row.  The row's history (<= VS_MAX_WINDOW ids) is staged
+// in LDS; each thread owns history positions (dense mode) or candidate slots
+// (sparse mode) and counts occurrences by scanning the history.  In dense
+// mode only the first occurrence of a token applies its penalty, so distinct
+// threads write distinct logits.  The arithmetic is fp32, one rounding per
+// operation, in the documented order (the library is built without
+// floating-point contraction and with a correctly rounded divide).
+
+#include "vs_internal.h"
+
+namespace {
+
+constexpr int THREADS = 256;
+
+__device__ __forceinline__ float penalize_one(float l, int c, float rep, float pres, float freq) {
+  const float l1 = (l > 0.f) ? (l / rep) : (l * rep);
+  const float cf = static_cast<float>(c) * freq;
+  const float l2 = l1 - cf;
+  return l2 - pres;
+}
+
+__global__ void __launch_bounds__(THREADS)
+penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int64_t ld, int width,
+                int vocab, const int32_t* __restrict__ ctx, int ctx_len,
+                const int32_t* __restrict__ drafts, int n_drafts, int window, float rep,
+                float pres, float freq) {
+  __shared__ int32_t hist[VS_MAX_WINDOW];
+  const int row = blockIdx.x;
+  const int nd = row < n_drafts ? row : n_drafts;  // drafts visible to this row
+  const int64_t total = static_cast<int64_t>(ctx_len) + nd;
+  const int hlen = static_cast<int>(total < window ? total : window);
+  const int64_t start = total - hlen;  // position of H_i[0] in ctx || drafts
+  for (int j = threadIdx.x; j < hlen; j += blockDim.x) {
+    const int64_t pos = start + j;
+    int32_t t = pos < ctx_len ? ctx[pos] : drafts[pos - ctx_len];
+    hist[j] = (t >= 0 && t < vocab) ? t : -1;  // ids outside the vocabulary never match
+  }
+  __syncthreads();
+
+  float* lrow = logits + static_cast<int64_t>(row) * ld;
+  if (ids == nullptr) {
+    for (int j = threadIdx.x; j < hlen; j += blockDim.x) {
+      const int32_t t = hist[j];
+      if (t < 0) continue;
+      bool first = true;
+      for (int i = 0; i < j && first; ++i) first = hist[i] != t;
+      if (!first) continue;
+      int c = 1;
+      for (int i = j + 1; i < hlen; ++i) c += hist[i] == t;
+      lrow[t] = penalize_one(lrow[t], c, rep, pres, freq);
+    }
+  } else {
+    const int32_t* irow = ids + static_cast<int64_t>(row) * ld;
+    for (int m = threadIdx.x; m < width; m += blockDim.x) {
+      const int32_t t = irow[m];
+      if (t < 0 || t >= vocab) continue;
+      int c = 0;
+      for (int i = 0; i < hlen; ++i) c += hist[i] == t;
+      if (c > 0) lrow[m] = penalize_one(lrow[m], c, rep, pres, freq);
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int penalize_rows(float* logits, const int32_t* ids, int64_t ld, int rows, int width,
+                             int vocab, const int32_t* ctx, int ctx_len, const int32_t* drafts,
+                             int n_drafts, int window, float repeat, float presence,
+                             float frequency, hipStream_t stream) {
+  if (!logits) return VS_ERR_NULL;
+  if (ctx_len < 0 || n_drafts < 0) return VS_ERR_SHAPE;
+  if ((ctx_len > 0 && !ctx) || (n_drafts > 0 && !drafts)) return VS_ERR_NULL;
+  if (rows < 1 || rows > 4096 || width < 1 || ld < width || vocab < 1) return VS_ERR_SHAPE;
+  if (ids == nullptr && width != vocab) return VS_ERR_SHAPE;
+  if (window < 0 || window > VS_MAX_WINDOW) return VS_ERR_PARAM;
+  if (!(repeat > 0.f) || !__builtin_isfinite(repeat) || !__builtin_isfinite(presence) ||
+      !__builtin_isfinite(frequency))
+    return VS_ERR_PARAM;
+  if (window == 0 || (ctx_len == 0 && n_drafts == 0)) return VS_OK;  // nothing to penalise
+  penalize_kernel<<<dim3(rows), dim3(THREADS), 0, stream>>>(logits, ids, ld, width, vocab, ctx,
+                                                            ctx_len, drafts, n_drafts, window,
+                                                            repeat, presence, frequency);
+  return vs::check_launch();
+}

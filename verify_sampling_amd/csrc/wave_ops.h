@@ -1,0 +1,44 @@
+// Wavefront-level helpers for the sampling kernels (one 64-lane wave per row
+// or per window).  Sums that define a result run sequentially in lane order
+// (every lane walks the same sequence through shuffles), which fixes the
+// rounding order independently of the hardware's reduction trees.
+#pragma once
+
+#include "vs_internal.h"
+
+namespace vs {
+
+__device__ __forceinline__ double bcast(double v, int src) { return __shfl(v, src, 64); }
+__device__ __forceinline__ int bcast(int v, int src) { return __shfl(v, src, 64); }
+
+// Sequential sum of w over lanes [0, n), lane order, fp64.
+__device__ __forceinline__ double seq_sum(double w, int n) {
+  double s = 0.0;
+  for (int j = 0; j < n; ++j) s += bcast(w, j);
+  return s;
+}
+
+// Inverse-CDF draw over lanes [0, n): the first lane j with u * C_n < C_j,
+// C_j the sequential fp64 sum of w over lanes 0..j.  If rounding leaves no
+// such lane, the last lane with positive weight (else 0).
+__device__ __forceinline__ int seq_draw(double w, int n, float u) {
+  const int lane = threadIdx.x & 63;
+  double acc = 0.0, mine = 0.0;
+  for (int j = 0; j < n; ++j) {
+    acc += bcast(w, j);
+    if (lane == j) mine = acc;
+  }
+  const double target = static_cast<double>(u) * acc;
+  const uint64_t hit = __ballot(lane < n && target < mine);
+  if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
+  const uint64_t pos = __ballot(lane < n && w > 0.0);
+  return pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane == 0 ? 0ull : (mask & (~0ull >> (64 - lane)));
+  return __popcll(below);
+}
+
+}  // namespace vs
