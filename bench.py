@@ -38,6 +38,31 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CALIB_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_rows_traffic_r4.md")
+KERNEL_SOURCE = os.path.join(ROOT, "verify_sampling_amd", "csrc", "gemv_rows.hip")
+
+
+def measured_traffic(R):
+    """HBM bytes per projection launch from the committed counter summary.
+
+    None unless the summary was taken at this R from the current kernel
+    source (its sha256 is recorded in the summary).
+    """
+    import hashlib
+    import re
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    r = re.search(r"rows:\s*(\d+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m and r and b) or m.group(1) != src or int(r.group(1)) != R:
+        return None
+    return float(b.group(1))
 CFG = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
 PEN = dict(window=64, repeat=1.1, presence=1.5, frequency=0.2)
 
@@ -57,6 +82,8 @@ def parse():
     ap.add_argument("--no-sampling", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (for scaling HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -288,6 +315,12 @@ def main():
     vs.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     R = args.rows
     rmax = 24
     log(f"generating weights: {args.layers} layers + LM head")
@@ -369,7 +402,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(R),
             "launches_per_pass": vp.n_launches(),
             "avg_launch_us": per_launch_ms * 1e3,
         },
