@@ -71,14 +71,13 @@ template <int T, int U, int CT>
 __device__ __forceinline__ void load_stage(Stage<T, U, CT>& st, int kb, int kb1, int K, int g,
                                            const uint16_t* const (&wrow)[T],
                                            const float* const (&xrow)[CT], const bool (&xon)[CT]) {
+  // activations first: memory returns in issue order, so the split of this
+  // stage's activations can start while its weights are still arriving
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int k = (kb + u) * KBLK + g * 8;
     const bool ok = (kb + u < kb1) && (k < K);  // K % 8 == 0: k < K covers all 8 values
     const int64_t off = static_cast<int64_t>(kb + u) * KBLK;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-      st.w[u][t] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + off) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       if (ok && xon[c]) {
@@ -91,6 +90,15 @@ __device__ __forceinline__ void load_stage(Stage<T, U, CT>& st, int kb, int kb1,
         for (int e = 0; e < 8; ++e) st.x[u][c][e] = 0.f;
       }
     }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = (kb + u) * KBLK + g * 8;
+    const bool ok = (kb + u < kb1) && (k < K);
+    const int64_t off = static_cast<int64_t>(kb + u) * KBLK;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      st.w[u][t] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + off) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -120,7 +128,7 @@ __device__ __forceinline__ void compute_stage(const Stage<T, U, CT>& st, int kb,
 // for all T); U: k-blocks per stage; CT: 16-column activation tiles; PIPE:
 // load stage s+1 while computing stage s.  None of these changes the order in
 // which a row is summed.
-template <int T, int U, int CT, bool PIPE>
+template <int T, int U, int CT, bool PIPE, bool XF = false>
 __global__ void __launch_bounds__(1024)
 gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
                  const float* __restrict__ X, int64_t ldx, int R,
@@ -166,6 +174,13 @@ gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
       if (kb + U >= kb1) break;
       if (kb + 2 * U < kb1) load_stage(sa, kb + 2 * U, kb1, K, g, wrow, xrow, xon);
       compute_stage(sb, kb + U, kb1, acc);
+    }
+  } else if (XF) {
+    // activations of the stage first, then its weights (see load_stage)
+    for (int kb = kb0; kb < kb1; kb += U) {
+      Stage<T, U, CT> st;
+      load_stage(st, kb, kb1, K, g, wrow, xrow, xon);
+      compute_stage(st, kb, kb1, acc);
     }
   } else {
     // weights of U k-blocks in flight; each k-block's activations are loaded
@@ -238,13 +253,13 @@ gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
 
 // Waves per workgroup (the k-split): a function of N and K alone, so that
 // the summation order of a row does not change with R.  Wide matrices (many
-// row tiles) do best with few, long waves; short ones need the k-split for
-// parallelism.  About 8 k-blocks per wave otherwise.
+// row tiles) do best with few, long waves; narrower ones split K further
+// for parallelism.  Chosen by a sweep on MI355X.
 int splits_for(int N, int K) {
   const int nkb = (K + KBLK - 1) / KBLK;
-  int s = (N >= 16384) ? (nkb + 31) / 32 : (N >= 6144 ? (nkb + 7) / 8 : (nkb + 9) / 10);
+  int s = (N >= 16384) ? (nkb + 31) / 32 : (nkb + 15) / 16;
   if (s < 1) s = 1;
-  if (s > 16) s = 16;
+  if (s > (N >= 16384 ? 16 : 8)) s = (N >= 16384 ? 16 : 8);
   return s;
 }
 
@@ -261,27 +276,26 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   const int nkb = (K + KBLK - 1) / KBLK;
   const int splits = splits_for(N, K);
   const dim3 block(64 * splits);
-  // Tile shape by matrix shape (it never changes a row's summation order):
-  // tall matrices take two row tiles per wave, which halves the activation
-  // traffic and the splitting work per weight while keeping all 8 wave slots
-  // per SIMD; short ones keep one tile per wave for parallelism and overlap
-  // the next k-blocks' loads with the current ones' arithmetic.
-  const bool tall = N >= 6144;
+  // Tile shape by matrix shape and R (it never changes a row's summation
+  // order): taller matrices take more row tiles per wave, which divides the
+  // activation traffic and the splitting work per weight; "activations
+  // first" issues a stage's activation loads ahead of its weights so that
+  // their split overlaps the weight latency.  Chosen by a sweep on MI355X.
   auto launch = [&](auto kernel, int T, int CT) {
     const dim3 grid((N + TILE * T - 1) / (TILE * T));
     const size_t shm = static_cast<size_t>(splits) * T * CT * 256 * sizeof(float);
     kernel<<<grid, block, shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
   };
-  const bool huge = N >= 65536;  // vocabulary-sized: enough row tiles for 4 per wave
   if (R <= 16) {
-    if (huge && R > 8) launch(gemv_rows_kernel<4, 1, 1, false>, 4, 1);
-    else if (huge) launch(gemv_rows_kernel<2, 4, 1, false>, 2, 1);
-    else if (tall) launch(gemv_rows_kernel<2, 2, 1, false>, 2, 1);
-    else launch(gemv_rows_kernel<1, 2, 1, true>, 1, 1);
+    if (N >= 65536 && R > 8) launch(gemv_rows_kernel<4, 1, 1, false, true>, 4, 1);
+    else if (N >= 65536) launch(gemv_rows_kernel<2, 4, 1, false, true>, 2, 1);
+    else if (N >= 16384 && R > 8) launch(gemv_rows_kernel<2, 2, 1, false, false>, 2, 1);
+    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 1, false, true>, 2, 1);
+    else launch(gemv_rows_kernel<1, 4, 1, false, true>, 1, 1);
   } else {
-    if (huge) launch(gemv_rows_kernel<4, 1, 2, false>, 4, 2);
-    else if (tall) launch(gemv_rows_kernel<2, 2, 2, false>, 2, 2);
-    else launch(gemv_rows_kernel<1, 2, 2, true>, 1, 2);
+    if (N >= 65536) launch(gemv_rows_kernel<4, 1, 2, false, false>, 4, 2);
+    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 2, false, false>, 2, 2);
+    else launch(gemv_rows_kernel<1, 2, 2, true, false>, 1, 2);
   }
   return vs::check_launch();
 }
