@@ -78,3 +78,39 @@ def test_repeat_runs_are_identical():
     a = host(vs.topk_rows(X, 16)[1])
     for _ in range(3):
         assert np.array_equal(host(vs.topk_rows(X, 16)[1]), a)
+
+
+def crafted_dense_lanes(V=4096):
+    """A row whose top values sit in 16 of the 64 lanes of the wavefront layout,
+    so the group-maxima threshold passes 784 keys and the exact radix select
+    of the batched kernel runs."""
+    x = np.full(V, -5.0, dtype=np.float32)
+    i = np.arange(V)
+    lane = (i % 256) // 4
+    j = 4 * (i // 256) + i % 4
+    x[lane < 16] = 1000.0 + j[lane < 16]
+    return x
+
+
+def test_batched_rows_wave_kernel():
+    """2048 rows x 4096: the throughput kernel (one wavefront per row)."""
+    rows = 2048
+    x = logits(1510, (rows, 4096))
+    x[1] = crafted_dense_lanes()
+    x[2] = 0.75                       # all equal
+    x[3] = np.arange(4096, dtype=np.float32)
+    x[4, ::5] = np.nan
+    x[5, :4000] = -np.inf
+    x[6, ::3] = x[6, 0]               # ties
+    x[7] = crafted_dense_lanes()[::-1].copy()
+    compare(x, 64)
+
+
+def test_batched_multi_chunk_rows_wave_kernel():
+    """1024 rows x 8292 (three chunks, the last ragged): stage 1 by wavefront, then stage 2."""
+    rows = 1024
+    x = logits(1511, (rows, 8292))
+    x[0, :4096] = crafted_dense_lanes()
+    x[1, :] = 3.0
+    x[2, 8190:] = 1e30                # maxima in the ragged chunk
+    compare(x, 16)
