@@ -41,7 +41,7 @@ __device__ __forceinline__ int clamp_len(int n, int ld) { return n < 0 ? 0 : (n 
 __device__ __forceinline__ double prob_of(int32_t id, double p, int n, int32_t x) {
   double s = 0.0;
   for (int j = 0; j < n; ++j) {
-    const int32_t t = __shfl(id, j, 64);
+    const int32_t t = vs::bcast(id, j);
     const double pj = vs::bcast(p, j);
     if (t == x) s += pj;
   }
@@ -129,7 +129,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       // residual (p - q)+ over p's support, in p's order
       double qt = 0.0;
       for (int j = 0; j < ql; ++j) {
-        const int32_t t = __shfl(qid, j, 64);
+        const int32_t t = vs::bcast(qid, j);
         const double pj = vs::bcast(qp, j);
         if (t == pid) qt += pj;
       }
@@ -137,7 +137,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const double r = (lane < pl && diff > 0.0) ? diff : 0.0;
       const double z = vs::seq_sum(r, pl);
       const int j = z > 0.0 ? vs::seq_draw(r, pl, ub[2 * i + 1]) : vs::seq_draw(pp, pl, ub[2 * i + 1]);
-      const int32_t t = __shfl(pid, j, 64);
+      const int32_t t = vs::bcast(pid, j);
       if (lane == n) my_tok = t;
       ++n;
       stopped = true;
@@ -148,7 +148,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
       const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
       const int j = vs::seq_draw(pp, pl, ub[2 * k + 1]);
-      const int32_t t = __shfl(pid, j, 64);
+      const int32_t t = vs::bcast(pid, j);
       if (lane == n) my_tok = t;
       ++n;
     }

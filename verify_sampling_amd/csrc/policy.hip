@@ -51,7 +51,7 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
     bool one_hot = !(temperature > 0.f);
     double e = 0.0;
     if (!one_hot) {
-      const float l0 = __shfl(v, 0, 64);
+      const float l0 = __builtin_bit_cast(float, vs::bcast(static_cast<int>(vbits), 0));
       const double T = static_cast<double>(temperature);
       const bool cand = real && lane < k_eff;
       if (__builtin_isinf(l0) && l0 > 0.f) {
@@ -71,13 +71,16 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
         // weight-0 candidates carry no mass; min-p relative to the first
         const bool keep1 = e > 0.0 && e >= static_cast<double>(min_p) * e0;
         const double tp = static_cast<double>(top_p);
+        // only the first nk lanes can carry weight; the sums stop there (adding
+        // +0.0 to a non-negative sum changes nothing)
+        const int nk = n_real < k_eff ? n_real : k_eff;
         bool keep2 = keep1;
         if (tp < 1.0) {
-          const double s = vs::seq_sum(keep1 ? e : 0.0, 64);
+          const double s = vs::seq_sum(keep1 ? e : 0.0, nk);
           keep2 = false;
           double c = 0.0;
           bool first = true;
-          for (int j = 0; j < 64; ++j) {
+          for (int j = 0; j < nk; ++j) {
             const double ej = vs::bcast(e, j);
             const int kj = vs::bcast(keep1 ? 1 : 0, j);
             if (!kj) continue;
@@ -90,7 +93,7 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
             }
           }
         }
-        const double z = vs::seq_sum(keep2 ? e : 0.0, 64);
+        const double z = vs::seq_sum(keep2 ? e : 0.0, nk);
         keep = keep2;
         prob = keep ? static_cast<float>(e / z) : 0.f;
       }
@@ -122,8 +125,10 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
     const double w = keep ? static_cast<double>(prob) : 0.0;
     int32_t pick = -1;
     if (L > 0) {
+      // kept lanes lie below the last kept lane + 1
+      const int nl = 64 - __clzll(static_cast<long long>(kmask));
       double acc = 0.0, mine = 0.0;
-      for (int j = 0; j < 64; ++j) {
+      for (int j = 0; j < nl; ++j) {
         acc += vs::bcast(w, j);
         if (lane == j) mine = acc;
       }
@@ -136,7 +141,7 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
         const uint64_t posm = __ballot(keep && w > 0.0);
         src = posm ? 63 - __clzll(static_cast<long long>(posm)) : (__ffsll(static_cast<long long>(kmask)) - 1);
       }
-      pick = __shfl(tok, src, 64);
+      pick = vs::bcast(tok, src);
     }
     if (lane == 0) drawn[row] = pick;
   }

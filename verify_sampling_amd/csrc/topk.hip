@@ -207,8 +207,8 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
 }
 
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
-  const uint32_t lo = __shfl(static_cast<uint32_t>(v), src, 64);
-  const uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src, 64);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v & 0xffffffffu), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), src));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
@@ -393,8 +393,8 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
         }
       }
       const int src = __ffsll(static_cast<long long>(__ballot(mine))) - 1;
-      digit = __shfl(digit, src, 64);
-      need = __shfl(rest, src, 64);
+      digit = vs::bcast(digit, src);
+      need = vs::bcast(rest, src);
       prefix |= static_cast<uint64_t>(digit) << shift;
       wave_lds_sync();
     }

@@ -8,8 +8,16 @@
 
 namespace vs {
 
-__device__ __forceinline__ double bcast(double v, int src) { return __shfl(v, src, 64); }
-__device__ __forceinline__ int bcast(int v, int src) { return __shfl(v, src, 64); }
+// Value of lane `src` (uniform across the wave) in every lane.  A lane read
+// into a scalar register: no LDS round trip, so sequential loops over the
+// lanes stay short.
+__device__ __forceinline__ double bcast(double v, int src) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffu), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), src));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 // Sequential sum of w over lanes [0, n), lane order, fp64.
 __device__ __forceinline__ double seq_sum(double w, int n) {
