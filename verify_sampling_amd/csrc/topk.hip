@@ -183,9 +183,9 @@ topk_stage2(const float* __restrict__ X, int64_t ldx, int K, int chunks,
 //
 // Lane l holds 64 values of the chunk (element j of the lane is chunk index
 // 256*(j/4) + 4*l + j%4, so every load is a coalesced 1 KB).  The K-th
-// largest of 256 group maxima (16 keys each) is a threshold at least K keys
+// largest of 128 group maxima (32 keys each) is a threshold at least K keys
 // reach (the maxima are distinct keys), so only the keys at or above it can
-// be in the top K.  For ordinary rows they number about a hundred; they
+// be in the top K.  For ordinary rows they number about ninety; they
 // are compacted to LDS and bitonic-sorted across the wave, and the first K
 // are the answer.  If more than CAND survive (adversarial rows), an exact
 // per-wave radix select on the 64-bit keys finds the K-th largest key
@@ -193,7 +193,8 @@ topk_stage2(const float* __restrict__ X, int64_t ldx, int K, int chunks,
 
 constexpr int WAVES = 4;               // wavefronts per workgroup
 constexpr int NPL = CHUNK / 64;        // values per lane
-constexpr int CAND = 256;              // candidates sorted directly (4 per lane)
+constexpr int GROUPS = 2;              // group maxima per lane for the threshold
+constexpr int CAND = 64 * GROUPS;      // candidates sorted directly (GROUPS per lane)
 
 struct WaveShared {
   uint64_t cand[CAND];
@@ -221,18 +222,19 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ int chunk_index(int lane, int j) { return ((j >> 2) << 8) + (lane << 2) + (j & 3); }
 
-// Sorts 256 keys held 4 per lane (element 4*lane + r) in descending order.
-__device__ __forceinline__ void wave_sort256_desc(uint64_t (&k)[4]) {
+// Sorts 64*E keys held E per lane (element E*lane + r) in descending order.
+template <int E>
+__device__ __forceinline__ void wave_sort_desc_n(uint64_t (&k)[E]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int size = 2; size <= 256; size <<= 1) {
+  for (int size = 2; size <= 64 * E; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= 4) {
+      if (stride >= E) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint64_t other = shfl_xor64(k[r], stride >> 2);
-          const int e = 4 * lane + r;
+        for (int r = 0; r < E; ++r) {
+          const uint64_t other = shfl_xor64(k[r], stride / E);
+          const int e = E * lane + r;
           const bool desc = (e & size) == 0;
           const bool lower = (e & stride) == 0;
           const bool take_max = lower == desc;
@@ -240,10 +242,10 @@ __device__ __forceinline__ void wave_sort256_desc(uint64_t (&k)[4]) {
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < E; ++r) {
           if (r & stride) continue;
           const int r2 = r | stride;
-          const int e = 4 * lane + r;
+          const int e = E * lane + r;
           const bool desc = (e & size) == 0;
           const uint64_t a = k[r], b = k[r2];
           const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
@@ -296,17 +298,18 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
                   : 0ull;
   };
 
-  // threshold: the K-th largest of 256 group maxima (each lane's 64 keys in
-  // four groups of 16); the K largest group maxima are K distinct keys.
+  // threshold: the K-th largest of the 64*GROUPS group maxima (each lane's 64
+  // keys in GROUPS runs); the K largest group maxima are K distinct keys.
   // Within a lane the index grows with j, so the first maximal value key in
   // a group has the largest complemented index.
-  uint64_t gmax[4];
+  constexpr int GL = NPL / GROUPS;
+  uint64_t gmax[GROUPS];
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
+  for (int gi = 0; gi < GROUPS; ++gi) {
     uint32_t best = 0;
     int bj = -1;
 #pragma unroll
-    for (int j = 16 * gi; j < 16 * gi + 16; ++j) {
+    for (int j = GL * gi; j < GL * gi + GL; ++j) {
       const bool valid = chunk_index(lane, j) < n;
       if (valid && (bj < 0 || vk[j] > best)) {
         best = vk[j];
@@ -317,12 +320,12 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
                       : ((static_cast<uint64_t>(best) << 32) |
                          static_cast<uint32_t>(~static_cast<uint32_t>(base + chunk_index(lane, bj))));
   }
-  wave_sort256_desc(gmax);
-  // element K-1 of the sorted 256 sits in lane (K-1)/4, slot (K-1)%4
+  wave_sort_desc_n<GROUPS>(gmax);
+  // element K-1 of the sorted maxima sits in lane (K-1)/GROUPS, slot (K-1)%GROUPS
   uint64_t mine = gmax[0];
 #pragma unroll
-  for (int r = 1; r < 4; ++r) mine = ((K - 1) & 3) == r ? gmax[r] : mine;
-  uint64_t thr = shfl64(mine, (K - 1) >> 2);
+  for (int r = 1; r < GROUPS; ++r) mine = ((K - 1) % GROUPS) == r ? gmax[r] : mine;
+  uint64_t thr = shfl64(mine, (K - 1) / GROUPS);
   if (thr == 0) thr = 1;  // fewer than K real keys: take them all
 
   // key(j) >= thr without forming the 64-bit key
@@ -418,16 +421,16 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
   }
   const int pos = count;
   wave_lds_sync();
-  uint64_t k4[4];
+  uint64_t kc[GROUPS];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = 4 * lane + r;
-    k4[r] = e < pos && e < CAND ? sh.cand[e] : 0ull;
+  for (int r = 0; r < GROUPS; ++r) {
+    const int e = GROUPS * lane + r;
+    kc[r] = e < pos && e < CAND ? sh.cand[e] : 0ull;
   }
   wave_lds_sync();
-  wave_sort256_desc(k4);
+  wave_sort_desc_n<GROUPS>(kc);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sh.cand[4 * lane + r] = k4[r];
+  for (int r = 0; r < GROUPS; ++r) sh.cand[GROUPS * lane + r] = kc[r];
   wave_lds_sync();
   if (lane < K) {
     const uint64_t kk = sh.cand[lane];
