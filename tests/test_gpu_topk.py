@@ -114,3 +114,69 @@ def test_batched_multi_chunk_rows_wave_kernel():
     x[1, :] = 3.0
     x[2, 8190:] = 1e30                # maxima in the ragged chunk
     compare(x, 16)
+
+
+def compare_rows(x, K, check):
+    """Runs the whole batch on the GPU; the oracle checks the listed rows."""
+    vals, idx = vs.topk_rows(dev(x), K)
+    gv, gi = host(vals), host(idx)
+    ov, oi = topk_rows(x[check], K)
+    assert np.array_equal(gi[check], oi)
+    assert np.array_equal(gv[check].view(np.uint32), ov.view(np.uint32))
+
+
+def from_bits(b):
+    return np.asarray(b, dtype=np.uint32).view(np.float32)
+
+
+def special_batch(seed, rows=2048, V=4096):
+    g = np.random.default_rng(seed)
+    x = logits(seed, (rows, V))
+    # distinct denormals of both signs: the threshold comparison runs on them
+    mag = g.choice(np.arange(1, 1 << 23, dtype=np.uint32), size=V, replace=False)
+    sign = (g.random(V) < 0.5).astype(np.uint32) << np.uint32(31)
+    x[0] = from_bits(mag | sign)
+    x[1] = x[0]
+    x[1, ::2] = 0.0
+    x[1, 1::4] = -0.0
+    # signalling and negative NaN bit patterns among ordinary values
+    x[2, ::7] = from_bits(0x7F800001)
+    x[3, ::5] = from_bits(0xFFC00000)
+    x[4, 3::11] = from_bits(0x7FBFFFFF)
+    x[4, 5::13] = from_bits(0xFF800001)
+    # NaN apart from a few numbers: fewer than K group maxima are numbers
+    x[5] = np.nan
+    x[5, [5, 900, V - 1]] = [1.0, -2.0, 3.0]
+    x[6] = np.nan
+    x[6, g.choice(V, 100, replace=False)] = g.standard_normal(100).astype(np.float32)
+    x[7] = np.nan
+    x[8] = -np.inf
+    x[8, 17] = np.nan
+    # 70 copies of +inf: ties at the top, ordered by index
+    x[9, g.choice(V, 70, replace=False)] = np.inf
+    # values spread over one lane's groups only
+    x[10] = -1.0
+    x[10, 4 * 9 + 256 * np.arange(16)[:, None] + np.arange(4)[None, :]] = np.arange(64).reshape(16, 4)
+    return x
+
+
+@pytest.mark.parametrize("K", [64, 16, 7, 1])
+def test_batched_wave_kernel_special_values(K):
+    """Denormals, NaN bit patterns, NaN-dominated rows and ties through the
+    wavefront kernel (2048 rows x 4096); the oracle checks the crafted rows
+    and a sample of the ordinary ones."""
+    x = special_batch(1512)
+    check = np.r_[0:16, 16:2048:97]
+    compare_rows(x, K, check)
+
+
+@pytest.mark.parametrize("V,K", [(4106, 64), (4196, 64), (4196, 16), (8192, 64)])
+def test_batched_wave_kernel_ragged_last_chunk(V, K):
+    """1024 rows of two chunks; the last one holds 10 or 100 elements (fewer
+    group maxima than K, or fewer elements than K) or is full."""
+    x = logits(1513 + V + K, (1024, V))
+    x[0, :4096] = np.nan
+    x[1, 4096:] = 1e30
+    x[2, :] = 2.0
+    check = np.r_[0:8, 8:1024:61]
+    compare_rows(x, K, check)

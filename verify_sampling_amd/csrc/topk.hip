@@ -182,36 +182,39 @@ topk_stage2(const float* __restrict__ X, int64_t ldx, int K, int chunks,
 // Stage 1, one wavefront per (row, chunk of up to 4096 elements).
 //
 // Lane l holds 64 values of the chunk (element j of the lane is chunk index
-// 256*(j/4) + 4*l + j%4, so every load is a coalesced 1 KB).  The K-th
-// largest of 128 group maxima (32 keys each) is a threshold at least K keys
-// reach (the maxima are distinct keys), so only the keys at or above it can
-// be in the top K.  For ordinary rows they number about ninety; they
-// are compacted to LDS and bitonic-sorted across the wave, and the first K
-// are the answer.  If more than CAND survive (adversarial rows), an exact
-// per-wave radix select on the 64-bit keys finds the K-th largest key
-// instead.  Either way the result is exact: keys are unique.
+// 256*(j/4) + 4*l + j%4, so every load is a coalesced 1 KB), in four groups
+// of 16.  Steps, each cheap in vector instructions:
+//   1. the float maximum of each group (NaN is skipped or, if signalling,
+//      makes the maximum NaN: either way the group holds an element at
+//      least as large, in key order, as the maximum found);
+//   2. v = the K-th largest value key of the 256 group maxima, by a bitwise
+//      search on ballot counts.  The K groups at or above v hold K distinct
+//      elements of value key >= v, so the top K are among the survivors
+//      "value key >= v", a single float comparison x >= t for t the value
+//      whose key is v (NaN never passes, -0 and +0 compare equal as their
+//      keys do; fp32 denormals are kept, so the comparison is exact);
+//   3. the survivors (about 73 for K = 64 on ordinary rows) are compacted to
+//      LDS as (bits, chunk index) pairs;
+//   4. each survivor's rank is the number of larger 64-bit keys among them;
+//      ranks below K are the output positions.
+// If fewer than K group maxima are real numbers, every valid element
+// survives; if more than CAND survive (adversarial rows), an exact per-wave
+// radix select on the 64-bit keys finds the K-th largest key and only the
+// keys at or above it are compacted.  Either way the result is exact: keys
+// are unique.
 
 constexpr int WAVES = 4;               // wavefronts per workgroup
 constexpr int NPL = CHUNK / 64;        // values per lane
-constexpr int GROUPS = 2;              // group maxima per lane for the threshold
-constexpr int CAND = 64 * GROUPS;      // candidates sorted directly (GROUPS per lane)
+constexpr int GROUPS = 4;              // group maxima per lane
+constexpr int GL = NPL / GROUPS;       // values per group
+constexpr int CAND = 256;              // survivors ranked directly
 
 struct WaveShared {
-  uint64_t cand[CAND];
-  uint32_t hist[256];
+  uint32_t bits[CAND + 1];  // survivors' input bits; slot CAND absorbs overflow writes
+  uint32_t li[CAND + 1];    // survivors' chunk-local indices
+  uint64_t key[CAND];       // survivors' 64-bit keys, zero-padded
+  uint32_t hist[256];       // radix-select histogram (fallback only)
 };
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v & 0xffffffffu), src));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), src));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 
 // Makes this wave's LDS writes visible to its other lanes before they read.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -222,37 +225,81 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ int chunk_index(int lane, int j) { return ((j >> 2) << 8) + (lane << 2) + (j & 3); }
 
-// Sorts 64*E keys held E per lane (element E*lane + r) in descending order.
+// The hardware three-way maximum, without the compiler's NaN quieting of
+// each operand (its effect on NaN is covered by step 1 above).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// The float whose value key is v (v >= 1 and the key of a number).
+__device__ __forceinline__ uint32_t key_bits(uint32_t v) { return (v & 0x80000000u) ? (v ^ 0x80000000u) : ~v; }
+
+// Appends the elements of lane-column j that pass to the survivor list.
+__device__ __forceinline__ void compact_one(WaveShared& sh, int& count, bool take, uint32_t bits, uint32_t li) {
+  const uint64_t m = __ballot(take);
+  if (m == 0) return;  // uniform
+  if (take) {
+    uint32_t slot = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), count));
+    slot = slot < CAND ? slot : CAND;
+    sh.bits[slot] = bits;
+    sh.li[slot] = li;
+  }
+  count += __popcll(m);
+}
+
+// Ranks the c <= 64*E survivors and writes those of rank < K.
 template <int E>
-__device__ __forceinline__ void wave_sort_desc_n(uint64_t (&k)[E]) {
+__device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int base, int chunks,
+                                               int64_t row, int chunk, uint64_t* __restrict__ ws,
+                                               float* __restrict__ out_vals,
+                                               int32_t* __restrict__ out_idx, int64_t ld_out) {
   const int lane = threadIdx.x & 63;
+  uint32_t b[E], l[E];
+  uint64_t k[E];
 #pragma unroll
-  for (int size = 2; size <= 64 * E; size <<= 1) {
+  for (int r = 0; r < E; ++r) {
+    const int s = lane + 64 * r;
+    const bool live = s < c;
+    b[r] = live ? sh.bits[s] : 0u;
+    l[r] = live ? sh.li[s] : 0u;
+    k[r] = live ? ((static_cast<uint64_t>(vs::value_key(b[r])) << 32) |
+                   static_cast<uint32_t>(~static_cast<uint32_t>(base + static_cast<int>(l[r]))))
+                : 0ull;
+    sh.key[s] = k[r];  // empty slots hold 0, which is below every key
+  }
+  wave_lds_sync();
+  int rank[E];
 #pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= E) {
+  for (int r = 0; r < E; ++r) rank[r] = 0;
+  const int cr = (c + 3) & ~3;  // <= 64*E; keys past c are 0
+  for (int s = 0; s < cr; s += 4) {
+    const uint64_t k0 = sh.key[s], k1 = sh.key[s + 1], k2 = sh.key[s + 2], k3 = sh.key[s + 3];
 #pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const uint64_t other = shfl_xor64(k[r], stride / E);
-          const int e = E * lane + r;
-          const bool desc = (e & size) == 0;
-          const bool lower = (e & stride) == 0;
-          const bool take_max = lower == desc;
-          k[r] = take_max ? (other > k[r] ? other : k[r]) : (other < k[r] ? other : k[r]);
-        }
+    for (int r = 0; r < E; ++r)
+      rank[r] += (k0 > k[r]) + (k1 > k[r]) + (k2 > k[r]) + (k3 > k[r]);
+  }
+  const bool single = chunks == 1;
+  int64_t obase = single ? row * ld_out : (row * chunks + chunk) * K;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    if (lane + 64 * r < c && rank[r] < K) {
+      if (single) {
+        out_idx[obase + rank[r]] = base + static_cast<int>(l[r]);
+        out_vals[obase + rank[r]] = __builtin_bit_cast(float, b[r]);  // the input's bits
       } else {
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          if (r & stride) continue;
-          const int r2 = r | stride;
-          const int e = E * lane + r;
-          const bool desc = (e & size) == 0;
-          const uint64_t a = k[r], b = k[r2];
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          k[r] = desc ? hi : lo;
-          k[r2] = desc ? lo : hi;
-        }
+        ws[obase + rank[r]] = k[r];
       }
+    }
+  }
+  if (lane >= c && lane < K) {  // fewer than K elements: empty entries
+    if (single) {
+      out_idx[obase + lane] = -1;
+      out_vals[obase + lane] = __builtin_nanf("");
+    } else {
+      ws[obase + lane] = 0ull;
     }
   }
 }
@@ -273,92 +320,75 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
   const int base = chunk * CHUNK;
   const int n = V - base < CHUNK ? V - base : CHUNK;
 
-  // value keys of the lane's 64 elements (0 for elements past the row's end)
-  uint32_t vk[NPL];
+  // the lane's 64 values; elements past the row's end read as NaN, which no
+  // maximum or threshold comparison selects
+  float x[NPL];
   const bool vec = n == CHUNK && ((reinterpret_cast<uintptr_t>(xrow + base) & 15u) == 0);
   if (vec) {
 #pragma unroll
     for (int q = 0; q < NPL / 4; ++q) {
       const float4 f = *reinterpret_cast<const float4*>(xrow + base + (q << 8) + (lane << 2));
-      vk[4 * q + 0] = vs::value_key(__builtin_bit_cast(uint32_t, f.x));
-      vk[4 * q + 1] = vs::value_key(__builtin_bit_cast(uint32_t, f.y));
-      vk[4 * q + 2] = vs::value_key(__builtin_bit_cast(uint32_t, f.z));
-      vk[4 * q + 3] = vs::value_key(__builtin_bit_cast(uint32_t, f.w));
+      x[4 * q + 0] = f.x;
+      x[4 * q + 1] = f.y;
+      x[4 * q + 2] = f.z;
+      x[4 * q + 3] = f.w;
     }
   } else {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int li = chunk_index(lane, j);
-      vk[j] = li < n ? vs::value_key(__builtin_bit_cast(uint32_t, xrow[base + li])) : 0u;
+      x[j] = li < n ? xrow[base + li] : __builtin_nanf("");
     }
   }
-  auto key = [&](int j) -> uint64_t {
-    const int li = chunk_index(lane, j);
-    return li < n ? ((static_cast<uint64_t>(vk[j]) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(base + li)))
-                  : 0ull;
-  };
 
-  // threshold: the K-th largest of the 64*GROUPS group maxima (each lane's 64
-  // keys in GROUPS runs); the K largest group maxima are K distinct keys.
-  // Within a lane the index grows with j, so the first maximal value key in
-  // a group has the largest complemented index.
-  constexpr int GL = NPL / GROUPS;
-  uint64_t gmax[GROUPS];
+  // 1-2: group maxima and the K-th largest of their value keys
+  uint32_t mk[GROUPS];
 #pragma unroll
-  for (int gi = 0; gi < GROUPS; ++gi) {
-    uint32_t best = 0;
-    int bj = -1;
+  for (int g = 0; g < GROUPS; ++g) {
+    float m = max3f(x[GL * g], x[GL * g + 1], x[GL * g + 2]);
 #pragma unroll
-    for (int j = GL * gi; j < GL * gi + GL; ++j) {
-      const bool valid = chunk_index(lane, j) < n;
-      if (valid && (bj < 0 || vk[j] > best)) {
-        best = vk[j];
-        bj = j;
-      }
-    }
-    gmax[gi] = bj < 0 ? 0ull
-                      : ((static_cast<uint64_t>(best) << 32) |
-                         static_cast<uint32_t>(~static_cast<uint32_t>(base + chunk_index(lane, bj))));
+    for (int i = 3; i + 1 < GL; i += 2) m = max3f(m, x[GL * g + i], x[GL * g + i + 1]);
+    if ((GL - 3) % 2) m = max3f(m, x[GL * g + GL - 1], x[GL * g + GL - 1]);
+    mk[g] = vs::value_key(__builtin_bit_cast(uint32_t, m));
   }
-  wave_sort_desc_n<GROUPS>(gmax);
-  // element K-1 of the sorted maxima sits in lane (K-1)/GROUPS, slot (K-1)%GROUPS
-  uint64_t mine = gmax[0];
+  uint32_t v = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = v | (1u << bit);
+    int c = 0;
 #pragma unroll
-  for (int r = 1; r < GROUPS; ++r) mine = ((K - 1) % GROUPS) == r ? gmax[r] : mine;
-  uint64_t thr = shfl64(mine, (K - 1) / GROUPS);
-  if (thr == 0) thr = 1;  // fewer than K real keys: take them all
+    for (int g = 0; g < GROUPS; ++g) c += __popcll(__ballot(mk[g] >= cand));
+    if (c >= K) v = cand;
+  }
 
-  // key(j) >= thr without forming the 64-bit key
-  auto at_least = [&](int j, uint64_t t) -> bool {
-    const uint32_t th = static_cast<uint32_t>(t >> 32), tl = static_cast<uint32_t>(t);
-    const int li = chunk_index(lane, j);
-    const uint32_t lo = static_cast<uint32_t>(~static_cast<uint32_t>(base + li));
-    return li < n && (vk[j] > th || (vk[j] == th && lo >= tl));
-  };
-  // compact the keys >= thr to LDS while counting them (at most CAND kept)
+  // 3: compaction
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   int count = 0;
+  if (v != 0) {
+    const float t = __builtin_bit_cast(float, key_bits(v));
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const bool take = at_least(j, thr);
-    const uint64_t m = __ballot(take);
-    if (take) {
-      const int slot = count + vs::lanes_below(m);
-      if (slot < CAND) sh.cand[slot] = key(j);
+    for (int j = 0; j < NPL; ++j)
+      compact_one(sh, count, x[j] >= t, __builtin_bit_cast(uint32_t, x[j]),
+                  lane4 | static_cast<uint32_t>(((j >> 2) << 8) | (j & 3)));
+  } else {  // fewer than K group maxima are numbers: every valid element
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int li = chunk_index(lane, j);
+      compact_one(sh, count, li < n, __builtin_bit_cast(uint32_t, x[j]), static_cast<uint32_t>(li));
     }
-    count += __popcll(m);
   }
 
   if (count > CAND) {
-    // exact radix select of the K-th largest key, 8 bits at a time.  This
-    // path is rare (adversarial rows); it re-reads the chunk each pass so that
-    // its keys never occupy registers alongside the main path's.
+    // exact radix select of the K-th largest key, 8 bits at a time (more
+    // than CAND >= K valid keys exist here).  This path is rare (adversarial
+    // rows); it re-reads the chunk each pass so that its keys never occupy
+    // registers alongside the main path's.
     uint64_t prefix = 0;
     int need = K;
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
 #pragma unroll
-      for (int b = 0; b < 4; ++b) sh.hist[4 * lane + b] = 0u;
+      for (int bb = 0; bb < 4; ++bb) sh.hist[4 * lane + bb] = 0u;
       wave_lds_sync();
       asm volatile("" ::: "memory");  // keep the re-reads inside this pass
       for (int j = 0; j < NPL; ++j) {
@@ -372,13 +402,13 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
       wave_lds_sync();
       uint32_t c[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) c[b] = sh.hist[255 - 4 * lane - b];
+      for (int bb = 0; bb < 4; ++bb) c[bb] = sh.hist[255 - 4 * lane - bb];
       const uint32_t sum = c[0] + c[1] + c[2] + c[3];
       uint32_t incl = sum;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
+        const uint32_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
       }
       const uint32_t excl = incl - sum;
       const bool mine = excl < static_cast<uint32_t>(need) && static_cast<uint32_t>(need) <= incl;
@@ -386,13 +416,13 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
       if (mine) {
         uint32_t cum = excl;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (cum + c[b] >= static_cast<uint32_t>(need)) {
-            digit = 255 - 4 * lane - b;
+        for (int bb = 0; bb < 4; ++bb) {
+          if (cum + c[bb] >= static_cast<uint32_t>(need)) {
+            digit = 255 - 4 * lane - bb;
             rest = need - static_cast<int>(cum);
             break;
           }
-          cum += c[b];
+          cum += c[bb];
         }
       }
       const int src = __ffsll(static_cast<long long>(__ballot(mine))) - 1;
@@ -401,49 +431,29 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
       prefix |= static_cast<uint64_t>(digit) << shift;
       wave_lds_sync();
     }
-    thr = prefix;  // exactly K keys are >= thr: compact them again
+    // exactly K keys are >= prefix: compact them again
     count = 0;
     asm volatile("" ::: "memory");
     for (int j = 0; j < NPL; ++j) {
       const int li = chunk_index(lane, j);
+      uint32_t bits = 0;
       uint64_t kj = 0;
-      if (li < n)
-        kj = (static_cast<uint64_t>(vs::value_key(__builtin_bit_cast(uint32_t, xrow[base + li]))) << 32) |
-             static_cast<uint32_t>(~static_cast<uint32_t>(base + li));
-      const bool take = kj != 0 && kj >= thr;
-      const uint64_t m = __ballot(take);
-      if (take) {
-        const int slot = count + vs::lanes_below(m);
-        if (slot < CAND) sh.cand[slot] = kj;
+      if (li < n) {
+        bits = __builtin_bit_cast(uint32_t, xrow[base + li]);
+        kj = (static_cast<uint64_t>(vs::value_key(bits)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(base + li));
       }
-      count += __popcll(m);
+      compact_one(sh, count, kj != 0 && kj >= prefix, bits, static_cast<uint32_t>(li));
     }
   }
-  const int pos = count;
+
+  // 4: ranks and output
   wave_lds_sync();
-  uint64_t kc[GROUPS];
-#pragma unroll
-  for (int r = 0; r < GROUPS; ++r) {
-    const int e = GROUPS * lane + r;
-    kc[r] = e < pos && e < CAND ? sh.cand[e] : 0ull;
-  }
-  wave_lds_sync();
-  wave_sort_desc_n<GROUPS>(kc);
-#pragma unroll
-  for (int r = 0; r < GROUPS; ++r) sh.cand[GROUPS * lane + r] = kc[r];
-  wave_lds_sync();
-  if (lane < K) {
-    const uint64_t kk = sh.cand[lane];
-    if (chunks == 1) {
-      // a single-chunk row has V >= K real keys, so kk is never the empty key
-      const uint32_t idx = vs::key_index(kk);
-      const bool real = kk != 0;
-      out_idx[static_cast<int64_t>(row) * ld_out + lane] = real ? static_cast<int32_t>(idx) : -1;
-      out_vals[static_cast<int64_t>(row) * ld_out + lane] = real ? xrow[idx] : __builtin_nanf("");
-    } else {
-      ws[(static_cast<int64_t>(row) * chunks + chunk) * K + lane] = kk;
-    }
-  }
+  if (count <= 64)
+    rank_and_write<1>(sh, count, K, base, chunks, row, chunk, ws, out_vals, out_idx, ld_out);
+  else if (count <= 128)
+    rank_and_write<2>(sh, count, K, base, chunks, row, chunk, ws, out_vals, out_idx, ld_out);
+  else
+    rank_and_write<4>(sh, count, K, base, chunks, row, chunk, ws, out_vals, out_idx, ld_out);
 }
 
 int n_chunks(int V) { return (V + CHUNK - 1) / CHUNK; }
