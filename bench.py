@@ -126,14 +126,23 @@ class VerifyPass:
         return len(self.mats) + 1
 
     def _args(self, R):
-        """C-ABI arguments of every projection launch at R rows (pointers cached)."""
+        """C-ABI arguments of every projection launch at R rows (pointers cached).
+
+        The launches run in order on one stream, so they share one workspace
+        sized for the largest of them.
+        """
         if R not in self._arg_cache:
+            mats = self.mats + [(self.head, self.head_x, self.logits)]
+            nbytes = max(self.vs.verify_gemv_rows_workspace_bytes(W.shape[0], W.shape[1], R)
+                         for W, _, _ in mats)
+            ws = self.torch.empty(max(nbytes, 16), dtype=self.torch.uint8, device=self.dev)
             out = []
-            for W, X, Y in self.mats + [(self.head, self.head_x, self.logits)]:
+            for W, X, Y in mats:
                 N, K = W.shape
-                out.append((W.data_ptr(), K, N, K, X.data_ptr(), K, R, Y.data_ptr(), N))
-            self._arg_cache[R] = out
-        return self._arg_cache[R]
+                out.append((W.data_ptr(), K, N, K, X.data_ptr(), K, R, Y.data_ptr(), N,
+                            ws.data_ptr(), nbytes))
+            self._arg_cache[R] = (out, ws)
+        return self._arg_cache[R][0]
 
     def projections(self, R):
         """The R-row projections of the stack and the LM head, in pass order."""

@@ -48,7 +48,7 @@ enum vs_status {
   VS_ERR_HIP = -7          /* the HIP runtime reported an error at launch    */
 };
 
-#define VS_ABI_VERSION 1
+#define VS_ABI_VERSION 2
 #define VS_MAX_ROWS 24     /* verify rows R = k + 1 per projection call      */
 #define VS_POOL 64         /* width of the sampler's candidate pool          */
 #define VS_MAX_WINDOW 4096 /* longest penalty window                         */
@@ -73,17 +73,26 @@ const char* vs_last_error_detail(void);
  *   Y[r][n] = sum_k W[n][k] * X[r][k],  0 <= r < R, 0 <= n < N,
  * with bf16 weights, fp32 activations and fp32 accumulation.  Row r of the
  * result is bit-identical to the result of the same call with R = 1 and
- * X = row r: the summation order depends only on N and K.
+ * X = row r: the summation order depends only on N and K.  It also does
+ * not depend on the workspace: with or without one the bits are the same.
  *
  *   W    bf16 bit patterns, row-major [N][ldw] (nn.Linear layout, out x in);
  *        16-byte aligned, ldw % 8 == 0, ldw >= K.
  *   X    fp32 [R][ldx]; 16-byte aligned, ldx % 4 == 0, ldx >= K.
- *   Y    fp32 [R][ldy]; ldy >= N.  Must not overlap W or X.
+ *   Y    fp32 [R][ldy]; ldy >= N.  Must not overlap W, X or the workspace.
  *   N >= 1, 1 <= K with K % 8 == 0, 1 <= R <= VS_MAX_ROWS.
+ *   workspace  optional device scratch (16-byte aligned) of at least
+ *        verify_gemv_rows_workspace_bytes(N, K, R) bytes.  Some (N, K, R)
+ *        run faster with it (partial sums of K partitions are kept there
+ *        between two launches); NULL, or a smaller or misaligned buffer,
+ *        selects a single-launch path with the same result.  Its contents
+ *        on entry do not matter and are overwritten.
  */
+size_t verify_gemv_rows_workspace_bytes(int N, int K, int R);
 int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K,
                      const float* X, int64_t ldx, int R,
-                     float* Y, int64_t ldy, hipStream_t stream);
+                     float* Y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * penalize_rows: windowed repeat / frequency / presence penalties, in place.

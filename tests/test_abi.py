@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = vs.library()
-    assert lib.vs_abi_version() == 1
+    assert lib.vs_abi_version() == 2
     assert lib.vs_status_string(0) == b"ok"
     for code in range(-7, 0):
         assert lib.vs_status_string(code) != b"unknown status"
@@ -44,12 +44,19 @@ FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
 
 def test_gemv_rejects_before_launch():
     lib = vs.library()
-    assert lib.verify_gemv_rows(None, 8, 4, 8, FAKE, 8, 1, FAKE, 4, None) == -1
-    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 0, FAKE, 4, None) == -2      # R = 0
-    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 25, FAKE, 4, None) == -2     # R > 24
-    assert lib.verify_gemv_rows(FAKE, 12, 4, 12, FAKE, 12, 1, FAKE, 4, None) == -2   # K % 8
-    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 1, FAKE, 3, None) == -2      # ldy < N
-    assert lib.verify_gemv_rows(ctypes.c_void_p(0x100008), 8, 4, 8, FAKE, 8, 1, FAKE, 4, None) == -6
+    assert lib.verify_gemv_rows(None, 8, 4, 8, FAKE, 8, 1, FAKE, 4, None, 0, None) == -1
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 0, FAKE, 4, None, 0, None) == -2      # R = 0
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 25, FAKE, 4, None, 0, None) == -2     # R > 24
+    assert lib.verify_gemv_rows(FAKE, 12, 4, 12, FAKE, 12, 1, FAKE, 4, None, 0, None) == -2   # K % 8
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 1, FAKE, 3, None, 0, None) == -2      # ldy < N
+    assert lib.verify_gemv_rows(ctypes.c_void_p(0x100008), 8, 4, 8, FAKE, 8, 1, FAKE, 4, None, 0, None) == -6
+    # the workspace is optional; its size is zero where no path uses one
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 4) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(151936, 4096, 24) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 4) == 0
+    # 4096 x 12288 at 16 rows: 8 K partitions of 16 x 4096 fp32 partial sums
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 16) == 8 * 16 * 4096 * 4
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 25) == 0
 
 
 def test_topk_rejects_before_launch():

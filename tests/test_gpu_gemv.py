@@ -118,3 +118,27 @@ def test_strided_operands():
     y = host(Y)
     check(y[:, :300], w, x)
     assert (y[:, 300:] == -7.0).all()
+
+
+@pytest.mark.parametrize("N,K", [(65573, 1064), (6151, 4104), (24576, 4096), (4096, 12288),
+                                 (6144, 4096)])
+def test_shared_activation_paths_bit_identical(N, K):
+    """From 9 rows on, wide matrices (N >= 65536) and matrices of >= 48 MB run
+    the shared-activation kernels (the latter with a workspace of K-partition
+    partial sums).  Their rows equal the 1-row call bit for bit, with the
+    workspace and without it, and match the oracle.  Ragged N and a partial
+    last k-block are included."""
+    W = torch_bf16_weights((N, K), 3000 + N % 97 + K % 89, "cuda:0")
+    x = np.random.default_rng(3100 + N % 97).standard_normal((24, K)).astype(np.float32)
+    X = dev(x)
+    single = np.stack([host(vs.verify_gemv_rows(W, X[r:r + 1]))[0] for r in range(24)])
+    for R in (9, 12, 16, 17, 24):
+        y = host(vs.verify_gemv_rows(W, X[:R].contiguous()))
+        assert np.array_equal(y.view(np.uint32), single[:R].view(np.uint32)), f"R={R}"
+        y0 = host(vs.verify_gemv_rows(W, X[:R].contiguous(), workspace=None))
+        assert np.array_equal(y0.view(np.uint32), y.view(np.uint32)), f"R={R} without workspace"
+    rows = sampled_rows(N, 800, 3200 + N % 97)
+    w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
+    ref, s = gemv_rows(w_rows, x)
+    err = np.abs(y[:, rows].astype(np.float64) - ref)
+    assert (err <= TOL * s).all()

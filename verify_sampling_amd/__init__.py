@@ -22,6 +22,7 @@ __all__ = [
     "VerifySamplingError",
     "library",
     "verify_gemv_rows",
+    "verify_gemv_rows_workspace_bytes",
     "penalize_rows",
     "topk_rows",
     "topk_rows_workspace_bytes",
@@ -43,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "vs_abi_version",
     "vs_status_string",
     "vs_last_error_detail",
+    "verify_gemv_rows_workspace_bytes",
     "verify_gemv_rows",
     "penalize_rows",
     "topk_rows_workspace_bytes",
@@ -67,7 +69,8 @@ _SIGNATURES = {
     "vs_abi_version": ([], I32),
     "vs_status_string": ([I32], ctypes.c_char_p),
     "vs_last_error_detail": ([], ctypes.c_char_p),
-    "verify_gemv_rows": ([P, I64, I32, I32, P, I64, I32, P, I64, P], I32),
+    "verify_gemv_rows_workspace_bytes": ([I32, I32, I32], SZ),
+    "verify_gemv_rows": ([P, I64, I32, I32, P, I64, I32, P, I64, P, SZ, P], I32),
     "penalize_rows": ([P, P, I64, I32, I32, I32, P, I32, P, I32, I32, F32, F32, F32, P], I32),
     "topk_rows_workspace_bytes": ([I32, I32, I32], SZ),
     "topk_rows": ([P, I64, I32, I32, I32, P, P, I64, P, SZ, P], I32),
@@ -133,11 +136,18 @@ def _ld(t, name):
     return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
 
 
-def verify_gemv_rows(W, X, Y=None, stream=None):
+def verify_gemv_rows_workspace_bytes(N: int, K: int, R: int) -> int:
+    """Bytes of the optional workspace that lets verify_gemv_rows take its fastest path."""
+    return int(library().verify_gemv_rows_workspace_bytes(N, K, R))
+
+
+def verify_gemv_rows(W, X, Y=None, stream=None, workspace="auto"):
     """Y[R][N] = X[R][K] @ W[N][K]^T with bf16 W, fp32 X and fp32 accumulation.
 
     W: torch.bfloat16 [N][K] (or int16/uint16 holding bf16 bits); X: float32
-    [R][K]; Y: optional float32 [R][N] output.  Returns Y.
+    [R][K]; Y: optional float32 [R][N] output.  workspace: "auto" allocates
+    the optional workspace when the call can use one, None runs without it
+    (same bits), or a uint8 device tensor.  Returns Y.
     """
     import torch
 
@@ -153,9 +163,17 @@ def verify_gemv_rows(W, X, Y=None, stream=None):
         Y = torch.empty((R, N), dtype=torch.float32, device=X.device)
     if tuple(Y.shape) != (R, N):
         raise VerifySamplingError(f"Y must be [{R}][{N}]")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise VerifySamplingError('workspace must be "auto", None or a uint8 tensor')
+        nbytes = verify_gemv_rows_workspace_bytes(N, K, R)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device) if nbytes else None
+    ws_ptr = _ptr(workspace, torch.uint8, "workspace", allow_none=True)
+    ws_bytes = workspace.numel() if workspace is not None else 0
     st = library().verify_gemv_rows(_ptr(W, torch.bfloat16, "W"), _ld(W, "W"), N, K,
                                     _ptr(X, torch.float32, "X"), _ld(X, "X"), R,
-                                    _ptr(Y, torch.float32, "Y"), _ld(Y, "Y"), _stream(stream))
+                                    _ptr(Y, torch.float32, "Y"), _ld(Y, "Y"), ws_ptr, ws_bytes,
+                                    _stream(stream))
     _check(st, "verify_gemv_rows")
     return Y
 

@@ -23,8 +23,22 @@
 //    per-wave partial sums are added in wave order.  None of this depends on
 //    R or on the column a row lands in, so row r of an R-row call equals the
 //    1-row call on X[r] bit for bit.
-//  * Workgroup = `splits` wavefronts over T 16-row tiles; wave w owns
-//    k-blocks [w*nkb/splits, (w+1)*nkb/splits).  Partial sums meet in LDS.
+//  * K is cut into `splits` partitions [s*nkb/splits, (s+1)*nkb/splits) of
+//    32-wide k-blocks, a function of N and K alone.  Each partition is
+//    accumulated from zero in increasing k order, and the partition sums
+//    are added left to right.  Every kernel below follows exactly this
+//    order, so they all give the same bits and may be chosen per R.
+//  * Row-block kernel: workgroup = `splits` wavefronts over T 16-row tiles;
+//    wave w owns partition w; partial sums meet in LDS.  Every wave loads
+//    and splits the activations of its partition itself.
+//  * Shared-activation kernels (R > 8): a workgroup of P wavefronts along N
+//    loads each activation tile once, splits it once into the three bf16
+//    planes in LDS, and all P waves read their MFMA operand from there.
+//    This divides the activation traffic per weight byte by P, which is what
+//    makes a row-block pass slow down with R.  Either every wave walks all
+//    of K and adds its partition sums in registers (wide matrices), or each
+//    workgroup takes one partition (grid.y) and writes its partial sums to a
+//    caller workspace, which a second small kernel adds in partition order.
 
 #include "vs_internal.h"
 
@@ -251,6 +265,220 @@ gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
   }
 }
 
+// Activations of one pipeline stage in the MFMA B-operand layout, split into
+// three bf16 planes: [U k-blocks][hi, mid, lo][CT column tiles][64 lanes].
+template <int U, int CT>
+struct XTile {
+  u32x4 v[U][3][CT][64];
+};
+
+// Shared-activation kernel.  Workgroup = P wavefronts; wave p owns the T
+// 16-row tiles starting at row (blockIdx.x * P + p) * 16 * T.  SPLITK: the
+// workgroup takes partition blockIdx.y and writes its partial sums to
+// parts[(s * R + r) * ldp + n]; otherwise each wave walks all partitions and
+// writes Y.  Stage s + 1 (weights in registers, activations split into the
+// other LDS buffer) is loaded while stage s is computed.
+template <int T, int U, int CT, int P, bool SPLITK>
+__global__ void __launch_bounds__(64 * P)
+gemv_shared_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
+                   const float* __restrict__ X, int64_t ldx, int R, float* __restrict__ Y,
+                   int64_t ldy, float* __restrict__ parts, int64_t ldp, int nkb, int splits) {
+  __shared__ XTile<U, CT> xs[2];
+  constexpr int IMG = U * CT;             // activation images (one k-block, one column tile) per stage
+  constexpr int IPW = (IMG + P - 1) / P;  // images each wave loads and splits
+  const int lane = threadIdx.x & 63;
+  const int p = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int n0 = (blockIdx.x * P + p) * TILE * T;
+  int kb0 = 0, kb1 = nkb;
+  if (SPLITK) {
+    kb0 = static_cast<int>((static_cast<int64_t>(blockIdx.y) * nkb) / splits);
+    kb1 = static_cast<int>((static_cast<int64_t>(blockIdx.y + 1) * nkb) / splits);
+  }
+
+  const uint16_t* wrow[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    int wr = n0 + t * TILE + col;
+    if (wr >= N) wr = N - 1;  // ragged tile: load a valid row, discard its results
+    wrow[t] = W + static_cast<int64_t>(wr) * ldw + g * 8;
+  }
+  f32x4 acc[T][CT], y[T][CT];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      y[t][c] = acc[t][c];
+    }
+
+  auto load_w = [&](u32x4 (&w)[U][T], int kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = kb + u < kb1 && (kb + u) * KBLK + g * 8 < K;  // K % 8 == 0
+      const int64_t off = static_cast<int64_t>(kb + u) * KBLK;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        w[u][t] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto load_x = [&](float (&x)[IPW][8], int kb) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int img = p + i * P;
+      const int u = img / CT, c = img % CT;
+      const int r = c * 16 + col;
+      const int k = (kb + u) * KBLK + g * 8;
+      if (img < IMG && kb + u < kb1 && k < K && r < R) {
+        const float* src = X + static_cast<int64_t>(r) * ldx + k;
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        x[i][0] = a.x; x[i][1] = a.y; x[i][2] = a.z; x[i][3] = a.w;
+        x[i][4] = b.x; x[i][5] = b.y; x[i][6] = b.z; x[i][7] = b.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+      }
+    }
+  };
+  auto store_x = [&](const float (&x)[IPW][8], int buf) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int img = p + i * P;
+      if (img < IMG) {
+        const int u = img / CT, c = img % CT;
+        u32x4 hi, mid, lo;
+        split3(x[i], hi, mid, lo);
+        xs[buf].v[u][0][c][lane] = hi;
+        xs[buf].v[u][1][c][lane] = mid;
+        xs[buf].v[u][2][c][lane] = lo;
+      }
+    }
+  };
+  // all-K mode: partition `part` ends at k-block `bound`; its sum is added
+  // into y (left to right) and the accumulator restarts from zero
+  int part = 0;
+  int bound = static_cast<int>(static_cast<int64_t>(nkb) / splits);
+  auto flush_to = [&](int kb) {
+    while (part < splits && bound <= kb) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          y[t][c] = part == 0 ? acc[t][c] : y[t][c] + acc[t][c];
+          acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      ++part;
+      bound = static_cast<int>((static_cast<int64_t>(part + 1) * nkb) / splits);
+    }
+  };
+
+  u32x4 w[U][T];
+  float x[IPW][8];
+  load_w(w, kb0);
+  load_x(x, kb0);
+  store_x(x, 0);
+  __syncthreads();
+  if (!SPLITK) flush_to(kb0);
+  int buf = 0;
+  for (int kb = kb0; kb < kb1; kb += U) {  // uniform over the workgroup
+    const bool more = kb + U < kb1;
+    u32x4 wn[U][T];
+    if (more) {
+      load_x(x, kb + U);
+      load_w(wn, kb + U);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb + u >= kb1) break;
+      if (!SPLITK && kb + u == bound) flush_to(kb + u);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const u32x4 hi = xs[buf].v[u][0][c][lane];
+        const u32x4 mid = xs[buf].v[u][1][c][lane];
+        const u32x4 lo = xs[buf].v[u][2][c][lane];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          acc[t][c] = mfma(w[u][t], hi, acc[t][c]);
+          acc[t][c] = mfma(w[u][t], mid, acc[t][c]);
+          acc[t][c] = mfma(w[u][t], lo, acc[t][c]);
+        }
+      }
+    }
+    if (more) {
+      store_x(x, buf ^ 1);  // the other buffer was last read before the previous barrier
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < T; ++t) w[u][t] = wn[u][t];
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // MFMA 16x16 output layout: lane l, element e holds weight row 4*(l/16)+e
+  // of the tile and activation row l%16 of the column tile.
+  if (SPLITK) {
+    const int64_t pbase = static_cast<int64_t>(blockIdx.y) * R;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int r = c * 16 + col;
+        const int n = n0 + t * TILE + 4 * g;
+        if (r >= R || n >= N) continue;
+        float* dst = parts + (pbase + r) * ldp + n;
+        if (n + 3 < N) {
+          *reinterpret_cast<f32x4*>(dst) = acc[t][c];  // ldp % 4 == 0, n % 4 == 0
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) dst[e] = acc[t][c][e];
+        }
+      }
+  } else {
+    flush_to(kb1);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int r = c * 16 + col;
+        const int n = n0 + t * TILE + 4 * g;
+        if (r >= R) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) Y[static_cast<int64_t>(r) * ldy + n + e] = y[t][c][e];
+      }
+  }
+}
+
+// Y[r][n..n+3] = the partition sums of parts added left to right.  All
+// partition loads are issued before the first add (the add order is fixed,
+// the load order is not), so the kernel costs one memory round trip.
+constexpr int MAX_SPLITS = 16;
+
+__global__ void __launch_bounds__(256)
+reduce_partials_kernel(const float* __restrict__ parts, int64_t ldp, int splits, int R, int N,
+                       float* __restrict__ Y, int64_t ldy) {
+  const int r = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= N) return;
+  f32x4 v[MAX_SPLITS];
+#pragma unroll
+  for (int q = 0; q < MAX_SPLITS; ++q)
+    if (q < splits)  // ldp % 4 == 0 and n % 4 == 0: 16-byte aligned, inside the row's ldp
+      v[q] = *reinterpret_cast<const f32x4*>(parts + (static_cast<int64_t>(q) * R + r) * ldp + n);
+  f32x4 s = v[0];
+#pragma unroll
+  for (int q = 1; q < MAX_SPLITS; ++q)
+    if (q < splits) s += v[q];
+  float* dst = Y + static_cast<int64_t>(r) * ldy + n;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (n + e < N) dst[e] = s[e];
+}
+
 // Waves per workgroup (the k-split): a function of N and K alone, so that
 // the summation order of a row does not change with R.  Wide matrices (many
 // row tiles) do best with few, long waves; narrower ones split K further
@@ -260,27 +488,95 @@ int splits_for(int N, int K) {
   int s = (N >= 16384) ? (nkb + 31) / 32 : (nkb + 15) / 16;
   if (s < 1) s = 1;
   if (s > (N >= 16384 ? 16 : 8)) s = (N >= 16384 ? 16 : 8);
-  return s;
+  return s;  // <= MAX_SPLITS
+}
+
+// Which kernel runs for (N, K, R).  Chosen by sweeps on MI355X: up to 8
+// rows the row-block kernel is fastest; from 9 rows on, activation traffic
+// dominates it and the shared-activation kernels take over (all-K for very
+// wide matrices, partitions across workgroups for matrices of >= 48 MB);
+// small matrices stay on the row-block kernel, whose launch is cheapest.
+enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK };
+
+Kind kind_for(int N, int K, int R) {
+  if (R <= 8) return Kind::kRowBlock;
+  if (N >= 65536) return Kind::kSharedAllK;
+  if (2.0 * N * K >= 48e6) return Kind::kSharedSplitK;
+  return Kind::kRowBlock;
+}
+
+int64_t parts_ld(int N) { return (static_cast<int64_t>(N) + 3) & ~int64_t{3}; }
+
+size_t split_workspace_bytes(int N, int K, int R) {
+  return static_cast<size_t>(splits_for(N, K)) * R * parts_ld(N) * sizeof(float);
 }
 
 }  // namespace
 
+extern "C" size_t verify_gemv_rows_workspace_bytes(int N, int K, int R) {
+  if (N < 1 || K < 1 || R < 1 || R > VS_MAX_ROWS) return 0;
+  return kind_for(N, K, R) == Kind::kSharedSplitK ? split_workspace_bytes(N, K, R) : 0;
+}
+
 extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, const float* X,
-                                int64_t ldx, int R, float* Y, int64_t ldy, hipStream_t stream) {
+                                int64_t ldx, int R, float* Y, int64_t ldy, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   if (!W || !X || !Y) return VS_ERR_NULL;
   if (N < 1 || K < 1 || R < 1 || R > VS_MAX_ROWS) return VS_ERR_SHAPE;
   if (K % 8 != 0 || ldw < K || ldx < K || ldy < N) return VS_ERR_SHAPE;
   if (ldw % 8 != 0 || ldx % 4 != 0 || !vs::aligned16(W) || !vs::aligned16(X)) return VS_ERR_ALIGN;
-  if (static_cast<int64_t>(N) > (int64_t{1} << 31) - TILE) return VS_ERR_SHAPE;
+  if (static_cast<int64_t>(N) > (int64_t{1} << 31) - 1024) return VS_ERR_SHAPE;
 
   const int nkb = (K + KBLK - 1) / KBLK;
   const int splits = splits_for(N, K);
+  Kind kind = kind_for(N, K, R);
+  // without a (large enough, aligned) workspace the row-block kernel runs:
+  // same summation order, same bits
+  if (kind == Kind::kSharedSplitK &&
+      (!workspace || workspace_bytes < split_workspace_bytes(N, K, R) || !vs::aligned16(workspace)))
+    kind = Kind::kRowBlock;
+
+  if (kind == Kind::kSharedAllK) {
+    auto launch = [&](auto kernel, int T, int P) {
+      const dim3 grid((N + TILE * T * P - 1) / (TILE * T * P));
+      kernel<<<grid, dim3(64 * P), 0, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nullptr, 0, nkb,
+                                                splits);
+    };
+    if (R <= 16) launch(gemv_shared_kernel<2, 4, 1, 2, false>, 2, 2);
+    else launch(gemv_shared_kernel<1, 2, 2, 8, false>, 1, 8);
+    return vs::check_launch();
+  }
+  if (kind == Kind::kSharedSplitK) {
+    float* parts = static_cast<float*>(workspace);
+    const int64_t ldp = parts_ld(N);
+    auto launch = [&](auto kernel, int T, int P) {
+      const dim3 grid((N + TILE * T * P - 1) / (TILE * T * P), splits);
+      kernel<<<grid, dim3(64 * P), 0, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, parts, ldp, nkb,
+                                                splits);
+    };
+    if (R <= 16) {
+      if (N >= 16384) launch(gemv_shared_kernel<1, 2, 1, 8, true>, 1, 8);
+      else if (K >= 8192) launch(gemv_shared_kernel<1, 4, 1, 2, true>, 1, 2);
+      else launch(gemv_shared_kernel<1, 4, 1, 4, true>, 1, 4);
+    } else {
+      if (N >= 16384) launch(gemv_shared_kernel<1, 2, 2, 8, true>, 1, 8);
+      else launch(gemv_shared_kernel<1, 2, 2, 4, true>, 1, 4);
+    }
+    int st = vs::check_launch();
+    if (st != VS_OK) return st;
+    const int quads = static_cast<int>((N + 3) / 4);
+    reduce_partials_kernel<<<dim3((quads + 255) / 256, R), dim3(256), 0, stream>>>(parts, ldp, splits,
+                                                                                   R, N, Y, ldy);
+    return vs::check_launch();
+  }
+
   const dim3 block(64 * splits);
-  // Tile shape by matrix shape and R (it never changes a row's summation
-  // order): taller matrices take more row tiles per wave, which divides the
-  // activation traffic and the splitting work per weight; "activations
-  // first" issues a stage's activation loads ahead of its weights so that
-  // their split overlaps the weight latency.  Chosen by a sweep on MI355X.
+  // Row-block tile shape by matrix shape and R (it never changes a row's
+  // summation order): taller matrices take more row tiles per wave, which
+  // divides the activation traffic and the splitting work per weight;
+  // "activations first" issues a stage's activation loads ahead of its
+  // weights so that their split overlaps the weight latency.  Chosen by a
+  // sweep on MI355X.
   auto launch = [&](auto kernel, int T, int CT) {
     const dim3 grid((N + TILE * T - 1) / (TILE * T));
     const size_t shm = static_cast<size_t>(splits) * T * CT * 256 * sizeof(float);
@@ -293,9 +589,9 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
     else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 1, false, true>, 2, 1);
     else launch(gemv_rows_kernel<1, 4, 1, false, true>, 1, 1);
   } else {
-    if (N >= 65536) launch(gemv_rows_kernel<4, 1, 2, false, false>, 4, 2);
-    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 2, false, false>, 2, 2);
-    else launch(gemv_rows_kernel<1, 2, 2, true, false>, 1, 2);
+    if (N >= 65536) launch(gemv_rows_kernel<4, 1, 2, false, true>, 4, 2);
+    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 2, false, true>, 2, 2);
+    else launch(gemv_rows_kernel<1, 2, 2, false, true>, 1, 2);
   }
   return vs::check_launch();
 }
