@@ -93,3 +93,26 @@ def test_special_values_and_empty_slots():
     ], dtype=np.int32)
     compare(vals, ids, uniforms(1708, 6), **CFG)
     compare(vals, ids, uniforms(1709, 6), temperature=1.0, top_k=0, top_p=1.0, min_p=0.0)
+
+
+def test_presorted_and_shuffled_pools_agree():
+    """A pool already in pool order (as topk_rows leaves it) skips the sort;
+    the same candidates in any other order give the same distribution and
+    draw bit for bit.  NaN, -inf and trailing empty slots included."""
+    x = logits(1710, (64, 4096))
+    x[0, :4000] = np.nan
+    x[1, ::2] = -np.inf
+    x[2, :] = 1.5
+    pv, pi = topk_rows(x, 64)
+    pi = pi.copy()
+    pi[3, 40:] = -1          # trailing empty slots
+    pi[4, 1:] = -1
+    u = uniforms(1711, 64)
+    for cfg in (CFG, dict(temperature=1.0, top_k=0, top_p=0.9, min_p=0.0)):
+        a = run(pv, pi, u, **cfg)
+        g = np.random.default_rng(1712)
+        perm = np.stack([g.permutation(64) for _ in range(64)])
+        b = run(np.take_along_axis(pv, perm, axis=1), np.take_along_axis(pi, perm, axis=1), u, **cfg)
+        for ga, gb in zip(a, b):
+            assert np.array_equal(np.asarray(ga).view(np.uint32), np.asarray(gb).view(np.uint32))
+        compare(pv, pi, u, **cfg)

@@ -6,13 +6,22 @@
 // draft's re-scored candidates).
 //
 // One 64-lane wave per row, one candidate per lane.  The candidates are
-// bitonic-sorted into pool order by their 64-bit order key; the weights
-// exp((l_j - l_0)/T) are computed lane-parallel in fp64; every sum the
-// result depends on is taken sequentially in pool order (all lanes walk the
-// same shuffle sequence), so the distribution does not depend on the
-// hardware's reduction order.  Both filters compare ratios of weights and
-// are evaluated on the unnormalised weights; the kept weights are normalised
-// once and rounded to fp32.
+// bitonic-sorted into pool order by their 64-bit order key (skipped when
+// they already are in that order, as topk_rows leaves them); the weights
+// exp((l_j - l_0)/T) are computed lane-parallel in fp64.  Every sum the
+// result depends on is taken sequentially in pool order, so the
+// distribution does not depend on the hardware's reduction order.  Both
+// filters compare ratios of weights and are evaluated on the unnormalised
+// weights; the kept weights are normalised once and rounded to fp32.
+//
+// One sequential prefix scan over the min-p survivors' weights (zero for
+// the others; adding +0.0 to a non-negative sum is exact) gives every sum
+// the policy needs: its total is the top-p reference sum, the exclusive
+// prefix at a candidate is the mass kept before it (the scan is
+// non-decreasing, so the top-p survivors are the min-p survivors up to the
+// first failure, plus always the first one), and the inclusive prefix at
+// the last top-p survivor is the normaliser.  Each of these equals the
+// corresponding separate left-to-right sum bit for bit.
 
 #include "wave_ops.h"
 
@@ -39,7 +48,12 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
     const int32_t id = irow[lane];
     if (id >= 0) key = vs::order_key(vbits, static_cast<uint32_t>(id));
   }
-  vs::wave_sort_desc(key, vbits);  // lane j now holds the j-th candidate in pool order
+  // already in pool order (descending keys, empty slots last)?  Keys are
+  // unique, so this holds exactly when no lane is below its successor.
+  const uint32_t next_lo = __shfl_down(static_cast<uint32_t>(key), 1, 64);
+  const uint32_t next_hi = __shfl_down(static_cast<uint32_t>(key >> 32), 1, 64);
+  const uint64_t next = lane == 63 ? 0ull : ((static_cast<uint64_t>(next_hi) << 32) | next_lo);
+  if (__ballot(key < next) != 0) vs::wave_sort_desc(key, vbits);  // lane j: the j-th candidate
   const bool real = key != 0;
   const int n_real = __popcll(__ballot(real));
   const int32_t tok = real ? static_cast<int32_t>(vs::key_index(key)) : -1;
@@ -70,30 +84,24 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
       if (!one_hot) {
         // weight-0 candidates carry no mass; min-p relative to the first
         const bool keep1 = e > 0.0 && e >= static_cast<double>(min_p) * e0;
-        const double tp = static_cast<double>(top_p);
-        // only the first nk lanes can carry weight; the sums stop there (adding
-        // +0.0 to a non-negative sum changes nothing)
+        const double w1 = keep1 ? e : 0.0;
+        // only the first nk lanes can carry weight
         const int nk = n_real < k_eff ? n_real : k_eff;
+        double acc = 0.0, excl = 0.0;
+        for (int j = 0; j < nk; ++j) {
+          if (lane == j) excl = acc;
+          acc += vs::bcast(w1, j);
+        }
+        const double incl = excl + w1;  // the scan's value after this lane, same rounding
+        const double tp = static_cast<double>(top_p);
         bool keep2 = keep1;
         if (tp < 1.0) {
-          const double s = vs::seq_sum(keep1 ? e : 0.0, nk);
-          keep2 = false;
-          double c = 0.0;
-          bool first = true;
-          for (int j = 0; j < nk; ++j) {
-            const double ej = vs::bcast(e, j);
-            const int kj = vs::bcast(keep1 ? 1 : 0, j);
-            if (!kj) continue;
-            if (c < tp * s || first) {
-              if (lane == j) keep2 = true;
-              c += ej;
-              first = false;
-            } else {
-              break;
-            }
-          }
+          const uint64_t k1 = __ballot(keep1);
+          const int first = k1 ? __ffsll(static_cast<long long>(k1)) - 1 : -1;
+          keep2 = keep1 && (excl < tp * acc || lane == first);
         }
-        const double z = vs::seq_sum(keep2 ? e : 0.0, nk);
+        const uint64_t k2 = __ballot(keep2);
+        const double z = k2 ? vs::bcast(incl, 63 - __clzll(static_cast<long long>(k2))) : 1.0;
         keep = keep2;
         prob = keep ? static_cast<float>(e / z) : 0.f;
       }
