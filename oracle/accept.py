@@ -13,6 +13,16 @@ drafts are accepted, draw the bonus from p at the last row.  With a
 point-mass draft q = delta(c) ([SD] §06) the same rule accepts with
 probability p(c) and otherwise draws from p without c.
 
+Deterministic drafts (the draft is a token, not a distribution):
+  * point-mass rule, [SD] §06 (n-gram takeovers): the sampled rule with
+    q = delta(d): accept d with probability p(d), otherwise emit a draw from
+    p with d removed, renormalised;
+  * naive-sampling verify, [PR] "Code map" (the generic chain's greedy and
+    temp > 0 verify, exact for any deterministic draft): each verify row
+    draws its own token from p and the window keeps going while that token
+    equals the draft; the first differing draw is emitted and ends the
+    window, and after k matches the bonus is drawn from the last row.
+
 Greedy tree: [TREE] "Spend the budget on a tree, not a longer guess":
 several continuations sharing a prefix are verified in one pass and the
 longest branch the target agrees with is accepted.
@@ -27,7 +37,10 @@ Readings taken:
   * the residual is r_j = max(0, p_j - q(t_j)) over p's support in pool
     order, in fp64; if its total is 0 the replacement is drawn from p;
   * row i uses the uniforms u[i][0] (accept test) and u[i][1]
-    (replacement or bonus draw); the bonus uses u[k][1];
+    (replacement or bonus draw); the bonus uses u[k][1].  The naive verify
+    has no accept test: row i draws with u[i][1];
+  * point-mass rule: u0 < p(d) (u0 * 1 in the sampled test); if p has no
+    mass outside d the replacement is drawn from p, as for a zero residual;
   * a target row with an empty distribution emits token -1 (not a
     token; the policy only yields one when every candidate slot is empty);
   * argmax ties go to the lowest token id (the pool order), so a row's
@@ -136,4 +149,53 @@ def accept_sampled(p_rows, q_rows, drafts, u) -> list[int]:
         return out
     ids, probs = p_rows[k]
     out.append(int(ids[draw(probs, u[k][1])]) if len(ids) else -1)
+    return out
+
+
+def accept_point_mass(p_rows, drafts, u) -> list[int]:
+    """One window of deterministic drafts under the point-mass rule.
+
+    Row i accepts d_i when u[i][0] < p_i(d_i); otherwise it emits a draw
+    (with u[i][1]) from p_i without d_i, renormalised, and ends the window.
+    After k acceptances the bonus is drawn from p_k with u[k][1].
+    """
+    out = []
+    k = len(drafts)
+    for i in range(k):
+        x = int(drafts[i])
+        ids, probs = p_rows[i]
+        if float(np.float32(u[i][0])) < prob_of(p_rows[i], x):
+            out.append(x)
+            continue
+        w = [0.0 if int(t) == x else float(pj) for t, pj in zip(ids, probs)]
+        z = 0.0
+        for wj in w:
+            z += wj
+        if len(ids) == 0:
+            out.append(-1)
+        elif z > 0.0:
+            out.append(int(ids[draw_weights(w, u[i][1])]))
+        else:
+            out.append(int(ids[draw(probs, u[i][1])]))
+        return out
+    ids, probs = p_rows[k]
+    out.append(int(ids[draw(probs, u[k][1])]) if len(ids) else -1)
+    return out
+
+
+def accept_naive(p_rows, drafts, u) -> list[int]:
+    """One window under the naive-sampling verify.
+
+    Row i draws x_i from p_i with u[i][1] and emits it; the window goes on
+    while x_i equals d_i, and after k matches emits the bonus draw x_k from
+    p_k with u[k][1].  Every emitted token is a draw from its row's p.
+    """
+    out = []
+    k = len(drafts)
+    for i in range(k + 1):
+        ids, probs = p_rows[i]
+        x = int(ids[draw(probs, u[i][1])]) if len(ids) else -1
+        out.append(x)
+        if i == k or x != int(drafts[i]):
+            return out
     return out

@@ -242,3 +242,106 @@ def test_chi_square_control_replacement_from_p_fails(rho, monkeypatch):
     outs = run_trials(p_rows, q_rows, TRIALS, 42)
     pv = row_pvalues(p_rows, outs)
     assert pv[0] < 1e-6, pv
+
+
+# ------------------------------------------------- deterministic drafts
+
+
+def test_point_mass_rule_equals_sampled_rule_with_delta_q():
+    """The point-mass rule ([SD] §06) is the sampled rule with q = delta(d):
+    two formulations, one through the residual (p - q)+, one removing d."""
+    from oracle.accept import accept_point_mass
+
+    for seed in range(6):
+        p_rows, _ = make_case(0.9, 1300 + seed)
+        g = np.random.default_rng(1310 + seed)
+        for trial in range(300):
+            drafts = []
+            for i in range(3):
+                ids = p_rows[i][0]
+                drafts.append(int(ids[g.integers(len(ids))]) if g.random() < 0.8 else 4095 - i)
+            u = uniforms(1320 + seed * 1000 + trial, (4, 2))
+            q_rows = [dist([d], [1.0]) for d in drafts]
+            assert accept_point_mass(p_rows, drafts, u) == accept_sampled(p_rows, q_rows, drafts, u)
+
+
+def test_point_mass_rule_closed_form_grid():
+    """Accept with probability p(c), else a draw from p without c; together
+    the emitted token follows p exactly (dyadic boundaries, exact grid)."""
+    from oracle.accept import accept_point_mass
+
+    p = dist([0, 1, 2, 3], [0.5, 0.25, 0.125, 0.125])
+    bonus = dist([9], [1.0])
+    grid = np.arange(64) / 64
+    accepted = [len(accept_point_mass([p, bonus], [0], [[u0, 0.0], [0, 0]])) == 2 for u0 in grid]
+    assert np.mean(accepted) == 0.5
+    reps = [accept_point_mass([p, bonus], [0], [[0.999, u1], [0, 0]])[0] for u1 in grid]
+    assert list(np.bincount(reps, minlength=4) / len(grid)) == [0.0, 0.5, 0.25, 0.25]
+    g32 = np.arange(32) / 32
+    first = [accept_point_mass([p, bonus], [0], [[u0, u1], [0, 0]])[0] for u0 in g32 for u1 in g32]
+    assert list(np.bincount(first, minlength=4) / len(first)) == [0.5, 0.25, 0.125, 0.125]
+
+
+def test_naive_verify_closed_forms():
+    """Naive-sampling verify ([PR] "Code map"): every emitted token is a draw
+    from its row's p, so the first token follows p_0 exactly, and the window
+    length is 1 + the number of leading rows whose draw equals the draft:
+    P(n = 1) = 1 - p_0(d_0), P(n = 2) = p_0(d_0)(1 - p_1(d_1)),
+    P(n = 3) = p_0(d_0) p_1(d_1)."""
+    from oracle.accept import accept_naive
+
+    p0 = dist([0, 1, 2, 3], [0.5, 0.25, 0.125, 0.125])
+    p1 = dist([5, 6], [0.75, 0.25])
+    p2 = dist([9], [1.0])
+    grid = np.arange(32) / 32
+    outs = [accept_naive([p0, p1, p2], [1, 5], [[0, a], [0, b], [0, 0.5]]) for a in grid for b in grid]
+    n = len(outs)
+    first = np.bincount([o[0] for o in outs], minlength=4) / n
+    assert list(first) == [0.5, 0.25, 0.125, 0.125]
+    lengths = np.bincount([len(o) for o in outs], minlength=4) / n
+    assert list(lengths[1:]) == [0.75, 0.25 * 0.25, 0.25 * 0.75]
+    second = [o[1] for o in outs if len(o) >= 2]
+    assert second.count(5) / len(second) == 0.75
+    assert all(o[-1] == 9 for o in outs if len(o) == 3)
+
+
+def test_naive_verify_on_one_hot_rows_is_greedy():
+    from oracle.accept import accept_naive
+
+    g = np.random.default_rng(1330)
+    for trial in range(200):
+        k = int(g.integers(0, 8))
+        argmax = g.integers(0, 50, size=k + 1)
+        drafts = np.where(g.random(k) < 0.7, argmax[:k], g.integers(0, 50, size=k))
+        rows = [dist([int(a)], [1.0]) for a in argmax]
+        u = uniforms(1331 + trial, (k + 1, 2))
+        assert accept_naive(rows, drafts, u) == accept_greedy_chain(argmax, drafts)
+
+
+def run_naive_trials(p_rows, q_rows, n, seed):
+    from oracle.accept import accept_naive
+
+    k = len(q_rows)
+    ud = uniforms(seed, (n, k))
+    u = uniforms(seed + 1, (n, k + 1, 2))
+    out = []
+    for b in range(n):
+        drafts = [int(q_rows[i][0][draw(q_rows[i][1], ud[b, i])]) for i in range(k)]
+        out.append(accept_naive(p_rows, drafts, u[b]))
+    return out
+
+
+def test_chi_square_naive_verify_follows_p():
+    p_rows, q_rows = make_case(0.9, 1109)
+    outs = run_naive_trials(p_rows, q_rows, TRIALS, 43)
+    pv = row_pvalues(p_rows, outs)
+    assert min(pv) >= 1e-3, pv
+
+
+def test_chi_square_control_naive_greedy_draw_fails(monkeypatch):
+    """Planted mistake: each row emits its most likely token instead of a draw."""
+    p_rows, q_rows = make_case(0.9, 1109)
+    monkeypatch.setattr(acc, "draw", lambda probs, u: 0)
+    outs = run_naive_trials(p_rows, q_rows, TRIALS, 43)
+    pv = row_pvalues(p_rows, outs)
+    assert pv[0] < 1e-6, pv
