@@ -189,6 +189,18 @@ int sample_policy_rows(const float* vals, const int32_t* ids, int64_t ld, int ro
  *                          that is all zero) and stop; after k acceptances
  *                          emit a bonus draw from p_k with u[k][1].  A
  *                          point-mass q = delta(c) gives [SD] §06.
+ *   VS_ACCEPT_POINT_MASS:  deterministic drafts under [SD] §06's rule, the
+ *                          sampled test with q_i = delta(d_i) (no q rows):
+ *                          accept d_i iff u[i][0] < p_i(d_i); otherwise emit
+ *                          a draw with u[i][1] from p_i without d_i,
+ *                          renormalised (from p_i if nothing else is left),
+ *                          and stop; bonus as in VS_ACCEPT_SAMPLED.  Same
+ *                          tokens as VS_ACCEPT_SAMPLED with one-entry q rows.
+ *   VS_ACCEPT_NAIVE:       [PR] "Code map", the naive-sampling verify (exact
+ *                          for any deterministic draft): row i emits its own
+ *                          draw from p_i with u[i][1] and the window goes on
+ *                          while that draw equals d_i; after k matches the
+ *                          bonus is the draw from p_k with u[k][1].
  *   VS_ACCEPT_GREEDY_TREE: [TREE] "Spend the budget on a tree": node j has
  *                          token drafts[j] and parent parent[j] (-1 = root,
  *                          else < j); row 0 is the root, row 1 + j is node
@@ -205,8 +217,9 @@ int sample_policy_rows(const float* vals, const int32_t* ids, int64_t ld, int ro
  *   among all windows).  p has k + 1 rows per window, q has k.
  *   drafts  int32 [B][k]   (tree: node tokens)
  *   parent  int32 [B][k]   (tree mode only, else may be NULL)
- *   u       fp32 [B][k+1][2] in [0, 1) (sampled mode only)
- *   q_*, p_probs, p_len may be NULL in the greedy modes.
+ *   u       fp32 [B][k+1][2] in [0, 1) (sampled, point-mass and naive modes)
+ *   q_* may be NULL except in VS_ACCEPT_SAMPLED; p_probs, p_len may be NULL
+ *   in the greedy modes.
  *   out_tokens int32 [B][k+1] (entries past the count are -1),
  *   out_n      int32 [B], 1 <= out_n[b] <= k + 1.
  *   1 <= B, 0 <= k <= VS_MAX_DRAFTS, 1 <= p_ld, q_ld <= VS_POOL.
@@ -214,7 +227,9 @@ int sample_policy_rows(const float* vals, const int32_t* ids, int64_t ld, int ro
 enum vs_accept_mode {
   VS_ACCEPT_SAMPLED = 0,
   VS_ACCEPT_GREEDY = 1,
-  VS_ACCEPT_GREEDY_TREE = 2
+  VS_ACCEPT_GREEDY_TREE = 2,
+  VS_ACCEPT_POINT_MASS = 3,
+  VS_ACCEPT_NAIVE = 4
 };
 int spec_accept_rows(int mode, int B, int k,
                      const int32_t* p_ids, const float* p_probs, const int32_t* p_len,

@@ -85,8 +85,13 @@ def test_policy_and_penalty_and_accept_reject_before_launch():
     # nothing to penalise: returns OK without launching
     assert lib.penalize_rows(FAKE, None, 100, 1, 100, 100, None, 0, None, 0, 64, 1.1, 0, 0,
                              None) == 0
-    assert lib.spec_accept_rows(3, 1, 1, FAKE, None, None, 4, 2, None, None, None, 1, 1, FAKE,
-                                None, None, FAKE, FAKE, None) == -3
+    assert lib.spec_accept_rows(5, 1, 1, FAKE, None, None, 4, 2, None, None, None, 1, 1, FAKE,
+                                None, None, FAKE, FAKE, None) == -3   # unknown mode
+    for mode in (3, 4):   # point-mass and naive modes need p's probabilities and the uniforms
+        assert lib.spec_accept_rows(mode, 1, 1, FAKE, None, FAKE, 4, 2, None, None, None, 1, 1,
+                                    FAKE, None, FAKE, FAKE, FAKE, None) == -1
+        assert lib.spec_accept_rows(mode, 1, 1, FAKE, FAKE, FAKE, 4, 2, None, None, None, 1, 1,
+                                    FAKE, None, None, FAKE, FAKE, None) == -1
     assert lib.spec_accept_rows(0, 1, 64, FAKE, FAKE, FAKE, 4, 65, FAKE, FAKE, FAKE, 4, 64, FAKE,
                                 None, FAKE, FAKE, FAKE, None) == -2   # k > 63
     assert lib.spec_accept_rows(0, 1, 2, FAKE, FAKE, FAKE, 4, 3, FAKE, FAKE, FAKE, 4, 2, FAKE,

@@ -169,3 +169,52 @@ def test_sampled_per_window_distributions():
         want = accept_sampled(p_rows_all[b * (k + 1):(b + 1) * (k + 1)],
                               q_rows_all[b * k:(b + 1) * k], drafts[b], u[b])
         assert list(tok[b, :n[b]]) == want, b
+
+
+def deterministic_drafts(p_rows, n, seed, k=3):
+    """Per window: row i's draft is a token of p_i's support (80%) or one outside it."""
+    g = np.random.default_rng(seed)
+    out = np.empty((n, k), dtype=np.int32)
+    for i in range(k):
+        ids = p_rows[i][0]
+        pick = ids[g.integers(0, len(ids), size=n)]
+        out[:, i] = np.where(g.random(n) < 0.8, pick, 4095 - i)
+    return out
+
+
+@pytest.mark.parametrize("mode", ["point", "naive"])
+def test_deterministic_draft_modes_match_oracle_and_follow_p(mode):
+    """Point-mass rule ([SD] §06) and naive-sampling verify ([PR] "Code map")
+    on 200,000 windows: tokens and counts equal the oracle's under the same
+    uniforms, and every row's emitted tokens pass the chi-square test against
+    p.  The point-mass mode also equals the sampled mode with q = delta(d)."""
+    from oracle.accept import accept_naive, accept_point_mass
+
+    k = 3
+    p_rows, _ = make_case(0.9, 1850)
+    drafts = deterministic_drafts(p_rows, TRIALS, 1851)
+    u = uniforms(1852, (TRIALS, k + 1, 2))
+    pi, pp, pln = pack(p_rows)
+    m = vs.ACCEPT_POINT_MASS if mode == "point" else vs.ACCEPT_NAIVE
+    tok, n = vs.spec_accept_rows(m, dev(drafts), (dev(pi), dev(pp), dev(pln)), u=dev(u),
+                                 p_win_stride=0)
+    tok, n = host(tok), host(n)
+    ref = accept_point_mass if mode == "point" else accept_naive
+    mism = 0
+    for b in range(TRIALS):
+        got = list(tok[b, :n[b]])
+        if got != ref(p_rows, drafts[b], u[b]) or (tok[b, n[b]:] != -1).any():
+            mism += 1
+    assert mism == 0, f"{mism} windows differ"
+    for i in range(k + 1):
+        toks = tok[n > i, i]
+        if len(toks) >= 200:
+            assert chi2_pvalue(toks, *p_rows[i]) >= 1e-3, i
+    if mode == "point":
+        q = np.full((TRIALS * k, 1), -1, dtype=np.int32)
+        q[:, 0] = drafts.reshape(-1)
+        qp = np.ones((TRIALS * k, 1), dtype=np.float32)
+        ql = np.ones(TRIALS * k, dtype=np.int32)
+        tok2, n2 = vs.spec_accept_rows(vs.ACCEPT_SAMPLED, dev(drafts), (dev(pi), dev(pp), dev(pln)),
+                                       (dev(q), dev(qp), dev(ql)), u=dev(u), p_win_stride=0)
+        assert np.array_equal(host(tok2), tok) and np.array_equal(host(n2), n)

@@ -31,12 +31,14 @@ __all__ = [
     "ACCEPT_SAMPLED",
     "ACCEPT_GREEDY",
     "ACCEPT_GREEDY_TREE",
+    "ACCEPT_POINT_MASS",
+    "ACCEPT_NAIVE",
     "POOL",
     "MAX_ROWS",
     "EXPORTED_SYMBOLS",
 ]
 
-ACCEPT_SAMPLED, ACCEPT_GREEDY, ACCEPT_GREEDY_TREE = 0, 1, 2
+ACCEPT_SAMPLED, ACCEPT_GREEDY, ACCEPT_GREEDY_TREE, ACCEPT_POINT_MASS, ACCEPT_NAIVE = 0, 1, 2, 3, 4
 POOL = 64
 MAX_ROWS = 24
 
@@ -274,7 +276,8 @@ def spec_accept_rows(mode, drafts, p, q=None, *, u=None, parent=None, p_win_stri
     drafts: int32 [B][k].  p = (ids int32 [P][p_ld], probs float32 [P][p_ld] or
     None, len int32 [P] or None) with window b's row i at row
     b * p_win_stride + i (default stride k + 1); q likewise with k rows per
-    window (default stride k).  u: float32 [B][k+1][2] (sampled mode);
+    window (default stride k; sampled mode only).  u: float32 [B][k+1][2]
+    (sampled, point-mass and naive modes);
     parent: int32 [B][k] (tree mode).  Returns (tokens int32 [B][k+1],
     n_emitted int32 [B]).
     """

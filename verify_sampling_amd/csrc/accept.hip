@@ -6,6 +6,11 @@
 // Sampled chain: §03 steps 1-4 (accept with min(1, p/q), else a draw from the
 // renormalised residual (p - q)+ and stop; bonus draw from p after k
 // acceptances); a point-mass q gives §06's takeover rule.
+// Deterministic drafts: the point-mass rule of §06 (the sampled test with
+// q = delta(d), no q rows needed), and the naive-sampling verify named in the
+// "Code map" of "feat(dflash): developer-only online draft tuning" (each row
+// emits its own draw from p; the window goes on while the draw equals the
+// draft).
 // Greedy tree: "One RDNA4 verify pass has slack for about two dozen
 // speculative tokens", "Spend the budget on a tree": the longest branch the
 // target agrees with is accepted.
@@ -106,6 +111,50 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
     const int32_t a = d.p_ids[(static_cast<int64_t>(b) * d.p_ws + last_row) * d.p_ld];
     if (lane == n) my_tok = a;
     ++n;
+  } else if (mode == VS_ACCEPT_NAIVE) {
+    const float* ub = u + static_cast<int64_t>(b) * (k + 1) * 2;
+    for (int i = 0; i <= k; ++i) {
+      const int64_t prow = static_cast<int64_t>(b) * d.p_ws + i;
+      const int pl = clamp_len(d.p_len[prow], d.p_ld);
+      const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
+      const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
+      const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * i + 1]));  // -1 if p is empty
+      if (lane == n) my_tok = x;
+      ++n;
+      if (i == k || x != dr[i]) break;
+    }
+  } else if (mode == VS_ACCEPT_POINT_MASS) {
+    const float* ub = u + static_cast<int64_t>(b) * (k + 1) * 2;
+    bool stopped = false;
+    for (int i = 0; i < k && !stopped; ++i) {
+      const int64_t prow = static_cast<int64_t>(b) * d.p_ws + i;
+      const int pl = clamp_len(d.p_len[prow], d.p_ld);
+      const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
+      const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
+      const int32_t x = dr[i];
+      if (static_cast<double>(ub[2 * i]) < prob_of(pid, pp, pl, x)) {  // u * q(x), q(x) = 1
+        if (lane == n) my_tok = x;
+        ++n;
+        continue;
+      }
+      // (p - delta(x))+ is p without x
+      const double r = (lane < pl && pid != x) ? pp : 0.0;
+      const double z = vs::seq_sum(r, pl);
+      const int j = z > 0.0 ? vs::seq_draw(r, pl, ub[2 * i + 1]) : vs::seq_draw(pp, pl, ub[2 * i + 1]);
+      const int32_t t = vs::bcast(pid, j);
+      if (lane == n) my_tok = t;
+      ++n;
+      stopped = true;
+    }
+    if (!stopped) {  // bonus draw from p_k
+      const int64_t prow = static_cast<int64_t>(b) * d.p_ws + k;
+      const int pl = clamp_len(d.p_len[prow], d.p_ld);
+      const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
+      const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
+      const int32_t t = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * k + 1]));
+      if (lane == n) my_tok = t;
+      ++n;
+    }
   } else {  // sampled chain
     const float* ub = u + static_cast<int64_t>(b) * (k + 1) * 2;
     bool stopped = false;
@@ -167,13 +216,17 @@ extern "C" int spec_accept_rows(int mode, int B, int k, const int32_t* p_ids, co
                                 int q_ld, int64_t q_win_stride, const int32_t* drafts,
                                 const int32_t* parent, const float* u, int32_t* out_tokens,
                                 int32_t* out_n, hipStream_t stream) {
-  if (mode != VS_ACCEPT_SAMPLED && mode != VS_ACCEPT_GREEDY && mode != VS_ACCEPT_GREEDY_TREE)
+  if (mode != VS_ACCEPT_SAMPLED && mode != VS_ACCEPT_GREEDY && mode != VS_ACCEPT_GREEDY_TREE &&
+      mode != VS_ACCEPT_POINT_MASS && mode != VS_ACCEPT_NAIVE)
     return VS_ERR_PARAM;
   if (B < 1 || k < 0 || k > VS_MAX_DRAFTS) return VS_ERR_SHAPE;
   if (!p_ids || !out_tokens || !out_n) return VS_ERR_NULL;
   if (k > 0 && !drafts) return VS_ERR_NULL;
   if (p_ld < 1 || p_ld > VS_POOL || p_win_stride < 0) return VS_ERR_SHAPE;
   if (mode == VS_ACCEPT_GREEDY_TREE && k > 0 && !parent) return VS_ERR_NULL;
+  if (mode == VS_ACCEPT_POINT_MASS || mode == VS_ACCEPT_NAIVE) {
+    if (!p_probs || !p_len || !u) return VS_ERR_NULL;
+  }
   if (mode == VS_ACCEPT_SAMPLED) {
     if (!p_probs || !p_len || !u) return VS_ERR_NULL;
     if (k > 0 && (!q_ids || !q_probs || !q_len)) return VS_ERR_NULL;
