@@ -266,6 +266,34 @@ def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, war
             "mean_emitted_per_window": mean_emitted}
 
 
+def depth_report(vs, sweep):
+    """The draft-depth choice on the measured window cost.
+
+    The cost of a window of r rows is the measured verify pass at R = r
+    (projections of the stack and the LM head; no attention).  Reports the
+    straight-line fits (base + per_row * (R - 1), least squares over
+    R = 1..8 and 1..24), the break-even tokens cost(R) / cost(1), and the
+    library's depth choice for constant per-depth acceptance rates.
+    """
+    Rs = sorted(sweep)
+    if len(Rs) < 2 or Rs != list(range(1, len(Rs) + 1)):
+        return None
+    cost = [float(sweep[r]) for r in Rs]
+    x = np.arange(len(Rs), dtype=np.float64)
+    fits = {}
+    for hi in (8, len(Rs)):
+        per_row, base = np.polyfit(x[:hi], np.array(cost[:hi]), 1)
+        fits[f"fit_ms_1_{hi}"] = {"base": round(float(base), 4), "per_row": round(float(per_row), 4)}
+    kmax = len(Rs) - 1
+    return {
+        "cost": f"measured verify-pass ms at R = 1..{len(Rs)} (projections only)",
+        **fits,
+        "break_even_tokens": {str(r): round(cost[r - 1] / cost[0], 4) for r in Rs[1:]},
+        "k_star_constant_alpha": {f"{a:.2f}": vs.choose_depth([a] * kmax, cost)[0]
+                                  for a in (0.3, 0.5, 0.6, 0.7, 0.8, 0.9, 0.95)},
+    }
+
+
 def cpu_baseline(synth, R, budget_s=12.0):
     """The oracle (as it stands) on a bounded sample of the same pass, on the host cores."""
     import oracle
@@ -406,7 +434,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_rows_kernel<1>" if R <= 16 else "gemv_rows_kernel<2>",
+            "kernel": ("verify_gemv_rows: gemv_rows_kernel (row-block)" if R <= 8 else
+                       "verify_gemv_rows: gemv_shared_kernel (shared activations) and gemv_rows_kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -422,6 +451,7 @@ def main():
         "gbs_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9, 1)
                      for r, v in sweep.items()},
         "knee_R": knee,
+        "depth_chooser": depth_report(vs, sweep) if sweep else None,
         "sampling": sampling,
         "cpu_baseline": cpu,
     }

@@ -239,6 +239,26 @@ int spec_accept_rows(int mode, int B, int k,
                      const int32_t* drafts, const int32_t* parent, const float* u,
                      int32_t* out_tokens, int32_t* out_n, hipStream_t stream);
 
+/*
+ * vs_choose_depth: the draft depth of the next window.
+ *   [SD] §05 "What a verify row costs on RDNA": pick the depth k that
+ *   maximises the expected emitted tokens (1 plus the running products of
+ *   the per-depth acceptance rates) per unit of window cost; k = 0 is one
+ *   token per plain decode step, the fallback.
+ *
+ *   E(k)  = 1 + sum_{j=1..k} prod_{i=1..j} alpha[i-1]   (fp64, increasing j)
+ *   rate  = E(k) / cost[k]          (cost[r-1]: cost of a window of r rows)
+ * Returns k* in [0, kmax], the depth with the largest rate (the smaller k
+ * on a tie), and writes its rate to *rate when rate is not NULL; or a
+ * negative status.  Host function: no device work, no stream.
+ *   alpha  [kmax] acceptance probability of draft j given drafts 1..j-1
+ *          were accepted, each in [0, 1] (may be NULL when kmax == 0)
+ *   cost   [kmax + 1] window costs, finite and > 0 (any unit, e.g. the
+ *          measured ms of a verify pass of r rows)
+ *   0 <= kmax <= VS_MAX_DRAFTS.
+ */
+int vs_choose_depth(const double* alpha, int kmax, const double* cost, double* rate);
+
 #ifdef __cplusplus
 }
 #endif

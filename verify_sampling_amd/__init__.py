@@ -28,6 +28,7 @@ __all__ = [
     "topk_rows_workspace_bytes",
     "sample_policy_rows",
     "spec_accept_rows",
+    "choose_depth",
     "ACCEPT_SAMPLED",
     "ACCEPT_GREEDY",
     "ACCEPT_GREEDY_TREE",
@@ -53,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "topk_rows",
     "sample_policy_rows",
     "spec_accept_rows",
+    "vs_choose_depth",
 )
 
 
@@ -79,6 +81,7 @@ _SIGNATURES = {
     "sample_policy_rows": ([P, P, I64, I32, I32, F32, I32, F32, F32, P, P, P, I64, P, P, P], I32),
     "spec_accept_rows": ([I32, I32, I32, P, P, P, I32, I64, P, P, P, I32, I64, P, P, P, P, P, P],
                          I32),
+    "vs_choose_depth": ([P, I32, P, P], I32),
 }
 
 
@@ -311,3 +314,20 @@ def spec_accept_rows(mode, drafts, p, q=None, *, u=None, parent=None, p_win_stri
         _ptr(n_emitted, torch.int32, "n_emitted"), _stream(stream))
     _check(st, "spec_accept_rows")
     return tokens, n_emitted
+
+
+def choose_depth(alpha, cost):
+    """(k*, rate): the draft depth with the most expected emitted tokens per unit cost.
+
+    alpha: per-depth acceptance probabilities (length kmax); cost: window
+    costs for 1..kmax+1 rows.  Host computation in the library.
+    """
+    a = (ctypes.c_double * max(1, len(alpha)))(*[float(x) for x in alpha])
+    c = (ctypes.c_double * len(cost))(*[float(x) for x in cost])
+    if len(cost) != len(alpha) + 1:
+        raise VerifySamplingError("cost needs one entry more than alpha")
+    rate = ctypes.c_double(0.0)
+    k = library().vs_choose_depth(a, len(alpha), c, ctypes.byref(rate))
+    if k < 0:
+        _check(k, "vs_choose_depth")
+    return int(k), rate.value
