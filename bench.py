@@ -294,6 +294,20 @@ def depth_report(vs, sweep):
     }
 
 
+def lookup_report(vs, synth, length=32768, calls=200):
+    """Host latency of drafting a prompt-lookup token tree (3 matches of the
+    last 3 tokens, depth 8, 24 nodes) from a context of copied lines."""
+    ctx = synth.lookup_context(8200, length + calls)
+    sizes = []
+    t0 = time.perf_counter()
+    for i in range(calls):
+        tk, _ = vs.lookup_tree(ctx[:length + i], 3, 3, 8, 24)
+        sizes.append(len(tk))
+    us = (time.perf_counter() - t0) / calls * 1e6
+    return {"context_tokens": length, "us_per_tree": round(us, 1),
+            "mean_nodes": round(float(np.mean(sizes)), 2), "host": "one core"}
+
+
 def cpu_baseline(synth, R, budget_s=12.0):
     """The oracle (as it stands) on a bounded sample of the same pass, on the host cores."""
     import oracle
@@ -452,6 +466,7 @@ def main():
                      for r, v in sweep.items()},
         "knee_R": knee,
         "depth_chooser": depth_report(vs, sweep) if sweep else None,
+        "prompt_lookup_drafter": lookup_report(vs, synth),
         "sampling": sampling,
         "cpu_baseline": cpu,
     }

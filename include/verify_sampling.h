@@ -9,8 +9,10 @@
  *   [PR]   "feat(dflash): developer-only online draft tuning" (hipfire PR #820)
  *
  * Conventions for every entry point:
- *   - Array arguments are DEVICE pointers owned by the caller.  The library
- *     allocates nothing and keeps no mutable global state; scratch space,
+ *   - Array arguments are DEVICE pointers owned by the caller (the host
+ *     functions vs_choose_depth and vs_lookup_tree take host arrays).  The
+ *     library allocates no device memory and keeps no mutable global state;
+ *     scratch space,
  *     where needed, is a caller-provided workspace whose size a companion
  *     *_workspace_bytes() call reports.
  *   - Every call only enqueues work on `stream` and returns; it never
@@ -258,6 +260,32 @@ int spec_accept_rows(int mode, int B, int k,
  *   0 <= kmax <= VS_MAX_DRAFTS.
  */
 int vs_choose_depth(const double* alpha, int kmax, const double* cost, double* rate);
+
+/*
+ * vs_lookup_tree: prompt-lookup drafting of a token tree.
+ *   [TREE] the introduction (prompt lookup proposes what followed an earlier
+ *   occurrence of the last n-gram), "Spend the budget on a tree" and "What I
+ *   am building toward" (keep the top few matches, ranked by how often they
+ *   recur, as branches sharing a prefix, within one verify pass's budget).
+ *
+ * Query: the last n tokens of ctx.  Every earlier position p (p + n <
+ * ctx_len) with ctx[p, p+n) equal to the query proposes the continuation
+ * ctx[p+n, p+n+depth) (shorter where ctx ends).  Identical proposals are one
+ * branch whose count is the number of matches proposing it; branches rank by
+ * count, then most recent match first.  The top `branches` are merged into a
+ * trie: walking each from the root in rank order, an existing child with the
+ * same token is shared, otherwise node `nodes++` is appended with its parent
+ * (-1 = the root, i.e. the current position).  Node j's parent is < j: the
+ * layout spec_accept_rows takes in VS_ACCEPT_GREEDY_TREE mode (tokens as
+ * drafts, parent as parent).  Nodes stop at max_nodes.
+ *   ctx     int32 [ctx_len] HOST array (token ids); may be NULL if ctx_len == 0
+ *   tokens, parent  int32 [max_nodes] HOST arrays, written
+ *   1 <= n, 1 <= branches, 1 <= depth, 1 <= max_nodes <= VS_MAX_DRAFTS.
+ * Returns the number of nodes (0: no earlier match) or a negative status.
+ * Host function: no device work, no stream; uses temporary host memory.
+ */
+int vs_lookup_tree(const int32_t* ctx, int ctx_len, int n, int branches, int depth,
+                   int max_nodes, int32_t* tokens, int32_t* parent);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,11 @@ Recipes (the workloads' shapes and value distributions):
     uniform takes the top 24 bits of a 32-bit draw), exact in fp32 and fp64;
   * draft-side top-K rows: N(0, 4) with planted exact ties, 1-ulp
     neighbours, duplicated maxima, -inf, NaN, +-0, an all-equal row and a
-    row with fewer finite values than K.
+    row with fewer finite values than K;
+  * prompt-lookup contexts: a coding agent's context is full of
+    near-identical lines, so the token stream is a sequence of "lines"
+    (6-20 tokens) drawn with Zipf-like popularity from a pool in which
+    families of lines share a prefix and differ after it.
 """
 
 from __future__ import annotations
@@ -39,6 +43,7 @@ __all__ = [
     "chain_greedy_case",
     "tree_greedy_case",
     "torch_bf16_weights",
+    "lookup_context",
     "LAYER_SHAPES",
     "LAYER_SHAPES_FUSED",
     "LM_HEAD_SHAPE",
@@ -252,3 +257,28 @@ def torch_bf16_weights(shape, seed: int, device, std: float = 0.02):
     w = torch.empty(shape, dtype=torch.float32, device=device)
     w.normal_(0.0, std, generator=gen)
     return w.to(torch.bfloat16)
+
+
+def lookup_context(seed: int, length: int, vocab: int = VOCAB, families: int = 60,
+                   variants: int = 4) -> np.ndarray:
+    """int32 token stream of `length` tokens built from repeated near-identical lines.
+
+    Each family has a shared prefix of 3-8 tokens and `variants` different
+    tails of 3-12 tokens; lines are drawn with probability proportional to
+    1 / (rank + 1) over all family variants.
+    """
+    g = rng(seed)
+    lines = []
+    for _ in range(families):
+        head = g.integers(0, vocab, size=int(g.integers(3, 9)))
+        for _ in range(variants):
+            lines.append(np.concatenate([head, g.integers(0, vocab, size=int(g.integers(3, 13)))]))
+    w = 1.0 / (np.arange(len(lines)) + 1.0)
+    w /= w.sum()
+    out = []
+    total = 0
+    while total < length:
+        line = lines[int(g.choice(len(lines), p=w))]
+        out.append(line)
+        total += len(line)
+    return np.concatenate(out)[:length].astype(np.int32)

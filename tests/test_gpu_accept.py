@@ -218,3 +218,48 @@ def test_deterministic_draft_modes_match_oracle_and_follow_p(mode):
         tok2, n2 = vs.spec_accept_rows(vs.ACCEPT_SAMPLED, dev(drafts), (dev(pi), dev(pp), dev(pln)),
                                        (dev(q), dev(qp), dev(ql)), u=dev(u), p_win_stride=0)
         assert np.array_equal(host(tok2), tok) and np.array_equal(host(n2), n)
+
+
+def test_prompt_lookup_trees_greedy_walk():
+    """Token trees drafted by prompt lookup (vs_lookup_tree: top 3 matches of
+    the last 3 tokens, depth 8, 24 nodes) over a context of copied lines,
+    verified by the greedy tree walk.  The target's argmax rows follow what
+    the context really does next: the root row and every node whose path is
+    a prefix of the true continuation predict its next token, other rows a
+    token of their own.  Trees shorter than 24 nodes are padded with nodes
+    that never agree (token -2).  GPU tokens equal the oracle's."""
+    from synth import lookup_context
+
+    ctx = lookup_context(1870, 40000)
+    g = np.random.default_rng(1871)
+    B, K = 512, 24
+    tokens = np.full((B, K), -2, dtype=np.int32)
+    parents = np.full((B, K), -1, dtype=np.int32)
+    p_ids = np.full((B * (K + 1), 2), -1, dtype=np.int32)
+    want, sizes = [], []
+    for b in range(B):
+        e = int(g.integers(1000, len(ctx) - 16))
+        tk, par = vs.lookup_tree(ctx[:e], 3, 3, 8, K)
+        truth = ctx[e:e + 10]
+        sizes.append(len(tk))
+        tokens[b, :len(tk)], parents[b, :len(tk)] = tk, par
+        am = np.empty(K + 1, dtype=np.int32)
+        am[0] = truth[0]
+        for j in range(K):
+            path, q = [], j
+            while q >= 0 and j < len(tk):
+                path.append(int(tokens[b, q]))
+                q = int(parents[b, q])
+            path.reverse()
+            d = len(path)
+            on_truth = j < len(tk) and list(truth[:d]) == path
+            am[j + 1] = truth[d] if on_truth else int(g.integers(0, VOCAB))
+        p_ids[b * (K + 1):(b + 1) * (K + 1), 0] = am
+        want.append(accept_greedy_tree(am, tokens[b], parents[b]))
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY_TREE, dev(tokens), (dev(p_ids), None, None),
+                                 parent=dev(parents))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        assert list(tok[b, :n[b]]) == want[b], b
+    print(f"mean tree nodes {np.mean(sizes):.1f}; mean emitted per window {np.mean(n):.2f}")
+    assert np.mean(n) > 1.5   # the trees do contain the context's next tokens

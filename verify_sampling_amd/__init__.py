@@ -29,6 +29,7 @@ __all__ = [
     "sample_policy_rows",
     "spec_accept_rows",
     "choose_depth",
+    "lookup_tree",
     "ACCEPT_SAMPLED",
     "ACCEPT_GREEDY",
     "ACCEPT_GREEDY_TREE",
@@ -55,6 +56,7 @@ EXPORTED_SYMBOLS = (
     "sample_policy_rows",
     "spec_accept_rows",
     "vs_choose_depth",
+    "vs_lookup_tree",
 )
 
 
@@ -82,6 +84,7 @@ _SIGNATURES = {
     "spec_accept_rows": ([I32, I32, I32, P, P, P, I32, I64, P, P, P, I32, I64, P, P, P, P, P, P],
                          I32),
     "vs_choose_depth": ([P, I32, P, P], I32),
+    "vs_lookup_tree": ([P, I32, I32, I32, I32, I32, P, P], I32),
 }
 
 
@@ -331,3 +334,21 @@ def choose_depth(alpha, cost):
     if k < 0:
         _check(k, "vs_choose_depth")
     return int(k), rate.value
+
+
+def lookup_tree(ctx, n: int, branches: int, depth: int, max_nodes: int = 24):
+    """(tokens, parent) int32 arrays of the prompt-lookup token tree drafted from ctx.
+
+    ctx: host sequence of token ids.  Host computation in the library.
+    """
+    import numpy as np
+
+    c = np.ascontiguousarray(np.asarray(ctx, dtype=np.int32))
+    tok = np.zeros(max(1, max_nodes), dtype=np.int32)
+    par = np.zeros(max(1, max_nodes), dtype=np.int32)
+    k = library().vs_lookup_tree(c.ctypes.data if c.size else None, int(c.size), int(n),
+                                 int(branches), int(depth), int(max_nodes),
+                                 tok.ctypes.data, par.ctypes.data)
+    if k < 0:
+        _check(k, "vs_lookup_tree")
+    return tok[:k].copy(), par[:k].copy()
