@@ -21,7 +21,13 @@ Deterministic drafts (the draft is a token, not a distribution):
     temp > 0 verify, exact for any deterministic draft): each verify row
     draws its own token from p and the window keeps going while that token
     equals the draft; the first differing draw is emitted and ends the
-    window, and after k matches the bonus is drawn from the last row.
+    window, and after k matches the bonus is drawn from the last row;
+  * naive-sampling verify of a token tree (deterministic drafts, e.g. the
+    prompt-lookup trees of [TREE]): start at the root row, draw from its p,
+    emit the draw, and move to the child whose token it is (the
+    lowest-numbered one if siblings repeat a token), continuing with that
+    child's row; a draw that no child carries ends the window.  Every
+    emitted token is a draw from its row's p, so the walk is lossless.
 
 Greedy tree: [TREE] "Spend the budget on a tree, not a longer guess":
 several continuations sharing a prefix are verified in one pass and the
@@ -41,6 +47,9 @@ Readings taken:
     has no accept test: row i draws with u[i][1];
   * point-mass rule: u0 < p(d) (u0 * 1 in the sampled test); if p has no
     mass outside d the replacement is drawn from p, as for a zero residual;
+  * a draw from an empty target row is -1 and always ends the window;
+  * tree row r (0 = root, 1 + j = node j) draws with u[r][1]; a node whose
+    parent lies outside [-1, j) is never reached;
   * a target row with an empty distribution emits token -1 (not a
     token; the policy only yields one when every candidate slot is empty);
   * argmax ties go to the lowest token id (the pool order), so a row's
@@ -196,6 +205,29 @@ def accept_naive(p_rows, drafts, u) -> list[int]:
         ids, probs = p_rows[i]
         x = int(ids[draw(probs, u[i][1])]) if len(ids) else -1
         out.append(x)
-        if i == k or x != int(drafts[i]):
+        if i == k or x < 0 or x != int(drafts[i]):
             return out
     return out
+
+
+def accept_naive_tree(p_rows, tokens, parent, u) -> list[int]:
+    """One token tree under the naive-sampling verify (see the module doc).
+
+    p_rows: n + 1 distributions (row 0 = root, row 1 + j = node j); tokens,
+    parent: [n] (parent -1 = root); u: [n + 1][2], row r draws with u[r][1].
+    """
+    n = len(tokens)
+    out = []
+    node, row = -1, 0
+    while True:
+        ids, probs = p_rows[row]
+        x = int(ids[draw(probs, u[row][1])]) if len(ids) else -1
+        out.append(x)
+        if x < 0:
+            return out
+        child = next((j for j in range(n)
+                      if -1 <= int(parent[j]) < j and int(parent[j]) == node and int(tokens[j]) == x),
+                     None)
+        if child is None:
+            return out
+        node, row = child, child + 1

@@ -17,6 +17,13 @@ fused multiply-add (the page calls the GPU prepass bit-identical to the
 host stage, which fixes an exact op sequence).  W = 0 means no penalties;
 a shorter history uses every token available; ids outside [0, V) are
 ignored.
+
+Token trees ([TREE] "Spend the budget on a tree": each branch attends only
+to its own ancestors): the same rule applied per branch.  Row 0 is the
+root (the current position) with H = last W of the context; row 1 + j is
+node j with H = last W of (context || the tokens on the path from the root
+down to node j, inclusive).  A chain (parent[j] = j - 1) gives the chain's
+H_{j+1}.  A parent outside [-1, j) ends the path as the root would.
 """
 
 from __future__ import annotations
@@ -31,6 +38,25 @@ def history(ctx: np.ndarray, drafts: np.ndarray, i: int, window: int) -> list[in
     if window <= 0:
         return []
     seq = [int(t) for t in ctx] + [int(t) for t in drafts[:min(i, len(drafts))]]
+    return seq[-window:] if len(seq) > window else seq
+
+
+def tree_path(tokens, parent, j: int) -> list[int]:
+    """Tokens from the root's child down to node j (inclusive)."""
+    path = [int(tokens[j])]
+    child, q = j, int(parent[j])
+    while -1 < q < child:
+        path.append(int(tokens[q]))
+        child, q = q, int(parent[q])
+    path.reverse()
+    return path
+
+
+def tree_history(ctx, tokens, parent, row: int, window: int) -> list[int]:
+    """Row 0: last `window` of ctx; row 1 + j: last `window` of ctx || tree_path(j)."""
+    if window <= 0:
+        return []
+    seq = [int(t) for t in ctx] + (tree_path(tokens, parent, row - 1) if row > 0 else [])
     return seq[-window:] if len(seq) > window else seq
 
 
@@ -75,4 +101,30 @@ def penalize_sparse(ids: np.ndarray, vals: np.ndarray, ctx: np.ndarray, drafts: 
             c = counts.get(int(ids[i, m]), 0)
             if c >= 1:
                 out[i, m] = penalize_value(out[i, m], c, repeat, presence, frequency)
+    return out
+
+
+def penalize_tree_dense(logits, ctx, tokens, parent, window: int, repeat: float, presence: float,
+                        frequency: float) -> np.ndarray:
+    """Rows [n_nodes + 1][V]: row r penalised by tree_history(r).  Returns a copy."""
+    out = np.array(logits, dtype=np.float32, copy=True)
+    V = out.shape[1]
+    for r in range(out.shape[0]):
+        counts = Counter(tree_history(ctx, tokens, parent, r, window))
+        for t, c in counts.items():
+            if 0 <= t < V:
+                out[r, t] = penalize_value(out[r, t], c, repeat, presence, frequency)
+    return out
+
+
+def penalize_tree_sparse(ids, vals, ctx, tokens, parent, window: int, repeat: float,
+                         presence: float, frequency: float) -> np.ndarray:
+    """Candidate lists per tree row, penalised with tree_history(r).  Returns a copy of vals."""
+    out = np.array(vals, dtype=np.float32, copy=True)
+    for r in range(out.shape[0]):
+        counts = Counter(tree_history(ctx, tokens, parent, r, window))
+        for m in range(out.shape[1]):
+            c = counts.get(int(ids[r, m]), 0)
+            if c >= 1:
+                out[r, m] = penalize_value(out[r, m], c, repeat, presence, frequency)
     return out

@@ -345,3 +345,116 @@ def test_chi_square_control_naive_greedy_draw_fails(monkeypatch):
     outs = run_naive_trials(p_rows, q_rows, TRIALS, 43)
     pv = row_pvalues(p_rows, outs)
     assert pv[0] < 1e-6, pv
+
+
+# --------------------------------------------- naive verify of a token tree
+
+
+def test_naive_tree_walk_on_a_chain_is_the_chain_rule():
+    from oracle.accept import accept_naive, accept_naive_tree
+
+    for seed in range(4):
+        p_rows, _ = make_case(0.9, 1400 + seed)
+        g = np.random.default_rng(1410 + seed)
+        for trial in range(300):
+            drafts = [int(p_rows[i][0][g.integers(len(p_rows[i][0]))]) for i in range(3)]
+            u = uniforms(1420 + seed * 1000 + trial, (4, 2))
+            assert accept_naive_tree(p_rows, drafts, [-1, 0, 1], u) == accept_naive(p_rows, drafts, u)
+
+
+def test_naive_tree_walk_exact_enumeration():
+    """Root draw follows p_0 exactly; the walk enters the child carrying the
+    draw and continues with that child's row (dyadic grid, exact)."""
+    from oracle.accept import accept_naive_tree
+
+    p0 = dist([0, 1, 2, 3], [0.5, 0.25, 0.125, 0.125])
+    p_a = dist([5, 6], [0.75, 0.25])      # row of node 0 (token 1)
+    p_b = dist([7, 8], [0.5, 0.5])        # row of node 1 (token 2)
+    p_c = dist([9], [1.0])                # row of node 2 (token 5, child of node 0)
+    tokens, parent = [1, 2, 5], [-1, -1, 0]
+    grid = np.arange(32) / 32
+    outs = [accept_naive_tree([p0, p_a, p_b, p_c], tokens, parent, [[0, a], [0, b], [0, c], [0, 0.5]])
+            for a in grid for b in grid for c in (0.25, 0.75)]
+    n = len(outs)
+    assert list(np.bincount([o[0] for o in outs], minlength=4) / n) == [0.5, 0.25, 0.125, 0.125]
+    via_a = [o for o in outs if o[0] == 1]
+    assert all(len(o) >= 2 for o in via_a) and sum(o[1] == 5 for o in via_a) / len(via_a) == 0.75
+    assert all(o == [1, 5, 9] for o in via_a if o[1] == 5)
+    via_b = [o for o in outs if o[0] == 2]
+    assert all(len(o) == 2 and o[1] in (7, 8) for o in via_b)
+    assert all(len(o) == 1 for o in outs if o[0] in (0, 3))
+
+
+def test_naive_tree_walk_on_one_hot_rows_is_the_greedy_tree_walk():
+    from oracle.accept import accept_naive_tree
+    from oracle.lookup import lookup_tree
+
+    g = np.random.default_rng(1430)
+    for trial in range(300):
+        ctx = list(g.integers(0, 6, size=int(g.integers(10, 120))))
+        tokens, parent = lookup_tree(ctx, 2, 3, 5, 16)      # a trie: siblings differ
+        if not tokens:
+            continue
+        am = g.integers(0, 6, size=len(tokens) + 1)
+        rows = [dist([int(a)], [1.0]) for a in am]
+        u = uniforms(1431 + trial, (len(tokens) + 1, 2))
+        assert accept_naive_tree(rows, tokens, parent, u) == accept_greedy_tree(am, tokens, parent)
+
+
+def tree_rows_case(seed, n_nodes=24):
+    """A random trie of n_nodes (3 branches) and its n_nodes + 1 policy rows."""
+    from oracle.topk import topk_rows
+
+    g = np.random.default_rng(seed)
+    pl = logits(seed, (n_nodes + 1, 4096))
+    pv, pi = topk_rows(pl, 64)
+    rows = [policy_row(pv[i], pi[i], **CFG) for i in range(n_nodes + 1)]
+    tokens, parent = [], []
+    # children tokens drawn from the parent row's support, so the walk goes deep
+    while len(tokens) < n_nodes:
+        node = int(g.integers(-1, len(tokens)))
+        prow = 0 if node < 0 else node + 1
+        sib = {tokens[j] for j in range(len(tokens)) if parent[j] == node}
+        cand = [int(t) for t in rows[prow][0][:4] if int(t) not in sib]
+        if cand:
+            tokens.append(cand[0])
+            parent.append(node)
+    return rows, tokens, parent
+
+
+def naive_tree_row_draws(rows, tokens, parent, outs):
+    """Per row, the tokens drawn there: the emitted token at each step of each walk."""
+    per = [[] for _ in rows]
+    for o in outs:
+        node, row = -1, 0
+        for x in o:
+            per[row].append(x)
+            child = next((j for j in range(len(tokens)) if parent[j] == node and tokens[j] == x), None)
+            if child is None:
+                break
+            node, row = child, child + 1
+    return per
+
+
+def naive_tree_pvalues(seed):
+    from oracle.accept import accept_naive_tree
+
+    rows, tokens, parent = tree_rows_case(seed)
+    u = uniforms(seed + 1, (TRIALS, len(tokens) + 1, 2))
+    outs = [accept_naive_tree(rows, tokens, parent, u[b]) for b in range(TRIALS)]
+    per = naive_tree_row_draws(rows, tokens, parent, outs)
+    return [chi2_pvalue(d, *rows[r]) for r, d in enumerate(per) if len(d) >= 200]
+
+
+def test_chi_square_naive_tree_walk_follows_p():
+    """Every visited row's draws follow its p: one test per row (25 rows), so
+    the threshold is family-wise, 1e-3 over the number of rows (Bonferroni)."""
+    pv = naive_tree_pvalues(1440)
+    assert len(pv) >= 3 and min(pv) >= 1e-3 / len(pv), pv
+
+
+def test_chi_square_control_naive_tree_greedy_draw_fails(monkeypatch):
+    """Planted mistake: every row emits its most likely token instead of a draw."""
+    monkeypatch.setattr(acc, "draw", lambda probs, u: 0)
+    pv = naive_tree_pvalues(1440)
+    assert pv[0] < 1e-6, pv

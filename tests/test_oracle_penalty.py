@@ -106,3 +106,50 @@ def test_sparse_matches_dense_on_the_same_ids():
     vals = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
     sparse = penalize_sparse(ids, vals, ctx, d, 16, 1.1, 1.5, 0.2)
     assert np.array_equal(sparse, np.take_along_axis(dense, ids.astype(np.int64), axis=1))
+
+
+# ----------------------------------------------------------- token trees
+
+
+def test_tree_histories_hand_worked():
+    """Row 0 (root) sees the context; node j's row sees context || its path."""
+    from oracle.penalty import tree_history
+
+    ctx, tokens, parent = [5, 6], [7, 8, 9, 4], [-1, 0, -1, 1]
+    assert [tree_history(ctx, tokens, parent, r, 3) for r in range(5)] == \
+        [[5, 6], [5, 6, 7], [6, 7, 8], [5, 6, 9], [7, 8, 4]]
+    assert [tree_history(ctx, tokens, parent, r, 0) for r in range(5)] == [[]] * 5
+    # a parent outside [-1, j) ends the path as the root would
+    assert tree_history(ctx, [7, 8], [1, 5], 2, 10) == [5, 6, 8]
+
+
+def test_chain_tree_gives_the_chain_histories():
+    from oracle.penalty import tree_history
+
+    g = np.random.default_rng(1970)
+    for _ in range(100):
+        ctx = list(g.integers(0, 50, size=int(g.integers(0, 80))))
+        k = int(g.integers(0, 20))
+        drafts = g.integers(0, 50, size=k)
+        W = int(g.integers(0, 40))
+        chain_parent = list(range(-1, k - 1))
+        for r in range(k + 1):
+            assert tree_history(ctx, drafts, chain_parent, r, W) == history(np.array(ctx), drafts, r, W)
+
+
+def test_tree_penalties_equal_chain_penalties_on_a_chain():
+    from oracle.penalty import penalize_tree_dense, penalize_tree_sparse
+
+    g = np.random.default_rng(1971)
+    V, k = 300, 6
+    logits = (g.standard_normal((k + 1, V)) * 3).astype(np.float32)
+    ctx = g.integers(0, V, size=120)
+    drafts = g.integers(0, V, size=k)
+    parent = np.arange(-1, k - 1)
+    args = (40, 1.1, 1.5, 0.2)
+    assert np.array_equal(penalize_tree_dense(logits, ctx, drafts, parent, *args),
+                          penalize_dense(logits, ctx, drafts, *args))
+    ids = g.integers(0, V, size=(k + 1, 8)).astype(np.int32)
+    vals = logits[:, :8].copy()
+    assert np.array_equal(penalize_tree_sparse(ids, vals, ctx, drafts, parent, *args),
+                          penalize_sparse(ids, vals, ctx, drafts, *args))
