@@ -127,6 +127,26 @@ int penalize_rows(float* logits, const int32_t* ids, int64_t ld, int rows, int w
                   hipStream_t stream);
 
 /*
+ * penalize_tree_rows: the penalty prepass for the rows of a token tree.
+ *   [SD] §04's history rule applied per branch ([TREE] "Spend the budget on
+ *   a tree": each branch sees only its own ancestors).  Row 0 is the root
+ *   (H = last `window` tokens of ctx); row 1 + j is node j (H = last
+ *   `window` tokens of ctx || the tokens on the path from the root down to
+ *   node j, inclusive).  The path follows parent[] upwards and stops at -1
+ *   or at a parent outside [-1, j).  Otherwise as penalize_rows: the same
+ *   penalties, order and rounding, dense (ids == NULL, width == vocab) or
+ *   sparse (ids [rows][ld] candidate slots).
+ *   logits  fp32 [n_nodes + 1][ld]
+ *   tokens, parent  int32 [n_nodes] device arrays (node tokens; parent -1 =
+ *           the root), as in spec_accept_rows' tree modes
+ *   0 <= n_nodes <= VS_MAX_DRAFTS.
+ */
+int penalize_tree_rows(float* logits, const int32_t* ids, int64_t ld, int width, int vocab,
+                       const int32_t* ctx, int ctx_len, const int32_t* tokens,
+                       const int32_t* parent, int n_nodes, int window, float repeat,
+                       float presence, float frequency, hipStream_t stream);
+
+/*
  * topk_rows: per-row top-K in the sampler's pool order.
  *   [SD] §03 "how hipfire does it": a 64-wide pool with a fixed tie order;
  *   [PR] "Code map": batched top-K over draft rows, several workgroups per
@@ -203,6 +223,15 @@ int sample_policy_rows(const float* vals, const int32_t* ids, int64_t ld, int ro
  *                          draw from p_i with u[i][1] and the window goes on
  *                          while that draw equals d_i; after k matches the
  *                          bonus is the draw from p_k with u[k][1].
+ *   VS_ACCEPT_NAIVE_TREE:  the naive-sampling verify of a token tree of
+ *                          deterministic drafts ([TREE] "Spend the budget on
+ *                          a tree"; [PR] "Code map"): starting at the root
+ *                          row, emit the row's draw from p with u[row][1];
+ *                          if a node whose parent is the current node carries
+ *                          that token (the lowest-numbered one), continue at
+ *                          its row, else stop.  Rows and nodes as in
+ *                          VS_ACCEPT_GREEDY_TREE; a -1 draw (empty row) ends
+ *                          the window.
  *   VS_ACCEPT_GREEDY_TREE: [TREE] "Spend the budget on a tree": node j has
  *                          token drafts[j] and parent parent[j] (-1 = root,
  *                          else < j); row 0 is the root, row 1 + j is node
@@ -218,8 +247,9 @@ int sample_policy_rows(const float* vals, const int32_t* ids, int64_t ld, int ro
  *   q likewise with q_win_stride (a stride of 0 shares one set of rows
  *   among all windows).  p has k + 1 rows per window, q has k.
  *   drafts  int32 [B][k]   (tree: node tokens)
- *   parent  int32 [B][k]   (tree mode only, else may be NULL)
+ *   parent  int32 [B][k]   (tree modes only, else may be NULL)
  *   u       fp32 [B][k+1][2] in [0, 1) (sampled, point-mass and naive modes)
+ *           In VS_ACCEPT_NAIVE a draw of -1 (empty row) also ends the window.
  *   q_* may be NULL except in VS_ACCEPT_SAMPLED; p_probs, p_len may be NULL
  *   in the greedy modes.
  *   out_tokens int32 [B][k+1] (entries past the count are -1),
@@ -231,7 +261,8 @@ enum vs_accept_mode {
   VS_ACCEPT_GREEDY = 1,
   VS_ACCEPT_GREEDY_TREE = 2,
   VS_ACCEPT_POINT_MASS = 3,
-  VS_ACCEPT_NAIVE = 4
+  VS_ACCEPT_NAIVE = 4,
+  VS_ACCEPT_NAIVE_TREE = 5
 };
 int spec_accept_rows(int mode, int B, int k,
                      const int32_t* p_ids, const float* p_probs, const int32_t* p_len,

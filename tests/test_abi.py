@@ -82,12 +82,22 @@ def test_policy_and_penalty_and_accept_reject_before_launch():
                              None) == -3   # repeat <= 0
     assert lib.penalize_rows(FAKE, None, 100, 1, 99, 100, FAKE, 4, None, 0, 64, 1.1, 0, 0,
                              None) == -2   # dense width != vocab
+    # tree rows: node count bounded, tokens and parent required when there are nodes
+    assert lib.penalize_tree_rows(FAKE, None, 100, 100, 100, FAKE, 4, FAKE, FAKE, 64, 64, 1.1,
+                                  0, 0, None) == -2
+    assert lib.penalize_tree_rows(FAKE, None, 100, 100, 100, FAKE, 4, FAKE, None, 3, 64, 1.1,
+                                  0, 0, None) == -1
+    assert lib.penalize_tree_rows(FAKE, None, 100, 100, 100, None, 0, None, None, 0, 64, 1.1,
+                                  0, 0, None) == 0
     # nothing to penalise: returns OK without launching
     assert lib.penalize_rows(FAKE, None, 100, 1, 100, 100, None, 0, None, 0, 64, 1.1, 0, 0,
                              None) == 0
-    assert lib.spec_accept_rows(5, 1, 1, FAKE, None, None, 4, 2, None, None, None, 1, 1, FAKE,
+    assert lib.spec_accept_rows(6, 1, 1, FAKE, None, None, 4, 2, None, None, None, 1, 1, FAKE,
                                 None, None, FAKE, FAKE, None) == -3   # unknown mode
-    for mode in (3, 4):   # point-mass and naive modes need p's probabilities and the uniforms
+    # the naive tree walk needs parent[] when there are nodes
+    assert lib.spec_accept_rows(5, 1, 1, FAKE, FAKE, FAKE, 4, 2, None, None, None, 1, 1, FAKE,
+                                None, FAKE, FAKE, FAKE, None) == -1
+    for mode in (3, 4, 5):   # point-mass and naive modes need p's probabilities and the uniforms
         assert lib.spec_accept_rows(mode, 1, 1, FAKE, None, FAKE, 4, 2, None, None, None, 1, 1,
                                     FAKE, None, FAKE, FAKE, FAKE, None) == -1
         assert lib.spec_accept_rows(mode, 1, 1, FAKE, FAKE, FAKE, 4, 2, None, None, None, 1, 1,

@@ -263,3 +263,72 @@ def test_prompt_lookup_trees_greedy_walk():
         assert list(tok[b, :n[b]]) == want[b], b
     print(f"mean tree nodes {np.mean(sizes):.1f}; mean emitted per window {np.mean(n):.2f}")
     assert np.mean(n) > 1.5   # the trees do contain the context's next tokens
+
+
+def test_naive_tree_walk_matches_oracle_and_follows_p():
+    """Naive-sampling verify of a 24-node token tree over 200,000 windows
+    (one tree and its 25 rows shared by all windows, fresh uniforms per
+    window): tokens and counts equal the oracle's, and every row's draws
+    pass the chi-square test against its p (family-wise 1e-3 over the rows
+    tested)."""
+    from oracle.accept import accept_naive_tree
+    import test_oracle_accept as toa
+
+    rows, tokens, parent = toa.tree_rows_case(1860)
+    K = len(tokens)
+    u = uniforms(1861, (TRIALS, K + 1, 2))
+    pi, pp, pln = pack(rows)
+    tk = np.broadcast_to(np.array(tokens, dtype=np.int32), (TRIALS, K)).copy()
+    pr = np.broadcast_to(np.array(parent, dtype=np.int32), (TRIALS, K)).copy()
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_NAIVE_TREE, dev(tk), (dev(pi), dev(pp), dev(pln)),
+                                 u=dev(u), parent=dev(pr), p_win_stride=0)
+    tok, n = host(tok), host(n)
+    outs = []
+    mism = 0
+    for b in range(TRIALS):
+        got = list(tok[b, :n[b]])
+        outs.append(got)
+        if got != accept_naive_tree(rows, tokens, parent, u[b]) or (tok[b, n[b]:] != -1).any():
+            mism += 1
+    assert mism == 0, f"{mism} windows differ"
+    per = toa.naive_tree_row_draws(rows, tokens, parent, outs)
+    pv = [chi2_pvalue(d, *rows[r]) for r, d in enumerate(per) if len(d) >= 200]
+    assert len(pv) >= 3 and min(pv) >= 1e-3 / len(pv), pv
+
+
+def test_naive_tree_walk_on_drafted_trees():
+    """Prompt-lookup trees (a different tree per window, padded with
+    never-matching nodes, one malformed parent) with seeded per-window rows
+    that favour the tree's tokens, fed identically to both sides: GPU
+    tokens equal the oracle's."""
+    from oracle.accept import accept_naive_tree
+    from synth import lookup_context
+
+    ctx = lookup_context(1870, 20000, vocab=4096)
+    g = np.random.default_rng(1872)
+    B, K = 256, 24
+    tokens = np.full((B, K), -2, dtype=np.int32)
+    parents = np.full((B, K), -1, dtype=np.int32)
+    rows = []
+    for b in range(B):
+        e = int(g.integers(1000, len(ctx) - 16))
+        tk, par = vs.lookup_tree(ctx[:e], 3, 3, 8, K)
+        tokens[b, :len(tk)], parents[b, :len(tk)] = tk, par
+        for r in range(K + 1):
+            # row r: its children's tokens plus random ones, children weighted up
+            kids = [int(tk[j]) for j in range(len(tk)) if (par[j] + 1 if par[j] >= 0 else 0) == r]
+            other = [int(t) for t in g.integers(0, 4096, size=12) if int(t) not in kids]
+            ids = np.array(kids + other, dtype=np.int32)
+            w = np.concatenate([np.full(len(kids), 16.0), g.random(len(other))])
+            rows.append((ids, (w / w.sum()).astype(np.float32)))
+    parents[0, K - 1] = K + 3                         # malformed: never reached
+    pi, pp, pln = pack(rows)
+    u = uniforms(1874, (B, K + 1, 2))
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_NAIVE_TREE, dev(tokens), (dev(pi), dev(pp), dev(pln)),
+                                 u=dev(u), parent=dev(parents))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        want = accept_naive_tree(rows[b * (K + 1):(b + 1) * (K + 1)], tokens[b], parents[b], u[b])
+        assert list(tok[b, :n[b]]) == want, b
+    print(f"mean emitted per window {np.mean(n):.2f}")
+    assert np.mean(n) > 1.5

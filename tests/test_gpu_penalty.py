@@ -73,3 +73,51 @@ def test_window_zero_and_neutral_are_noops():
     assert np.array_equal(run_dense(x, ctx, d, 0, **P).view(np.uint32), x.view(np.uint32))
     neutral = dict(repeat=1.0, presence=0.0, frequency=0.0)
     assert np.array_equal(run_dense(x, ctx, d, 64, **neutral).view(np.uint32), x.view(np.uint32))
+
+
+def tree_cases():
+    """(ctx, tokens, parent) trees: prompt-lookup trees over copied lines, a
+    chain, a 63-node tree, a root-only tree and malformed parents."""
+    from synth import lookup_context
+
+    V = 4096
+    ctx = lookup_context(1620, 6000, vocab=V)
+    out = []
+    for e, n, B, D in ((2000, 3, 3, 8), (4100, 2, 4, 6), (5990, 3, 3, 8)):
+        tk, par = vs.lookup_tree(ctx[:e], n, B, D, 24)
+        out.append((ctx[:e], tk, par))
+    g = np.random.default_rng(1621)
+    chain = g.integers(0, V, size=10).astype(np.int32)
+    out.append((ctx[:300], chain, np.arange(-1, 9, dtype=np.int32)))
+    big_par = np.array([-1] + [int(g.integers(-1, j)) for j in range(1, 63)], dtype=np.int32)
+    out.append((ctx[:700], g.integers(0, V, size=63).astype(np.int32), big_par))
+    out.append((ctx[:50], np.zeros(0, dtype=np.int32), np.zeros(0, dtype=np.int32)))
+    bad = np.array([-1, 5, 0, 3, -7], dtype=np.int32)   # parents outside [-1, j) end the path
+    out.append((ctx[:90], g.integers(0, V, size=5).astype(np.int32), bad))
+    return out
+
+
+@pytest.mark.parametrize("case", range(7))
+@pytest.mark.parametrize("window", [64, 5, 4096])
+def test_tree_rows_dense_and_sparse(case, window):
+    """penalize_tree_rows: row 0 sees the context, row 1 + j the context and
+    node j's root path ("Spend the budget on a tree" of the verify-slack
+    page); bit-identical to the oracle, dense and sparse."""
+    from oracle.penalty import penalize_tree_dense, penalize_tree_sparse
+
+    ctx, tk, par = tree_cases()[case]
+    V = 4096
+    rows = len(tk) + 1
+    x = logits(1630 + case, (rows, V))
+    t = dev(x)
+    vs.penalize_tree_rows(t, dev(ctx), dev(tk), dev(par), window=window, **P)
+    want = penalize_tree_dense(x, ctx, tk, par, window, **P)
+    assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))
+    g = np.random.default_rng(1640 + case)
+    ids = np.where(g.random((rows, 8)) < 0.5, g.choice(ctx[-64:], size=(rows, 8)),
+                   g.integers(0, V, size=(rows, 8))).astype(np.int32)
+    vals = logits(1650 + case, (rows, 8))
+    t = dev(vals)
+    vs.penalize_tree_rows(t, dev(ctx), dev(tk), dev(par), window=window, ids=dev(ids), vocab=V, **P)
+    want = penalize_tree_sparse(ids, vals, ctx, tk, par, window, **P)
+    assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))

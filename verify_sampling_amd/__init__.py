@@ -24,6 +24,7 @@ __all__ = [
     "verify_gemv_rows",
     "verify_gemv_rows_workspace_bytes",
     "penalize_rows",
+    "penalize_tree_rows",
     "topk_rows",
     "topk_rows_workspace_bytes",
     "sample_policy_rows",
@@ -35,12 +36,14 @@ __all__ = [
     "ACCEPT_GREEDY_TREE",
     "ACCEPT_POINT_MASS",
     "ACCEPT_NAIVE",
+    "ACCEPT_NAIVE_TREE",
     "POOL",
     "MAX_ROWS",
     "EXPORTED_SYMBOLS",
 ]
 
-ACCEPT_SAMPLED, ACCEPT_GREEDY, ACCEPT_GREEDY_TREE, ACCEPT_POINT_MASS, ACCEPT_NAIVE = 0, 1, 2, 3, 4
+(ACCEPT_SAMPLED, ACCEPT_GREEDY, ACCEPT_GREEDY_TREE, ACCEPT_POINT_MASS, ACCEPT_NAIVE,
+ ACCEPT_NAIVE_TREE) = 0, 1, 2, 3, 4, 5
 POOL = 64
 MAX_ROWS = 24
 
@@ -51,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "verify_gemv_rows_workspace_bytes",
     "verify_gemv_rows",
     "penalize_rows",
+    "penalize_tree_rows",
     "topk_rows_workspace_bytes",
     "topk_rows",
     "sample_policy_rows",
@@ -78,6 +82,7 @@ _SIGNATURES = {
     "verify_gemv_rows_workspace_bytes": ([I32, I32, I32], SZ),
     "verify_gemv_rows": ([P, I64, I32, I32, P, I64, I32, P, I64, P, SZ, P], I32),
     "penalize_rows": ([P, P, I64, I32, I32, I32, P, I32, P, I32, I32, F32, F32, F32, P], I32),
+    "penalize_tree_rows": ([P, P, I64, I32, I32, P, I32, P, P, I32, I32, F32, F32, F32, P], I32),
     "topk_rows_workspace_bytes": ([I32, I32, I32], SZ),
     "topk_rows": ([P, I64, I32, I32, I32, P, P, I64, P, SZ, P], I32),
     "sample_policy_rows": ([P, P, I64, I32, I32, F32, I32, F32, F32, P, P, P, I64, P, P, P], I32),
@@ -212,6 +217,39 @@ def penalize_rows(logits, ctx, drafts, *, window, repeat, presence, frequency, v
         _ptr(drafts, torch.int32, "drafts", True) if n_d else None, n_d,
         int(window), float(repeat), float(presence), float(frequency), _stream(stream))
     _check(st, "penalize_rows")
+    return logits
+
+
+def penalize_tree_rows(logits, ctx, tokens, parent, *, window, repeat, presence, frequency,
+                       vocab=None, ids=None, stream=None):
+    """In-place penalties on the n_nodes + 1 rows of a token tree.
+
+    Row 0 (root) uses the last `window` of ctx; row 1 + j (node j) the last
+    `window` of ctx || the path from the root down to node j.  tokens,
+    parent: int32 [n_nodes] device tensors (parent -1 = root).  Dense or
+    sparse as penalize_rows.
+    """
+    import torch
+
+    rows, width = logits.shape
+    n_nodes = int(tokens.numel()) if tokens is not None else 0
+    if rows != n_nodes + 1:
+        raise VerifySamplingError(f"a tree of {n_nodes} nodes has {n_nodes + 1} rows, got {rows}")
+    if ids is None:
+        vocab = width if vocab is None else vocab
+    elif vocab is None:
+        raise VerifySamplingError("vocab is required in sparse mode")
+    if ids is not None and (tuple(ids.shape) != (rows, width) or ids.stride() != logits.stride()):
+        raise VerifySamplingError("ids must match logits in shape and strides")
+    n_ctx = int(ctx.numel()) if ctx is not None else 0
+    st = library().penalize_tree_rows(
+        _ptr(logits, torch.float32, "logits"), _ptr(ids, torch.int32, "ids", True),
+        _ld(logits, "logits"), width, int(vocab),
+        _ptr(ctx, torch.int32, "ctx", True) if n_ctx else None, n_ctx,
+        _ptr(tokens, torch.int32, "tokens", True) if n_nodes else None,
+        _ptr(parent, torch.int32, "parent", True) if n_nodes else None, n_nodes,
+        int(window), float(repeat), float(presence), float(frequency), _stream(stream))
+    _check(st, "penalize_tree_rows")
     return logits
 
 

@@ -11,6 +11,9 @@
 // "Code map" of "feat(dflash): developer-only online draft tuning" (each row
 // emits its own draw from p; the window goes on while the draw equals the
 // draft).
+// Sampled tree (deterministic drafts such as prompt-lookup trees): the naive
+// verify walked down the tree, each row's own draw deciding which child, if
+// any, the walk enters.
 // Greedy tree: "One RDNA4 verify pass has slack for about two dozen
 // speculative tokens", "Spend the budget on a tree": the longest branch the
 // target agrees with is accepted.
@@ -121,7 +124,31 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * i + 1]));  // -1 if p is empty
       if (lane == n) my_tok = x;
       ++n;
-      if (i == k || x != dr[i]) break;
+      if (i == k || x < 0 || x != dr[i]) break;  // an empty row's -1 always ends the window
+    }
+  } else if (mode == VS_ACCEPT_NAIVE_TREE) {
+    // walk from the root: draw at the current row, move to the child carrying
+    // the draw (lowest number if siblings repeat a token); node numbers only
+    // grow along the walk, so it emits at most k + 1 tokens
+    const int32_t* par = parent + static_cast<int64_t>(b) * k;
+    const float* ub = u + static_cast<int64_t>(b) * (k + 1) * 2;
+    const int32_t my_par = lane < k ? par[lane] : -2;
+    const int32_t my_tk = lane < k ? dr[lane] : -1;
+    const bool node_ok = lane < k && my_par >= -1 && my_par < lane;  // malformed nodes are unreachable
+    int node = -1, row = 0;
+    for (int step = 0; step <= k; ++step) {
+      const int64_t prow = static_cast<int64_t>(b) * d.p_ws + row;
+      const int pl = clamp_len(d.p_len[prow], d.p_ld);
+      const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
+      const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
+      const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * row + 1]));
+      if (lane == n) my_tok = x;
+      ++n;
+      if (x < 0) break;
+      const uint64_t m = __ballot(node_ok && my_par == node && my_tk == x);
+      if (m == 0) break;
+      node = __ffsll(static_cast<long long>(m)) - 1;
+      row = node + 1;
     }
   } else if (mode == VS_ACCEPT_POINT_MASS) {
     const float* ub = u + static_cast<int64_t>(b) * (k + 1) * 2;
@@ -217,16 +244,17 @@ extern "C" int spec_accept_rows(int mode, int B, int k, const int32_t* p_ids, co
                                 const int32_t* parent, const float* u, int32_t* out_tokens,
                                 int32_t* out_n, hipStream_t stream) {
   if (mode != VS_ACCEPT_SAMPLED && mode != VS_ACCEPT_GREEDY && mode != VS_ACCEPT_GREEDY_TREE &&
-      mode != VS_ACCEPT_POINT_MASS && mode != VS_ACCEPT_NAIVE)
+      mode != VS_ACCEPT_POINT_MASS && mode != VS_ACCEPT_NAIVE && mode != VS_ACCEPT_NAIVE_TREE)
     return VS_ERR_PARAM;
   if (B < 1 || k < 0 || k > VS_MAX_DRAFTS) return VS_ERR_SHAPE;
   if (!p_ids || !out_tokens || !out_n) return VS_ERR_NULL;
   if (k > 0 && !drafts) return VS_ERR_NULL;
   if (p_ld < 1 || p_ld > VS_POOL || p_win_stride < 0) return VS_ERR_SHAPE;
   if (mode == VS_ACCEPT_GREEDY_TREE && k > 0 && !parent) return VS_ERR_NULL;
-  if (mode == VS_ACCEPT_POINT_MASS || mode == VS_ACCEPT_NAIVE) {
+  if (mode == VS_ACCEPT_POINT_MASS || mode == VS_ACCEPT_NAIVE || mode == VS_ACCEPT_NAIVE_TREE) {
     if (!p_probs || !p_len || !u) return VS_ERR_NULL;
   }
+  if (mode == VS_ACCEPT_NAIVE_TREE && k > 0 && !parent) return VS_ERR_NULL;
   if (mode == VS_ACCEPT_SAMPLED) {
     if (!p_probs || !p_len || !u) return VS_ERR_NULL;
     if (k > 0 && (!q_ids || !q_probs || !q_len)) return VS_ERR_NULL;

@@ -3,6 +3,11 @@
 // "Speculative decoding on RDNA", §04 (figure "the penalty history of verify
 // row i"): row i is penalised against H_i = last W tokens of (prompt ||
 // emitted || drafts[0, i)); the draft step for row i uses the same H_i.
+// penalize_tree_rows: the same rule per branch of a token tree ("One RDNA4
+// verify pass has slack for about two dozen speculative tokens", "Spend the
+// budget on a tree": each branch sees only its ancestors): row 0 is the root
+// (history = the context), row 1 + j is node j (history = context || the
+// tokens on the path from the root down to node j).
 //
 // One workgroup per row.  The row's history (<= VS_MAX_WINDOW ids) is staged
 // in LDS; each thread owns history positions (dense mode) or candidate slots
@@ -28,17 +33,47 @@ __device__ __forceinline__ float penalize_one(float l, int c, float rep, float p
 __global__ void __launch_bounds__(THREADS)
 penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int64_t ld, int width,
                 int vocab, const int32_t* __restrict__ ctx, int ctx_len,
-                const int32_t* __restrict__ drafts, int n_drafts, int window, float rep,
+                const int32_t* __restrict__ drafts, int n_drafts,
+                bool tree, const int32_t* __restrict__ parent, int window, float rep,
                 float pres, float freq) {
   __shared__ int32_t hist[VS_MAX_WINDOW];
+  __shared__ int32_t path[VS_MAX_DRAFTS + 1];
+  __shared__ int path_len;
   const int row = blockIdx.x;
-  const int nd = row < n_drafts ? row : n_drafts;  // drafts visible to this row
+  // the draft tokens this row sees after the context: a chain's first
+  // min(row, n_drafts) drafts, or a tree node's root path
+  int nd = row < n_drafts ? row : n_drafts;
+  const int32_t* dsrc = drafts;
+  if (tree) {  // row 0 is the root; rows 1.. read tokens and parent
+    if (threadIdx.x == 0) {
+      int len = 0;
+      if (row > 0) {
+        // walk up from node row - 1; indices strictly decrease, so <= row steps
+        int child = row - 1, q = parent[child];
+        len = 1;
+        while (q > -1 && q < child) {
+          ++len;
+          child = q;
+          q = parent[q];
+        }
+        child = row - 1;
+        for (int i = len - 1; i >= 0; --i) {
+          path[i] = drafts[child];
+          child = parent[child];
+        }
+      }
+      path_len = len;
+    }
+    __syncthreads();
+    nd = path_len;
+    dsrc = path;
+  }
   const int64_t total = static_cast<int64_t>(ctx_len) + nd;
   const int hlen = static_cast<int>(total < window ? total : window);
   const int64_t start = total - hlen;  // position of H_i[0] in ctx || drafts
   for (int j = threadIdx.x; j < hlen; j += blockDim.x) {
     const int64_t pos = start + j;
-    int32_t t = pos < ctx_len ? ctx[pos] : drafts[pos - ctx_len];
+    int32_t t = pos < ctx_len ? ctx[pos] : dsrc[pos - ctx_len];
     hist[j] = (t >= 0 && t < vocab) ? t : -1;  // ids outside the vocabulary never match
   }
   __syncthreads();
@@ -84,7 +119,29 @@ extern "C" int penalize_rows(float* logits, const int32_t* ids, int64_t ld, int 
     return VS_ERR_PARAM;
   if (window == 0 || (ctx_len == 0 && n_drafts == 0)) return VS_OK;  // nothing to penalise
   penalize_kernel<<<dim3(rows), dim3(THREADS), 0, stream>>>(logits, ids, ld, width, vocab, ctx,
-                                                            ctx_len, drafts, n_drafts, window,
-                                                            repeat, presence, frequency);
+                                                            ctx_len, drafts, n_drafts, false,
+                                                            nullptr, window, repeat, presence,
+                                                            frequency);
+  return vs::check_launch();
+}
+
+extern "C" int penalize_tree_rows(float* logits, const int32_t* ids, int64_t ld, int width,
+                                  int vocab, const int32_t* ctx, int ctx_len,
+                                  const int32_t* tokens, const int32_t* parent, int n_nodes,
+                                  int window, float repeat, float presence, float frequency,
+                                  hipStream_t stream) {
+  if (!logits) return VS_ERR_NULL;
+  if (ctx_len < 0 || n_nodes < 0 || n_nodes > VS_MAX_DRAFTS) return VS_ERR_SHAPE;
+  if ((ctx_len > 0 && !ctx) || (n_nodes > 0 && (!tokens || !parent))) return VS_ERR_NULL;
+  if (width < 1 || ld < width || vocab < 1) return VS_ERR_SHAPE;
+  if (ids == nullptr && width != vocab) return VS_ERR_SHAPE;
+  if (window < 0 || window > VS_MAX_WINDOW) return VS_ERR_PARAM;
+  if (!(repeat > 0.f) || !__builtin_isfinite(repeat) || !__builtin_isfinite(presence) ||
+      !__builtin_isfinite(frequency))
+    return VS_ERR_PARAM;
+  if (window == 0 || (ctx_len == 0 && n_nodes == 0)) return VS_OK;  // nothing to penalise
+  penalize_kernel<<<dim3(n_nodes + 1), dim3(THREADS), 0, stream>>>(
+      logits, ids, ld, width, vocab, ctx, ctx_len, tokens, n_nodes, true, parent, window, repeat,
+      presence, frequency);
   return vs::check_launch();
 }
