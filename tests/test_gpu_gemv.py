@@ -123,9 +123,9 @@ def test_strided_operands():
 @pytest.mark.parametrize("N,K", [(65573, 1064), (6151, 4104), (24576, 4096), (4096, 12288),
                                  (6144, 4096)])
 def test_shared_activation_paths_bit_identical(N, K):
-    """From 9 rows on, wide matrices (N >= 65536) and matrices of >= 48 MB run
+    """Above 16 rows, wide matrices (N >= 65536) and matrices of >= 48 MB run
     the shared-activation kernels (the latter with a workspace of K-partition
-    partial sums).  Their rows equal the 1-row call bit for bit, with the
+    partial sums); up to 16 rows the row-block kernels.  Their rows equal the 1-row call bit for bit, with the
     workspace and without it, and match the oracle.  Ragged N and a partial
     last k-block are included."""
     W = torch_bf16_weights((N, K), 3000 + N % 97 + K % 89, "cuda:0")
@@ -141,4 +141,26 @@ def test_shared_activation_paths_bit_identical(N, K):
     w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
     ref, s = gemv_rows(w_rows, x)
     err = np.abs(y[:, rows].astype(np.float64) - ref)
+    assert (err <= TOL * s).all()
+
+
+@pytest.mark.parametrize("N,K", [(4100, 4096), (6150, 4096), (70001, 2048), (1000, 12288),
+                                 (17, 4096)])
+def test_staged_row_block_ragged_rows(N, K):
+    """Up to 8 rows (and below 6144 matrix rows at any R) the row-block kernel
+    stages row runs through LDS; ragged N exercises its clamped rows.
+    Matches the oracle on sampled rows, and rows equal 1-row calls bit for
+    bit up to 24 rows (where other kernels take over)."""
+    W = torch_bf16_weights((N, K), 3300 + N % 101, "cuda:0")
+    x = np.random.default_rng(3310 + N % 101).standard_normal((24, K)).astype(np.float32)
+    X = dev(x)
+    single = np.stack([host(vs.verify_gemv_rows(W, X[r:r + 1]))[0] for r in range(24)])
+    for R in (2, 4, 8, 12, 24):
+        y = host(vs.verify_gemv_rows(W, X[:R].contiguous()))
+        assert np.array_equal(y.view(np.uint32), single[:R].view(np.uint32)), f"R={R}"
+    rows = sampled_rows(N, 600, 3320 + N % 101)
+    w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
+    ref, s = gemv_rows(w_rows, x[:8])
+    y8 = host(vs.verify_gemv_rows(W, X[:8].contiguous()))
+    err = np.abs(y8[:, rows].astype(np.float64) - ref)
     assert (err <= TOL * s).all()

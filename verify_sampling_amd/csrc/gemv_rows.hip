@@ -28,10 +28,16 @@
 //    accumulated from zero in increasing k order, and the partition sums
 //    are added left to right.  Every kernel below follows exactly this
 //    order, so they all give the same bits and may be chosen per R.
-//  * Row-block kernel: workgroup = `splits` wavefronts over T 16-row tiles;
+//  * Row-block kernels: workgroup = `splits` wavefronts over T 16-row tiles;
 //    wave w owns partition w; partial sums meet in LDS.  Every wave loads
-//    and splits the activations of its partition itself.
-//  * Shared-activation kernels (R > 8): a workgroup of P wavefronts along N
+//    and splits the activations of its partition itself.  The MFMA operand
+//    layout wants 16 rows x 64 bytes per load instruction, which HBM serves
+//    worse than long row runs, so the staged variant loads 8 rows x 128
+//    bytes per instruction (branch-free, one stage ahead) and restages each
+//    stage through the wave's own LDS region into the operand layout.  The
+//    plain variant (operands loaded in place) covers the shapes the staged
+//    one does not (K % 32 != 0, short partitions, more than 8 waves).
+//  * Shared-activation kernels (R > 16): a workgroup of P wavefronts along N
 //    loads each activation tile once, splits it once into the three bf16
 //    planes in LDS, and all P waves read their MFMA operand from there.
 //    This divides the activation traffic per weight byte by P, which is what
@@ -265,6 +271,153 @@ gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
   }
 }
 
+// Staged row-block kernel: stage = U k-blocks of the wave's T*16 rows, loaded
+// as RPI rows x RB bytes per instruction (row runs instead of the operand
+// layout's 16 x 64 bytes), written to the wave's LDS region (rows padded by
+// 16 bytes so that the operand reads spread over the banks) and read back as
+// MFMA A operands.  Loads carry no per-lane guards, so the next stage stays
+// in flight while this one is computed: a stage past the partition's end
+// re-reads the partition's last k-blocks and computes nothing.  Same
+// partition, k order and reduction as gemv_rows_kernel.  Requires
+// K % 32 == 0, every partition >= U k-blocks, and <= LB threads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int T, int U, int CT>
+struct RunStage {
+  u32x4 w[T * TILE * U * 64 / 1024];  // this lane's 16-byte pieces of the stage
+  float4 x[U][CT][2];
+};
+
+template <int T, int U, int CT, int LB>
+__global__ void __launch_bounds__(LB)
+gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
+                        const float* __restrict__ X, int64_t ldx, int R,
+                        float* __restrict__ Y, int64_t ldy, int nkb, int splits) {
+  extern __shared__ float red[];  // stage buffers during the loop, then the reduction
+  constexpr int RB = U * 64;      // bytes of one row per stage
+  constexpr int RS = RB + 16;     // LDS row stride
+  constexpr int LPR = RB / 16;    // lanes per row in one load
+  constexpr int RPI = 64 / LPR;   // rows per load instruction
+  constexpr int NI = T * TILE / RPI;
+  static_assert(64 % LPR == 0 && (T * TILE) % RPI == 0, "stage shape");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int n0 = blockIdx.x * TILE * T;
+  uint8_t* stg = reinterpret_cast<uint8_t*>(red) + static_cast<size_t>(wave) * (T * TILE * RS);
+
+  const uint8_t* wsrc[NI];  // this lane's rows, at its 16-byte column of the stage
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    int wr = n0 + i * RPI + lane / LPR;
+    if (wr >= N) wr = N - 1;  // ragged tile: load a valid row, discard its results
+    wsrc[i] = reinterpret_cast<const uint8_t*>(W + static_cast<int64_t>(wr) * ldw) + (lane % LPR) * 16;
+  }
+  // activation row of this lane's column; columns >= R read row R - 1, and
+  // their (independent) MFMA outputs are never stored
+  const float* xrow[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int r = c * 16 + col;
+    xrow[c] = X + static_cast<int64_t>(r < R ? r : R - 1) * ldx + g * 8;
+  }
+  const int kb0 = static_cast<int>((static_cast<int64_t>(wave) * nkb) / splits);
+  const int kb1 = static_cast<int>((static_cast<int64_t>(wave + 1) * nkb) / splits);
+  f32x4 acc[T][CT];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the stage starting at k-block kb holds blocks [kl, kl + U), kept inside
+  // the wave's partition: a stage issued past its end re-reads the
+  // partition's last blocks (cache hits) instead of the next partition's
+  auto first_block = [&](int kb) { return kb + U <= kb1 ? kb : kb1 - U; };
+  auto issue = [&](RunStage<T, U, CT>& st, int kb) {
+    // activations first: memory returns in issue order
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = static_cast<int64_t>(kb + u < kb1 ? kb + u : kb1 - 1) * KBLK;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        st.x[u][c][0] = *reinterpret_cast<const float4*>(xrow[c] + off);
+        st.x[u][c][1] = *reinterpret_cast<const float4*>(xrow[c] + off + 4);
+      }
+    }
+    const int64_t woff = static_cast<int64_t>(first_block(kb)) * (KBLK * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) st.w[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + woff);
+  };
+  auto compute = [&](const RunStage<T, U, CT>& st, int kb) {
+    const int kl = first_block(kb);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<u32x4*>(stg + (i * RPI + lane / LPR) * RS + (lane % LPR) * 16) = st.w[i];
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb + u >= kb1) break;  // uniform across the wave
+      const int uu = kb + u - kl;
+      u32x4 a[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        a[t] = *reinterpret_cast<const u32x4*>(stg + (t * TILE + col) * RS + uu * (KBLK * 2) + g * 16);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const float xv[8] = {st.x[u][c][0].x, st.x[u][c][0].y, st.x[u][c][0].z, st.x[u][c][0].w,
+                             st.x[u][c][1].x, st.x[u][c][1].y, st.x[u][c][1].z, st.x[u][c][1].w};
+        u32x4 hi, mid, lo;
+        split3(xv, hi, mid, lo);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          acc[t][c] = mfma(a[t], hi, acc[t][c]);
+          acc[t][c] = mfma(a[t], mid, acc[t][c]);
+          acc[t][c] = mfma(a[t], lo, acc[t][c]);
+        }
+      }
+    }
+    wave_lds_sync();  // every lane has read the stage before the next one is written
+  };
+  if (kb0 < kb1) {
+    RunStage<T, U, CT> sa, sb;
+    issue(sa, kb0);
+    for (int kb = kb0; kb < kb1; kb += 2 * U) {
+      issue(sb, kb + U);
+      compute(sa, kb);
+      issue(sa, kb + 2 * U);
+      compute(sb, kb + U);
+    }
+  }
+  __syncthreads();  // the stage buffers become the reduction buffer
+
+  // Partial sums of all waves meet in LDS and are added in wave order.
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red[(((wave * T + t) * CT + c) * 4 + e) * 64 + lane] = acc[t][c][e];
+  __syncthreads();
+  const int per_wave = T * CT * 256;
+  for (int idx = threadIdx.x; idx < per_wave; idx += blockDim.x) {
+    float s = red[idx];
+    for (int w = 1; w < splits; ++w) s += red[w * per_wave + idx];
+    const int l = idx & 63;
+    const int e = (idx >> 6) & 3;
+    const int c = (idx >> 8) % CT;
+    const int t = (idx >> 8) / CT;
+    const int n = n0 + t * TILE + 4 * (l >> 4) + e;
+    const int r = c * 16 + (l & 15);
+    if (n < N && r < R) Y[static_cast<int64_t>(r) * ldy + n] = s;
+  }
+}
+
 // Activations of one pipeline stage in the MFMA B-operand layout, split into
 // three bf16 planes: [U k-blocks][hi, mid, lo][CT column tiles][64 lanes].
 template <int U, int CT>
@@ -491,15 +644,16 @@ int splits_for(int N, int K) {
   return s;  // <= MAX_SPLITS
 }
 
-// Which kernel runs for (N, K, R).  Chosen by sweeps on MI355X: up to 8
-// rows the row-block kernel is fastest; from 9 rows on, activation traffic
-// dominates it and the shared-activation kernels take over (all-K for very
-// wide matrices, partitions across workgroups for matrices of >= 48 MB);
-// small matrices stay on the row-block kernel, whose launch is cheapest.
+// Which kernel runs for (N, K, R).  Chosen by sweeps of the whole verify
+// pass on MI355X: up to 16 rows (one activation column tile) the row-block
+// kernel is fastest; above that its activation traffic dominates and the
+// shared-activation kernels take over (all-K for very wide matrices,
+// partitions across workgroups for matrices of >= 48 MB); small matrices
+// stay on the row-block kernel, whose launch is cheapest.
 enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK };
 
 Kind kind_for(int N, int K, int R) {
-  if (R <= 8) return Kind::kRowBlock;
+  if (R <= 16) return Kind::kRowBlock;
   if (N >= 65536) return Kind::kSharedAllK;
   if (2.0 * N * K >= 48e6) return Kind::kSharedSplitK;
   return Kind::kRowBlock;
@@ -542,8 +696,7 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
       kernel<<<grid, dim3(64 * P), 0, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nullptr, 0, nkb,
                                                 splits);
     };
-    if (R <= 16) launch(gemv_shared_kernel<2, 4, 1, 2, false>, 2, 2);
-    else launch(gemv_shared_kernel<1, 2, 2, 8, false>, 1, 8);
+    launch(gemv_shared_kernel<1, 2, 2, 8, false>, 1, 8);  // R > 16: two column tiles
     return vs::check_launch();
   }
   if (kind == Kind::kSharedSplitK) {
@@ -554,14 +707,8 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
       kernel<<<grid, dim3(64 * P), 0, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, parts, ldp, nkb,
                                                 splits);
     };
-    if (R <= 16) {
-      if (N >= 16384) launch(gemv_shared_kernel<1, 2, 1, 8, true>, 1, 8);
-      else if (K >= 8192) launch(gemv_shared_kernel<1, 4, 1, 2, true>, 1, 2);
-      else launch(gemv_shared_kernel<1, 4, 1, 4, true>, 1, 4);
-    } else {
-      if (N >= 16384) launch(gemv_shared_kernel<1, 2, 2, 8, true>, 1, 8);
-      else launch(gemv_shared_kernel<1, 2, 2, 4, true>, 1, 4);
-    }
+    if (N >= 16384) launch(gemv_shared_kernel<1, 2, 2, 8, true>, 1, 8);  // R > 16
+    else launch(gemv_shared_kernel<1, 2, 2, 4, true>, 1, 4);
     int st = vs::check_launch();
     if (st != VS_OK) return st;
     const int quads = static_cast<int>((N + 3) / 4);
@@ -571,6 +718,26 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   }
 
   const dim3 block(64 * splits);
+  // Staged row-block kernel where its conditions hold: every row-block
+  // launch up to 16 rows, and the matrices below 6144 rows (o) at any R.
+  constexpr int STAGE_U = 2;
+  const bool staged_ok = K % KBLK == 0 && nkb / splits >= STAGE_U && splits <= 8;
+  if (staged_ok && (R <= 16 || N < 6144)) {
+    auto launch_staged = [&](auto kernel, int T, int CT) {
+      const dim3 grid((N + TILE * T - 1) / (TILE * T));
+      size_t shm = static_cast<size_t>(splits) * T * CT * 256 * sizeof(float);
+      const size_t stage = static_cast<size_t>(splits) * T * TILE * (STAGE_U * KBLK * 2 + 16);
+      if (stage > shm) shm = stage;
+      kernel<<<grid, block, shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
+    };
+    if (N < 6144) {
+      if (R <= 16) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512>, 1, 1);
+      else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512>, 1, 2);
+    } else {
+      launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512>, 2, 1);  // R <= 16
+    }
+    return vs::check_launch();
+  }
   // Row-block tile shape by matrix shape and R (it never changes a row's
   // summation order): taller matrices take more row tiles per wave, which
   // divides the activation traffic and the splitting work per weight;
