@@ -54,9 +54,9 @@ def test_gemv_rejects_before_launch():
     assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 4) == 0
     assert lib.verify_gemv_rows_workspace_bytes(151936, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 4) == 0
-    # 4096 x 12288 at 24 rows: 8 K partitions of 24 x 4096 fp32 partial sums
+    # 4096 x 12288 at 24 rows: 16 K partitions of 24 x 4096 fp32 partial sums
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 16) == 0
-    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 24) == 8 * 24 * 4096 * 4
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 24) == 16 * 24 * 4096 * 4
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 25) == 0
 
 

@@ -277,9 +277,11 @@ gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
 // 16 bytes so that the operand reads spread over the banks) and read back as
 // MFMA A operands.  Loads carry no per-lane guards, so the next stage stays
 // in flight while this one is computed: a stage past the partition's end
-// re-reads the partition's last k-blocks and computes nothing.  Same
-// partition, k order and reduction as gemv_rows_kernel.  Requires
-// K % 32 == 0, every partition >= U k-blocks, and <= LB threads.
+// re-reads the range's last k-blocks and computes nothing.  Wave w owns PPW
+// consecutive partitions (one accumulator set each), so the partition count
+// can exceed the wave count; the partition sums are added in partition
+// order, as in gemv_rows_kernel.  Requires K % 32 == 0, every partition >= U
+// k-blocks, and <= LB threads.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
@@ -292,7 +294,7 @@ struct RunStage {
   float4 x[U][CT][2];
 };
 
-template <int T, int U, int CT, int LB>
+template <int T, int U, int CT, int LB, int PPW>
 __global__ void __launch_bounds__(LB)
 gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
                         const float* __restrict__ X, int64_t ldx, int R,
@@ -326,17 +328,22 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
     const int r = c * 16 + col;
     xrow[c] = X + static_cast<int64_t>(r < R ? r : R - 1) * ldx + g * 8;
   }
-  const int kb0 = static_cast<int>((static_cast<int64_t>(wave) * nkb) / splits);
-  const int kb1 = static_cast<int>((static_cast<int64_t>(wave + 1) * nkb) / splits);
-  f32x4 acc[T][CT];
+  static_assert(PPW == 1 || PPW == 2, "partitions per wave");
+  const int p0 = wave * PPW;
+  const int kb0 = static_cast<int>((static_cast<int64_t>(p0) * nkb) / splits);
+  const int kb1 = static_cast<int>((static_cast<int64_t>(p0 + PPW) * nkb) / splits);
+  const int kbm = static_cast<int>((static_cast<int64_t>(p0 + 1) * nkb) / splits);  // 2nd partition
+  f32x4 acc[PPW][T][CT];
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int q = 0; q < PPW; ++q)
 #pragma unroll
-    for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) acc[q][t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // the stage starting at k-block kb holds blocks [kl, kl + U), kept inside
-  // the wave's partition: a stage issued past its end re-reads the
-  // partition's last blocks (cache hits) instead of the next partition's
+  // the wave's range: a stage issued past its end re-reads the range's last
+  // blocks (cache hits) instead of the next wave's
   auto first_block = [&](int kb) { return kb + U <= kb1 ? kb : kb1 - U; };
   auto issue = [&](RunStage<T, U, CT>& st, int kb) {
     // activations first: memory returns in issue order
@@ -367,19 +374,23 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
 #pragma unroll
       for (int t = 0; t < T; ++t)
         a[t] = *reinterpret_cast<const u32x4*>(stg + (t * TILE + col) * RS + uu * (KBLK * 2) + g * 16);
+      auto accumulate = [&](f32x4 (&ac)[T][CT]) {
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const float xv[8] = {st.x[u][c][0].x, st.x[u][c][0].y, st.x[u][c][0].z, st.x[u][c][0].w,
-                             st.x[u][c][1].x, st.x[u][c][1].y, st.x[u][c][1].z, st.x[u][c][1].w};
-        u32x4 hi, mid, lo;
-        split3(xv, hi, mid, lo);
+        for (int c = 0; c < CT; ++c) {
+          const float xv[8] = {st.x[u][c][0].x, st.x[u][c][0].y, st.x[u][c][0].z, st.x[u][c][0].w,
+                               st.x[u][c][1].x, st.x[u][c][1].y, st.x[u][c][1].z, st.x[u][c][1].w};
+          u32x4 hi, mid, lo;
+          split3(xv, hi, mid, lo);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          acc[t][c] = mfma(a[t], hi, acc[t][c]);
-          acc[t][c] = mfma(a[t], mid, acc[t][c]);
-          acc[t][c] = mfma(a[t], lo, acc[t][c]);
+          for (int t = 0; t < T; ++t) {
+            ac[t][c] = mfma(a[t], hi, ac[t][c]);
+            ac[t][c] = mfma(a[t], mid, ac[t][c]);
+            ac[t][c] = mfma(a[t], lo, ac[t][c]);
+          }
         }
-      }
+      };
+      if (PPW == 1 || kb + u < kbm) accumulate(acc[0]);  // uniform across the wave
+      else accumulate(acc[PPW - 1]);
     }
     wave_lds_sync();  // every lane has read the stage before the next one is written
   };
@@ -395,14 +406,16 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   }
   __syncthreads();  // the stage buffers become the reduction buffer
 
-  // Partial sums of all waves meet in LDS and are added in wave order.
+  // Partition sums meet in LDS and are added in partition order.
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int q = 0; q < PPW; ++q)
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[(((wave * T + t) * CT + c) * 4 + e) * 64 + lane] = acc[t][c][e];
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          red[((((p0 + q) * T + t) * CT + c) * 4 + e) * 64 + lane] = acc[q][t][c][e];
   __syncthreads();
   const int per_wave = T * CT * 256;
   for (int idx = threadIdx.x; idx < per_wave; idx += blockDim.x) {
@@ -632,16 +645,20 @@ reduce_partials_kernel(const float* __restrict__ parts, int64_t ldp, int splits,
     if (n + e < N) dst[e] = s[e];
 }
 
-// Waves per workgroup (the k-split): a function of N and K alone, so that
-// the summation order of a row does not change with R.  Wide matrices (many
-// row tiles) do best with few, long waves; narrower ones split K further
-// for parallelism.  Chosen by a sweep on MI355X.
+// K partitions (the k-split): a function of N and K alone, so that the
+// summation order of a row does not change with R.  Wide matrices (many row
+// tiles) do best with few, long partitions; narrower ones split K further
+// for parallelism: 8 partitions, or 16 for long rows (the staged row-block
+// kernel then walks two partitions per wave and keeps its wave count, the
+// split-K kernel gets 16 workgroups per row block, which is what matters
+// above 16 rows).  Chosen by sweeps of the verify pass on MI355X.
 int splits_for(int N, int K) {
   const int nkb = (K + KBLK - 1) / KBLK;
-  int s = (N >= 16384) ? (nkb + 31) / 32 : (nkb + 15) / 16;
-  if (s < 1) s = 1;
-  if (s > (N >= 16384 ? 16 : 8)) s = (N >= 16384 ? 16 : 8);
-  return s;  // <= MAX_SPLITS
+  int s;
+  if (N >= 16384) s = (nkb + 31) / 32 < 16 ? (nkb + 31) / 32 : 16;
+  else if (nkb >= 256) s = 16;  // long rows (4096 x 12288): more, shorter partitions
+  else s = (nkb + 15) / 16 < 8 ? (nkb + 15) / 16 : 8;
+  return s < 1 ? 1 : s;  // <= MAX_SPLITS
 }
 
 // Which kernel runs for (N, K, R).  Chosen by sweeps of the whole verify
@@ -721,20 +738,29 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   // Staged row-block kernel where its conditions hold: every row-block
   // launch up to 16 rows, and the matrices below 6144 rows (o) at any R.
   constexpr int STAGE_U = 2;
-  const bool staged_ok = K % KBLK == 0 && nkb / splits >= STAGE_U && splits <= 8;
+  const bool staged_ok = K % KBLK == 0 && nkb / splits >= STAGE_U &&
+                         (splits <= 8 || splits % 2 == 0);
   if (staged_ok && (R <= 16 || N < 6144)) {
+    const int ppw = splits > 8 ? 2 : 1;  // partitions per wave: at most 8 waves
+    const int waves = splits / ppw;
     auto launch_staged = [&](auto kernel, int T, int CT) {
       const dim3 grid((N + TILE * T - 1) / (TILE * T));
       size_t shm = static_cast<size_t>(splits) * T * CT * 256 * sizeof(float);
-      const size_t stage = static_cast<size_t>(splits) * T * TILE * (STAGE_U * KBLK * 2 + 16);
+      const size_t stage = static_cast<size_t>(waves) * T * TILE * (STAGE_U * KBLK * 2 + 16);
       if (stage > shm) shm = stage;
-      kernel<<<grid, block, shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
+      kernel<<<grid, dim3(64 * waves), shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
     };
     if (N < 6144) {
-      if (R <= 16) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512>, 1, 1);
-      else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512>, 1, 2);
-    } else {
-      launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512>, 2, 1);  // R <= 16
+      if (R <= 16) {
+        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 2>, 1, 1);
+        else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 1>, 1, 1);
+      } else {
+        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 2>, 1, 2);
+        else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 1>, 1, 2);
+      }
+    } else {  // R <= 16
+      if (ppw == 2) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2>, 2, 1);
+      else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1>, 2, 1);
     }
     return vs::check_launch();
   }
