@@ -266,6 +266,56 @@ def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, war
             "mean_emitted_per_window": mean_emitted}
 
 
+def draft_side(torch, vs, synth, dev, steps=50, warmup=5):
+    """Draft-side work of one window: the top-16 of 15 draft rows over the
+    151936-token vocabulary (with planted near-ties), then greedy acceptance
+    of a 15-draft chain and of a 3-branch x depth-8 tree.  Launches go
+    straight to the C ABI with cached arguments, so the times are the GPU's."""
+    lib = vs.library()
+    stream = torch.cuda.current_stream().cuda_stream
+    V = synth.VOCAB
+    x = torch.from_numpy(synth.topk_planted_rows(8300, rows=15, vocab=V, K=16)).to(dev)
+    vals = torch.empty((15, 16), device=dev)
+    idx = torch.empty((15, 16), dtype=torch.int32, device=dev)
+    nws = vs.topk_rows_workspace_bytes(15, V, 16)
+    ws = torch.empty(max(16, nws), dtype=torch.uint8, device=dev)
+
+    def topk():
+        st = lib.topk_rows(x.data_ptr(), V, 15, V, 16, vals.data_ptr(), idx.data_ptr(), 16, ws.data_ptr(), nws, stream)
+        assert st == 0, st
+
+    ms_topk = time_region(torch, topk, steps, warmup)
+    topk_bytes = 15 * V * 4 + 15 * 16 * 8
+
+    def accept_launcher(mode, tokens, p_ids, parent, k):
+        tok = torch.empty((1, k + 1), dtype=torch.int32, device=dev)
+        n = torch.empty((1,), dtype=torch.int32, device=dev)
+        args = (mode, 1, k, p_ids.data_ptr(), None, None, p_ids.shape[1], k + 1, None, None, None, 1, 0,
+                tokens.data_ptr(), parent.data_ptr() if parent is not None else None, None,
+                tok.data_ptr(), n.data_ptr(), stream)
+
+        def run():
+            st = lib.spec_accept_rows(*args)
+            assert st == 0, st
+        return run
+
+    argmax, drafts = synth.chain_greedy_case(8301, 15, 7)
+    p_chain = torch.full((16, 2), -1, dtype=torch.int32, device=dev)
+    p_chain[:, 0] = torch.from_numpy(argmax).to(dev)
+    d_chain = torch.from_numpy(drafts[None, :]).to(dev)
+    ms_chain = time_region(torch, accept_launcher(vs.ACCEPT_GREEDY, d_chain, p_chain, None, 15), steps, warmup)
+    parent, tokens, t_am = synth.tree_greedy_case(8302, 3, 8, 1, 5)
+    p_tree = torch.full((25, 2), -1, dtype=torch.int32, device=dev)
+    p_tree[:, 0] = torch.from_numpy(t_am).to(dev)
+    d_tree = torch.from_numpy(tokens[None, :]).to(dev)
+    par = torch.from_numpy(parent[None, :]).to(dev)
+    ms_tree = time_region(torch, accept_launcher(vs.ACCEPT_GREEDY_TREE, d_tree, p_tree, par, 24), steps, warmup)
+    return {"workload": "15 draft rows x 151936, top-16; greedy chain of 15 drafts; greedy tree 3 x 8",
+            "topk_us": round(ms_topk * 1e3, 2), "topk_gbs": round(topk_bytes / (ms_topk * 1e-3) / 1e9, 1),
+            "greedy_chain_accept_us": round(ms_chain * 1e3, 2),
+            "greedy_tree_accept_us": round(ms_tree * 1e3, 2)}
+
+
 def depth_report(vs, sweep):
     """The draft-depth choice on the measured window cost.
 
@@ -417,6 +467,7 @@ def main():
     sampling = None if args.no_sampling else sampling_batch(torch, vs, synth, dev)
     if sampling:
         log(f"sampling: {sampling['rows_per_s']:.3e} rows/s")
+    draft = None if args.no_sampling else draft_side(torch, vs, synth, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -468,6 +519,7 @@ def main():
         "depth_chooser": depth_report(vs, sweep) if sweep else None,
         "prompt_lookup_drafter": lookup_report(vs, synth),
         "sampling": sampling,
+        "draft_side": draft,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
