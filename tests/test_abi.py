@@ -64,7 +64,11 @@ def test_topk_rejects_before_launch():
     lib = vs.library()
     assert lib.topk_rows(FAKE, 100, 1, 100, 65, FAKE, FAKE, 65, None, 0, None) == -2   # K > 64
     assert lib.topk_rows(FAKE, 10, 1, 10, 11, FAKE, FAKE, 11, None, 0, None) == -2     # K > V
-    assert lib.topk_rows_workspace_bytes(4, 151936, 64) == 4 * 38 * 64 * 8
+    # a few long rows take 1024-element chunks, batches 4096-element ones
+    assert lib.topk_rows_workspace_bytes(4, 151936, 64) == 4 * 149 * 64 * 8
+    assert lib.topk_rows_workspace_bytes(53, 151936, 16) == 53 * 149 * 16 * 8
+    assert lib.topk_rows_workspace_bytes(54, 151936, 64) == 54 * 38 * 64 * 8
+    assert lib.topk_rows_workspace_bytes(4, 1024, 64) == 0
     assert lib.topk_rows_workspace_bytes(4, 4096, 64) == 0
     assert lib.topk_rows(FAKE, 8192, 1, 8192, 8, FAKE, FAKE, 8, None, 0, None) == -5   # workspace
 

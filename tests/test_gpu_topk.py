@@ -180,3 +180,48 @@ def test_batched_wave_kernel_ragged_last_chunk(V, K):
     x[2, :] = 2.0
     check = np.r_[0:8, 8:1024:61]
     compare_rows(x, K, check)
+
+
+def crafted_lane_block(n):
+    """Values for a 1024-element chunk (its first n valid) whose largest values
+    sit in lanes 0-31 of the 16-values-per-lane layout, with distinct group
+    maxima: for K = 64 about 160 elements pass the group-maxima threshold
+    (the widest ranking)."""
+    i = np.arange(n)
+    lane = (i % 256) // 4
+    j = 4 * (i // 256) + i % 4
+    out = np.full(n, np.nan, dtype=np.float32)
+    sel = lane < 32
+    out[sel] = (1000.0 + j[sel] + 0.001 * lane[sel]).astype(np.float32)
+    return out, sel
+
+
+@pytest.mark.parametrize("K", [64, 16, 5])
+def test_few_rows_fallbacks_and_ties(K):
+    """A handful of long rows (1024-element chunks, then the merge): crowded
+    lanes in a full and in the ragged last chunk, exact ties over every chunk
+    (the merge's continuation for K = 16 and its second round for K = 64),
+    and NaN chunks with a few numbers (every element survives the group
+    maxima, so the chunk stage's exact threshold runs)."""
+    V = VOCAB
+    x = logits(1520 + K, (5, V))
+    x[3, :3072] = np.nan
+    x[3, [7, 1500, 2049, 3000]] = [1.0, -np.inf, 0.0, 2.5]
+    blk, sel = crafted_lane_block(1024)
+    x[0, :1024][sel] = blk[sel]
+    last = (V // 1024) * 1024
+    blk, sel = crafted_lane_block(V - last)
+    x[1, last:][sel] = blk[sel]
+    x[2] = np.random.default_rng(1525).integers(0, 10, V).astype(np.float32)
+    compare(x, K)
+
+
+@pytest.mark.parametrize("rows", [53, 54])
+def test_chunking_boundary(rows):
+    """53 rows of 151936 take 1024-element chunks, 54 rows take 4096-element
+    chunks; both give the oracle's result."""
+    x = logits(1530 + rows, (rows, VOCAB))
+    x[0] = 1.5
+    x[1] = np.random.default_rng(1531).integers(0, 4, VOCAB).astype(np.float32)
+    x[2, ::2] = np.nan
+    compare_rows(x, 64, np.r_[0:4, rows - 2:rows])

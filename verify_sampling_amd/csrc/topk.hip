@@ -7,213 +7,44 @@
 //
 // Each element becomes a unique 64-bit key (value order, then complemented
 // index; see vs_internal.h), so "top-K" is "the K largest keys" and there
-// are no ties left to break.  Two launches:
-//   stage 1: per (row, chunk of 4096 elements), the K largest keys of the
-//            chunk: a 256-thread radix select for small batches, one
-//            wavefront with a threshold filter for large ones (see
-//            topk_wave_stage1); rows of several chunks write them sorted to
-//            the workspace;
-//   stage 2: one workgroup per row selects the K largest of the chunks' K
-//            candidates by radix select (eight 8-bit digit passes over LDS
-//            histograms) and writes values (the input's bits, re-read by
-//            index) and indices.
-// A row of at most one chunk is finished by stage 1 alone.  The selection is
-// exact integer work, so the result does not depend on scheduling.
+// are no ties left to break.  Every kernel is one wavefront per unit of work
+// (no workgroup barriers), and every selection is a threshold filter: a
+// value every top-K element must reach, the few elements that reach it, and
+// their ranks among themselves.  Two launches:
+//   chunk stage: per (row, chunk), the K largest keys of the chunk (see
+//                topk_chunk_kernel); rows of several chunks write them
+//                sorted to the workspace.  Chunks hold 4096 elements for
+//                batches and 1024 for a handful of rows, so that a single
+//                verify window still spreads over the whole chip;
+//   merge stage: per row, the K largest of the chunks' K candidates (see
+//                topk_merge_kernel), written as values (the input's bits)
+//                and indices.
+// A row of one chunk is finished by the chunk stage alone.  Both stages fall
+// back to an exact radix select when adversarial ties leave too many
+// survivors.  The selection is exact integer work, so the result does not
+// depend on scheduling or on the chunking.
 
 #include "wave_ops.h"
 
 namespace {
 
-constexpr int THREADS = 256;
-constexpr int CHUNK = 4096;
-constexpr int PER = CHUNK / THREADS;  // keys per thread
-constexpr int MAX_CHUNKS = VS_MAX_VOCAB / CHUNK;
-
-struct SelectShared {
-  uint32_t hist[256];
-  uint64_t sel[VS_POOL];
-  uint64_t prefix;
-  int need;
-  int count;
-};
-
-// Leaves the K largest keys of the block (keys of 0 are empty slots) in
-// sh.sel[0, K), sorted descending, padded with 0.  All threads must call it.
-__device__ void block_topk(const uint64_t (&key)[PER], int K, SelectShared& sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  if (tid == 0) sh.count = 0;
-  __syncthreads();
-  int mine = 0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) mine += key[e] != 0;
-  if (mine) atomicAdd(&sh.count, mine);
-  __syncthreads();
-  const int n_real = sh.count;
-  __syncthreads();  // every thread has read the count before it is reused
-
-  uint64_t thr = 1;  // every real key is >= 1
-  if (n_real > K) {
-    uint64_t prefix = 0;
-    int need = K;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
-      sh.hist[tid] = 0;  // THREADS == 256 bins
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const uint64_t k = key[e];
-        if (k != 0 && ((k ^ prefix) & hmask) == 0)
-          atomicAdd(&sh.hist[static_cast<uint32_t>(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l covers bins 255-4l .. 252-4l, highest first
-        uint32_t c[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) c[b] = sh.hist[255 - 4 * lane - b];
-        const uint32_t s = c[0] + c[1] + c[2] + c[3];
-        uint32_t incl = s;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t v = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += v;
-        }
-        const uint32_t excl = incl - s;
-        if (excl < static_cast<uint32_t>(need) && static_cast<uint32_t>(need) <= incl) {
-          uint32_t cum = excl;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            if (cum + c[b] >= static_cast<uint32_t>(need)) {
-              const uint64_t digit = static_cast<uint64_t>(255 - 4 * lane - b);
-              sh.prefix = prefix | (digit << shift);
-              sh.need = need - static_cast<int>(cum);
-              break;
-            }
-            cum += c[b];
-          }
-        }
-      }
-      __syncthreads();
-      prefix = sh.prefix;
-      need = sh.need;
-      __syncthreads();
-    }
-    thr = prefix;  // the K-th largest key; keys are unique, so exactly K are >= thr
-  }
-
-  if (tid == 0) sh.count = 0;
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if (key[e] != 0 && key[e] >= thr) {
-      const int slot = atomicAdd(&sh.count, 1);
-      if (slot < VS_POOL) sh.sel[slot] = key[e];  // exactly K <= VS_POOL keys qualify
-    }
-  }
-  __syncthreads();
-  if (tid < 64) {
-    uint64_t k = lane < sh.count ? sh.sel[lane] : 0ull;
-    uint32_t dummy = 0;
-    vs::wave_sort_desc(k, dummy);
-    sh.sel[lane] = k;
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void write_row(const float* __restrict__ xrow, const uint64_t* sel,
-                                          int K, float* __restrict__ out_vals,
-                                          int32_t* __restrict__ out_idx) {
-  const int lane = threadIdx.x;
-  if (lane < K) {
-    const uint32_t idx = vs::key_index(sel[lane]);
-    out_idx[lane] = static_cast<int32_t>(idx);
-    out_vals[lane] = xrow[idx];  // the input's bits, unchanged
-  }
-}
-
-// Stage 1, one 256-thread workgroup per (row, chunk): lower latency when there
-// are few chunks in total (one verify window), so the chip is mostly idle.
-__global__ void __launch_bounds__(THREADS)
-topk_block_stage1(const float* __restrict__ X, int64_t ldx, int V, int K, int chunks,
-            uint64_t* __restrict__ ws, float* __restrict__ out_vals, int32_t* __restrict__ out_idx,
-            int64_t ld_out) {
-  __shared__ SelectShared sh;
-  const int row = blockIdx.x / chunks, chunk = blockIdx.x % chunks;
-  const float* xrow = X + static_cast<int64_t>(row) * ldx;
-  const int base = chunk * CHUNK;
-  uint64_t key[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int idx = base + e * THREADS + threadIdx.x;
-    key[e] = idx < V ? vs::order_key(__builtin_bit_cast(uint32_t, xrow[idx]), static_cast<uint32_t>(idx))
-                     : 0ull;
-  }
-  block_topk(key, K, sh);
-  if (chunks == 1) {
-    write_row(xrow, sh.sel, K, out_vals + static_cast<int64_t>(row) * ld_out,
-              out_idx + static_cast<int64_t>(row) * ld_out);
-  } else if (threadIdx.x < K) {
-    ws[(static_cast<int64_t>(row) * chunks + chunk) * K + threadIdx.x] = sh.sel[threadIdx.x];
-  }
-}
-
-__global__ void __launch_bounds__(THREADS)
-topk_stage2(const float* __restrict__ X, int64_t ldx, int K, int chunks,
-            const uint64_t* __restrict__ ws, float* __restrict__ out_vals,
-            int32_t* __restrict__ out_idx, int64_t ld_out) {
-  __shared__ SelectShared sh;
-  const int row = blockIdx.x;
-  const int n = chunks * K;  // <= MAX_CHUNKS * VS_POOL == CHUNK
-  const uint64_t* src = ws + static_cast<int64_t>(row) * n;
-  uint64_t key[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int c = e * THREADS + threadIdx.x;
-    key[e] = c < n ? src[c] : 0ull;
-  }
-  block_topk(key, K, sh);
-  write_row(X + static_cast<int64_t>(row) * ldx, sh.sel, K,
-            out_vals + static_cast<int64_t>(row) * ld_out, out_idx + static_cast<int64_t>(row) * ld_out);
-}
-
-// ---------------------------------------------------------------------------
-// Stage 1, one wavefront per (row, chunk of up to 4096 elements).
-//
-// Lane l holds 64 values of the chunk (element j of the lane is chunk index
-// 256*(j/4) + 4*l + j%4, so every load is a coalesced 1 KB), in four groups
-// of 16.  Steps, each cheap in vector instructions:
-//   1. the float maximum of each group (NaN is skipped or, if signalling,
-//      makes the maximum NaN: either way the group holds an element at
-//      least as large, in key order, as the maximum found);
-//   2. v = the K-th largest value key of the 256 group maxima, by a bitwise
-//      search on ballot counts.  The K groups at or above v hold K distinct
-//      elements of value key >= v, so the top K are among the survivors
-//      "value key >= v", a single float comparison x >= t for t the value
-//      whose key is v (NaN never passes, -0 and +0 compare equal as their
-//      keys do; fp32 denormals are kept, so the comparison is exact);
-//   3. the survivors (about 73 for K = 64 on ordinary rows) are compacted to
-//      LDS as (bits, chunk index) pairs;
-//   4. each survivor's rank is the number of larger 64-bit keys among them;
-//      ranks below K are the output positions.
-// If fewer than K group maxima are real numbers, every valid element
-// survives; if more than CAND survive (adversarial rows), an exact per-wave
-// radix select on the 64-bit keys finds the K-th largest key and only the
-// keys at or above it are compacted.  Either way the result is exact: keys
-// are unique.
-
-constexpr int WAVES = 4;               // wavefronts per workgroup
-constexpr int NPL = CHUNK / 64;        // values per lane
-constexpr int GROUPS = 4;              // group maxima per lane
-constexpr int GL = NPL / GROUPS;       // values per group
-constexpr int CAND = 256;              // survivors ranked directly
+constexpr int WAVES = 4;             // wavefronts per workgroup
+constexpr int CAND = 256;            // survivors ranked directly
+constexpr int SMALL_CHUNK = 1024;    // elements per chunk for a few rows
+constexpr int LARGE_CHUNK = 4096;    // elements per chunk for batches
+constexpr int MAX_CHUNKS = VS_MAX_VOCAB / SMALL_CHUNK;
+constexpr int MERGE_LOADS = 24;      // candidates a merge lane reads in one round
+constexpr int SMALL_BATCH_UNITS = 2048;  // fewer 4096-chunks than this: small chunks
 
 struct WaveShared {
   uint32_t bits[CAND + 1];  // survivors' input bits; slot CAND absorbs overflow writes
   uint32_t li[CAND + 1];    // survivors' chunk-local indices
   uint64_t key[CAND];       // survivors' 64-bit keys, zero-padded
-  uint32_t hist[256];       // radix-select histogram (fallback only)
+};
+
+struct MergeShared {
+  uint64_t key[CAND + 1];     // survivors; slot CAND absorbs overflow writes
+  uint32_t cont[MAX_CHUNKS];  // chunk lists: those to read on, the second round's
 };
 
 // Makes this wave's LDS writes visible to its other lanes before they read.
@@ -223,26 +54,35 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t add = 0) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), add));
+}
+
 __device__ __forceinline__ int chunk_index(int lane, int j) { return ((j >> 2) << 8) + (lane << 2) + (j & 3); }
 
 // The hardware three-way maximum, without the compiler's NaN quieting of
-// each operand (its effect on NaN is covered by step 1 above).
+// each operand (its effect on NaN is covered by topk_chunk_kernel, step 1).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 
+// Keeps three ballots in distinct scalar registers until this point, so the
+// compares that make them issue back to back instead of queueing on one
+// condition register.
+__device__ __forceinline__ void pin3(uint64_t a, uint64_t b, uint64_t c) { asm volatile("" ::"s"(a), "s"(b), "s"(c)); }
+
 // The float whose value key is v (v >= 1 and the key of a number).
 __device__ __forceinline__ uint32_t key_bits(uint32_t v) { return (v & 0x80000000u) ? (v ^ 0x80000000u) : ~v; }
 
-// Appends the elements of lane-column j that pass to the survivor list.
+// Appends the elements of one lane-column that pass to the survivor list.
 __device__ __forceinline__ void compact_one(WaveShared& sh, int& count, bool take, uint32_t bits, uint32_t li) {
   const uint64_t m = __ballot(take);
-  if (m == 0) return;  // uniform
   if (take) {
-    uint32_t slot = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), count));
+    uint32_t slot = lanes_below(m, static_cast<uint32_t>(count));
     slot = slot < CAND ? slot : CAND;
     sh.bits[slot] = bits;
     sh.li[slot] = li;
@@ -250,10 +90,21 @@ __device__ __forceinline__ void compact_one(WaveShared& sh, int& count, bool tak
   count += __popcll(m);
 }
 
+__device__ __forceinline__ void compact_key(MergeShared& sh, int& count, bool take, uint64_t key) {
+  const uint64_t m = __ballot(take);
+  if (take) {
+    uint32_t slot = lanes_below(m, static_cast<uint32_t>(count));
+    slot = slot < CAND ? slot : CAND;
+    sh.key[slot] = key;
+  }
+  count += __popcll(m);
+}
+
 // Ranks the c <= 64*E survivors and writes those of rank < K.
 template <int E>
 __device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int base, int chunks,
-                                               int64_t row, int chunk, uint64_t* __restrict__ ws,
+                                               int64_t row, int chunk, const float* __restrict__ xc,
+                                               bool reload, uint64_t* __restrict__ ws,
                                                float* __restrict__ out_vals,
                                                int32_t* __restrict__ out_idx, int64_t ld_out) {
   const int lane = threadIdx.x & 63;
@@ -263,8 +114,8 @@ __device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int
   for (int r = 0; r < E; ++r) {
     const int s = lane + 64 * r;
     const bool live = s < c;
-    b[r] = live ? sh.bits[s] : 0u;
     l[r] = live ? sh.li[s] : 0u;
+    b[r] = live ? (reload ? __builtin_bit_cast(uint32_t, xc[l[r]]) : sh.bits[s]) : 0u;
     k[r] = live ? ((static_cast<uint64_t>(vs::value_key(b[r])) << 32) |
                    static_cast<uint32_t>(~static_cast<uint32_t>(base + static_cast<int>(l[r]))))
                 : 0ull;
@@ -274,12 +125,15 @@ __device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int
   int rank[E];
 #pragma unroll
   for (int r = 0; r < E; ++r) rank[r] = 0;
-  const int cr = (c + 3) & ~3;  // <= 64*E; keys past c are 0
-  for (int s = 0; s < cr; s += 4) {
-    const uint64_t k0 = sh.key[s], k1 = sh.key[s + 1], k2 = sh.key[s + 2], k3 = sh.key[s + 3];
+  const int cr = (c + 15) & ~15;  // <= 64*E; keys past c are 0
+  for (int s = 0; s < cr; s += 16) {
+    uint64_t q[16];
 #pragma unroll
-    for (int r = 0; r < E; ++r)
-      rank[r] += (k0 > k[r]) + (k1 > k[r]) + (k2 > k[r]) + (k3 > k[r]);
+    for (int u = 0; u < 16; ++u) q[u] = sh.key[s + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int r = 0; r < E; ++r) rank[r] += q[u] > k[r];
   }
   const bool single = chunks == 1;
   int64_t obase = single ? row * ld_out : (row * chunks + chunk) * K;
@@ -304,10 +158,41 @@ __device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int
   }
 }
 
+// Chunk stage: one wavefront per (row, chunk of up to 64 * NPL elements).
+//
+// Lane l holds NPL values of the chunk (element j of the lane is chunk index
+// 256*(j/4) + 4*l + j%4, so every load is a coalesced 1 KB), in GROUPS groups
+// per lane.  Steps, each cheap in vector instructions:
+//   1. the float maximum of each group (NaN is skipped or, if signalling,
+//      makes the maximum NaN: either way the group holds an element at
+//      least as large, in key order, as the maximum found);
+//   2. v = the K-th largest value key of the group maxima, by a bitwise
+//      search on ballot counts.  The K groups at or above v hold K distinct
+//      elements of value key >= v, so the top K are among the elements with
+//      value key >= v: those above v, and of those equal to v (a tie, also
+//      the all-equal row) only the ones with the lowest indices, as many as
+//      the elements above v leave to fill.  With t the float whose key is v
+//      these are the float comparisons x > t and x == t (NaN passes neither,
+//      -0 and +0 compare equal as their keys do; fp32 denormals are kept, so
+//      the comparisons are exact);
+//   3. the survivors (a few dozen on ordinary rows) are compacted to LDS as
+//      (bits, chunk index) pairs;
+//   4. each survivor's rank is the number of larger 64-bit keys among them;
+//      ranks below K are the output positions.
+// If fewer than K group maxima are real numbers, every valid element
+// survives.  If more than CAND survive (adversarial rows, where the top
+// values crowd into a few lanes), the threshold is made exact: the K-th
+// largest value key of all the chunk's elements, by the same bitwise search,
+// leaves exactly K survivors after the same compaction.  Either way the
+// result is exact: keys are unique.
+template <int NPL, int GROUPS>
 __global__ void __launch_bounds__(64 * WAVES)
-topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int K, int chunks,
-                 uint64_t* __restrict__ ws, float* __restrict__ out_vals,
-                 int32_t* __restrict__ out_idx, int64_t ld_out) {
+topk_chunk_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int K, int chunks,
+                  uint64_t* __restrict__ ws, float* __restrict__ out_vals,
+                  int32_t* __restrict__ out_idx, int64_t ld_out) {
+  constexpr int CH = 64 * NPL;
+  constexpr int GL = NPL / GROUPS;
+  static_assert(NPL % 4 == 0 && GL >= 3, "chunk shape");
   __shared__ WaveShared shared[WAVES];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -317,13 +202,13 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
   const int chunk = static_cast<int>(unit - static_cast<int64_t>(row) * chunks);
   WaveShared& sh = shared[w];
   const float* xrow = X + static_cast<int64_t>(row) * ldx;
-  const int base = chunk * CHUNK;
-  const int n = V - base < CHUNK ? V - base : CHUNK;
+  const int base = chunk * CH;
+  const int n = V - base < CH ? V - base : CH;
 
-  // the lane's 64 values; elements past the row's end read as NaN, which no
-  // maximum or threshold comparison selects
+  // the lane's NPL values; elements past the row's end read as NaN, which
+  // no maximum or threshold comparison selects
   float x[NPL];
-  const bool vec = n == CHUNK && ((reinterpret_cast<uintptr_t>(xrow + base) & 15u) == 0);
+  const bool vec = n == CH && ((reinterpret_cast<uintptr_t>(xrow + base) & 15u) == 0);
   if (vec) {
 #pragma unroll
     for (int q = 0; q < NPL / 4; ++q) {
@@ -351,24 +236,58 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
     if ((GL - 3) % 2) m = max3f(m, x[GL * g + GL - 1], x[GL * g + GL - 1]);
     mk[g] = vs::value_key(__builtin_bit_cast(uint32_t, m));
   }
+  // two bits per step: the three candidates' counts are independent
   uint32_t v = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = v | (1u << bit);
-    int c = 0;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t c1 = v | (1u << bit), c2 = v | (2u << bit), c3 = v | (3u << bit);
+    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-    for (int g = 0; g < GROUPS; ++g) c += __popcll(__ballot(mk[g] >= cand));
-    if (c >= K) v = cand;
+    for (int g = 0; g < GROUPS; ++g) {
+      const uint64_t b1 = __ballot(mk[g] >= c1), b2 = __ballot(mk[g] >= c2), b3 = __ballot(mk[g] >= c3);
+      pin3(b1, b2, b3);
+      n1 += __popcll(b1);
+      n2 += __popcll(b2);
+      n3 += __popcll(b3);
+    }
+    v = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : v));
   }
 
-  // 3: compaction
+  // 3: compaction: the elements above t and, of those equal to t, the ones
+  // with the lowest chunk indices, until K are taken
   const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   int count = 0;
   if (v != 0) {
     const float t = __builtin_bit_cast(float, key_bits(v));
 #pragma unroll
     for (int j = 0; j < NPL; ++j)
-      compact_one(sh, count, x[j] >= t, __builtin_bit_cast(uint32_t, x[j]),
+      compact_one(sh, count, x[j] > t, __builtin_bit_cast(uint32_t, x[j]),
                   lane4 | static_cast<uint32_t>(((j >> 2) << 8) | (j & 3)));
+    const int need = K - count;  // ties still to take, lowest index first
+    if (need > 0) {
+      int ties_before = 0;  // in the 256-element blocks already passed
+#pragma unroll
+      for (int q = 0; q < NPL / 4; ++q) {
+        // within block q, chunk index order is lane-major, then j % 4
+        uint64_t tb[4];
+        int below = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tb[r] = __ballot(x[4 * q + r] == t);
+          below += static_cast<int>(lanes_below(tb[r]));
+        }
+        int own = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool tie = ((tb[r] >> lane) & 1ull) != 0;
+          compact_one(sh, count, tie && ties_before + below + own < need,
+                      __builtin_bit_cast(uint32_t, x[4 * q + r]), lane4 | static_cast<uint32_t>((q << 8) | r));
+          own += tie;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ties_before += __popcll(tb[r]);
+        if (ties_before >= need) break;  // uniform: no later tie is taken
+      }
+    }
   } else {  // fewer than K group maxima are numbers: every valid element
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
@@ -377,94 +296,403 @@ topk_wave_stage1(const float* __restrict__ X, int64_t ldx, int rows, int V, int 
     }
   }
 
-  if (count > CAND) {
-    // exact radix select of the K-th largest key, 8 bits at a time (more
-    // than CAND >= K valid keys exist here).  This path is rare (adversarial
-    // rows); it re-reads the chunk each pass so that its keys never occupy
-    // registers alongside the main path's.
-    uint64_t prefix = 0;
-    int need = K;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+  const bool exact = count > CAND;
+  if (exact) {
+    // the exact K-th largest value key of the chunk, by the same bitwise
+    // search over every element's value key (padding is NaN, value key 0,
+    // and ranks after every valid element of that key), then the same
+    // compaction: exactly K survivors.  x is turned into value keys in
+    // place; the survivors' bits are read again for output.
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) sh.hist[4 * lane + bb] = 0u;
-      wave_lds_sync();
-      asm volatile("" ::: "memory");  // keep the re-reads inside this pass
-      for (int j = 0; j < NPL; ++j) {
-        const int li = chunk_index(lane, j);
-        if (li >= n) continue;
-        const uint64_t kj = (static_cast<uint64_t>(vs::value_key(__builtin_bit_cast(uint32_t, xrow[base + li]))) << 32) |
-                            static_cast<uint32_t>(~static_cast<uint32_t>(base + li));
-        if (((kj ^ prefix) & hmask) == 0)
-          atomicAdd(&sh.hist[static_cast<uint32_t>(kj >> shift) & 255u], 1u);
-      }
-      wave_lds_sync();
-      uint32_t c[4];
+    for (int j = 0; j < NPL; ++j) x[j] = __builtin_bit_cast(float, vs::value_key(__builtin_bit_cast(uint32_t, x[j])));
+    uint32_t vt = 0;  // (one bit per step: this rare path keeps its scalar registers few)
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = vt | (1u << bit);
+      int c = 0;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) c[bb] = sh.hist[255 - 4 * lane - bb];
-      const uint32_t sum = c[0] + c[1] + c[2] + c[3];
-      uint32_t incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      const uint32_t excl = incl - sum;
-      const bool mine = excl < static_cast<uint32_t>(need) && static_cast<uint32_t>(need) <= incl;
-      int digit = 0, rest = 0;
-      if (mine) {
-        uint32_t cum = excl;
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          if (cum + c[bb] >= static_cast<uint32_t>(need)) {
-            digit = 255 - 4 * lane - bb;
-            rest = need - static_cast<int>(cum);
-            break;
-          }
-          cum += c[bb];
-        }
-      }
-      const int src = __ffsll(static_cast<long long>(__ballot(mine))) - 1;
-      digit = vs::bcast(digit, src);
-      need = vs::bcast(rest, src);
-      prefix |= static_cast<uint64_t>(digit) << shift;
-      wave_lds_sync();
+      for (int j = 0; j < NPL; ++j) c += __popcll(__ballot(__builtin_bit_cast(uint32_t, x[j]) >= cand));
+      if (c >= K) vt = cand;
     }
-    // exactly K keys are >= prefix: compact them again
     count = 0;
-    asm volatile("" ::: "memory");
-    for (int j = 0; j < NPL; ++j) {
-      const int li = chunk_index(lane, j);
-      uint32_t bits = 0;
-      uint64_t kj = 0;
-      if (li < n) {
-        bits = __builtin_bit_cast(uint32_t, xrow[base + li]);
-        kj = (static_cast<uint64_t>(vs::value_key(bits)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(base + li));
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      compact_one(sh, count, __builtin_bit_cast(uint32_t, x[j]) > vt, __builtin_bit_cast(uint32_t, x[j]),
+                  lane4 | static_cast<uint32_t>(((j >> 2) << 8) | (j & 3)));
+    const int need = K - count;  // ties still to take, lowest index first
+    if (need > 0) {
+      int ties_before = 0;  // in the 256-element blocks already passed
+#pragma unroll
+      for (int q = 0; q < NPL / 4; ++q) {
+        // within block q, chunk index order is lane-major, then j % 4
+        uint64_t tb[4];
+        int below = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tb[r] = __ballot(__builtin_bit_cast(uint32_t, x[4 * q + r]) == vt);
+          below += static_cast<int>(lanes_below(tb[r]));
+        }
+        int own = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool tie = ((tb[r] >> lane) & 1ull) != 0;
+          compact_one(sh, count, tie && ties_before + below + own < need,
+                      __builtin_bit_cast(uint32_t, x[4 * q + r]), lane4 | static_cast<uint32_t>((q << 8) | r));
+          own += tie;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ties_before += __popcll(tb[r]);
+        if (ties_before >= need) break;  // uniform: no later tie is taken
       }
-      compact_one(sh, count, kj != 0 && kj >= prefix, bits, static_cast<uint32_t>(li));
     }
   }
 
   // 4: ranks and output
+  if (count > CAND) count = CAND;  // not reached: the exact threshold leaves K
   wave_lds_sync();
+  const float* xc = xrow + base;
   if (count <= 64)
-    rank_and_write<1>(sh, count, K, base, chunks, row, chunk, ws, out_vals, out_idx, ld_out);
+    rank_and_write<1>(sh, count, K, base, chunks, row, chunk, xc, exact, ws, out_vals, out_idx, ld_out);
   else if (count <= 128)
-    rank_and_write<2>(sh, count, K, base, chunks, row, chunk, ws, out_vals, out_idx, ld_out);
+    rank_and_write<2>(sh, count, K, base, chunks, row, chunk, xc, exact, ws, out_vals, out_idx, ld_out);
   else
-    rank_and_write<4>(sh, count, K, base, chunks, row, chunk, ws, out_vals, out_idx, ld_out);
+    rank_and_write<4>(sh, count, K, base, chunks, row, chunk, xc, exact, ws, out_vals, out_idx, ld_out);
 }
 
-int n_chunks(int V) { return (V + CHUNK - 1) / CHUNK; }
+// The K-th largest of the wave's keys k[0..N) (0 = empty slot), or 0 if
+// fewer than K are non-zero.  A bitwise search, two bits per step, first
+// over the value keys (high halves), then, only if more keys than needed
+// share the value key found, over the index halves of those ties.  When
+// the ties are exactly as many as needed the result is the value key with
+// a zero index half: the same keys, exactly K, are at or above it.
+template <int N>
+__device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int K) {
+  uint32_t hi[N], lo[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    hi[i] = static_cast<uint32_t>(k[i] >> 32);
+    lo[i] = static_cast<uint32_t>(k[i]);
+  }
+  uint32_t vh = 0;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t c1 = vh | (1u << bit), c2 = vh | (2u << bit), c3 = vh | (3u << bit);
+    int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      uint32_t h = hi[i];
+      asm volatile("" : "+v"(h));  // keeps the compares of key i after those of key i - 1
+      const uint64_t b1 = __ballot(h >= c1), b2 = __ballot(h >= c2), b3 = __ballot(h >= c3);
+      pin3(b1, b2, b3);
+      n1 += __popcll(b1);
+      n2 += __popcll(b2);
+      n3 += __popcll(b3);
+    }
+    vh = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : vh));
+  }
+  // index halves of the ties, 0 for the other keys (an index half is the
+  // complement of an index below 2^31, so a real one is never 0)
+  int above = 0, ties = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool real = k[i] != 0ull;
+    const bool tie = real && hi[i] == vh;
+    lo[i] = tie ? lo[i] : 0u;
+    above += __popcll(__ballot(real && hi[i] > vh));
+    ties += __popcll(__ballot(tie));
+  }
+  const int need = K - above;
+  if (need > ties) return 0ull;  // fewer than K keys
+  const uint64_t base = static_cast<uint64_t>(vh) << 32;
+  if (need == ties) return base;
+  uint32_t vl = 0;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t c1 = vl | (1u << bit), c2 = vl | (2u << bit), c3 = vl | (3u << bit);
+    int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      uint32_t l = lo[i];
+      asm volatile("" : "+v"(l));
+      const uint64_t b1 = __ballot(l >= c1), b2 = __ballot(l >= c2), b3 = __ballot(l >= c3);
+      pin3(b1, b2, b3);
+      n1 += __popcll(b1);
+      n2 += __popcll(b2);
+      n3 += __popcll(b3);
+    }
+    vl = n3 >= need ? c3 : (n2 >= need ? c2 : (n1 >= need ? c1 : vl));
+  }
+  return base | vl;
+}
+
+// The input bits of the element a key stands for, when the key fixes them
+// (every value but NaN, whose payload, and zero, whose sign, it drops).
+__device__ __forceinline__ bool bits_of_key(uint64_t key, uint32_t& bits) {
+  const uint32_t vk = static_cast<uint32_t>(key >> 32);
+  if (vk == 0u || vk == 0x80000000u) return false;
+  bits = (vk & 0x80000000u) ? (vk & 0x7fffffffu) : ~vk;
+  return true;
+}
+
+// Ranks the c <= 64*E merge survivors and writes those of rank < K.
+template <int E>
+__device__ __forceinline__ void merge_rank_write(MergeShared& sh, int c, int K, int V, const float* __restrict__ xrow,
+                                                 float* __restrict__ ovals, int32_t* __restrict__ oidx) {
+  const int lane = threadIdx.x & 63;
+  uint64_t k[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int s = lane + 64 * r;
+    k[r] = s < c ? sh.key[s] : 0ull;
+  }
+  wave_lds_sync();  // every lane has its key before the tail is cleared
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int s = lane + 64 * r;
+    if (s >= c) sh.key[s] = 0ull;  // below every key
+  }
+  wave_lds_sync();
+  int rank[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) rank[r] = 0;
+  const int cr = (c + 15) & ~15;  // <= 64*E; keys past c are 0
+  for (int s = 0; s < cr; s += 16) {
+    uint64_t q[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) q[u] = sh.key[s + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int r = 0; r < E; ++r) rank[r] += q[u] > k[r];
+  }
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    if (lane + 64 * r < c && rank[r] < K) {
+      const uint32_t idx = vs::key_index(k[r]);
+      uint32_t bits;
+      if (!bits_of_key(k[r], bits)) bits = __builtin_bit_cast(uint32_t, xrow[idx < static_cast<uint32_t>(V) ? idx : 0u]);
+      oidx[rank[r]] = static_cast<int32_t>(idx);
+      ovals[rank[r]] = __builtin_bit_cast(float, bits);  // the input's bits
+    }
+  }
+  if (lane >= c && lane < K) {  // fewer than K elements: empty entries
+    oidx[lane] = -1;
+    ovals[lane] = __builtin_nanf("");
+  }
+}
+
+// Merge stage: one wavefront per row over the chunks' candidate lists (K
+// keys per chunk, sorted descending, zero-padded).
+//   1. v = the K-th largest key among the first jp entries of every chunk
+//      (jp = 1 when there are at least K chunks), by a bitwise search on
+//      ballot counts: those K keys are candidates, so every top-K key is
+//      >= v;
+//   2. the survivors, keys >= v, are a prefix of each chunk's list.  The
+//      first j2 entries of every chunk are read in one round
+//      (chunks * j2 <= 64 * MERGE_LOADS); the chunks whose j2 entries all
+//      survive are read on to the end of their lists;
+//   3. ranks among the survivors, as in the chunk stage.
+// More than CAND survivors (ties resolved by index crowd the top K into the
+// first chunks, as in the all-equal row with K = 64) take a second,
+// narrower round whose survivors are bounded by CAND.
+__global__ void __launch_bounds__(64 * WAVES)
+topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int K, int chunks, int lg_jp,
+                  int lg_j2, const uint64_t* __restrict__ ws, float* __restrict__ out_vals,
+                  int32_t* __restrict__ out_idx, int64_t ld_out) {
+  __shared__ MergeShared shared[WAVES];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int row = blockIdx.x * WAVES + w;
+  if (row >= rows) return;  // whole wave; no block barriers
+  MergeShared& sh = shared[w];
+  const int n = chunks * K;
+  const uint64_t* src = ws + static_cast<int64_t>(row) * n;
+  const int jp = 1 << lg_jp, j2 = 1 << lg_j2;
+
+  // both reads in one round: the threshold's entries (chunks * jp <= 256)
+  // and the first j2 entries of every chunk
+  uint64_t m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = lane + 64 * i;
+    const int c = t >> lg_jp, j = t & (jp - 1);
+    m[i] = (c < chunks && j < K) ? src[c * K + j] : 0ull;
+  }
+  uint64_t e[MERGE_LOADS];
+  const int n2 = chunks << lg_j2;
+#pragma unroll
+  for (int i = 0; i < MERGE_LOADS; ++i) {
+    e[i] = 0ull;
+    if (64 * i < n2) {  // uniform
+      const int s = lane + 64 * i;
+      const int c = s >> lg_j2, j = s & (j2 - 1);
+      if (c < chunks && j < K) e[i] = src[c * K + j];
+    }
+  }
+
+  // 1: the K-th largest key of the threshold's entries (0 if fewer than K)
+  const uint64_t v = wave_kth_largest<4>(m, K);
+
+  // 2: survivors of the first round, and the chunks to read on
+  int count = 0, n_cont = 0;
+#pragma unroll
+  for (int i = 0; i < MERGE_LOADS; ++i) {
+    if (64 * i < n2) {
+      const bool live = e[i] != 0ull && e[i] >= v;
+      compact_key(sh, count, live, e[i]);
+      if (j2 < K) {
+        const int s = lane + 64 * i;
+        const bool more = live && (s & (j2 - 1)) == j2 - 1;  // its chunk's last entry read
+        const uint64_t mm = __ballot(more);
+        if (more) sh.cont[lanes_below(mm, static_cast<uint32_t>(n_cont))] = static_cast<uint32_t>(s >> lg_j2);
+        n_cont += __popcll(mm);
+      }
+    }
+  }
+  wave_lds_sync();
+  if (n_cont > 0 && count <= CAND) {
+    // entries j2 .. K-1 of those chunks, P (a power of two >= K - j2) lanes per chunk
+    const int tail = K - j2;
+    const int lg_p = tail <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(tail - 1));
+    const int total = n_cont << lg_p;
+    for (int s0 = 0; s0 < total && count <= CAND; s0 += 64 * 8) {
+      uint64_t f[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + 64 * u + lane;
+        const int j = j2 + (s & ((1 << lg_p) - 1));
+        f[u] = 0ull;
+        if (s < total && j < K) f[u] = src[static_cast<int>(sh.cont[s >> lg_p]) * K + j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) compact_key(sh, count, f[u] != 0ull && f[u] >= v, f[u]);
+    }
+  }
+
+  if (count > CAND) {
+    // Second round.  Only the chunks whose first entry is >= v can hold a
+    // top-K key: exactly K of them when jp = 1, else at most chunks < K.
+    // Their first jb entries (nrel * jb <= 64 * MERGE_LOADS, so jb >= 16
+    // when jb < K) give the exact K-th largest key v2 of that set; exactly
+    // K read entries are >= v2, so at most K / jb chunks have all jb read
+    // entries >= v2, and only those are read on.  That bounds the
+    // survivors by K * K / jb <= CAND.
+    wave_lds_sync();  // the first round's survivors are dropped
+    int nrel = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = lane + 64 * i;
+      const bool rel = m[i] != 0ull && m[i] >= v && (t & (jp - 1)) == 0;
+      const uint64_t mm = __ballot(rel);
+      if (rel) sh.cont[lanes_below(mm, static_cast<uint32_t>(nrel))] = static_cast<uint32_t>(t >> lg_jp);
+      nrel += __popcll(mm);
+    }
+    wave_lds_sync();
+    int lg_jb = 31 - __builtin_clz(static_cast<unsigned>((64 * MERGE_LOADS) / (nrel > 0 ? nrel : 1)));
+    const int lg_k = K <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(K - 1));
+    lg_jb = lg_jb < lg_k ? lg_jb : lg_k;
+    const int jb = 1 << lg_jb;
+    const int nb = nrel << lg_jb;
+#pragma unroll
+    for (int i = 0; i < MERGE_LOADS; ++i) {
+      e[i] = 0ull;
+      if (64 * i < nb) {  // uniform
+        const int s = lane + 64 * i;
+        const int r = s >> lg_jb, j = s & (jb - 1);
+        if (r < nrel && j < K) e[i] = src[static_cast<int>(sh.cont[r]) * K + j];
+      }
+    }
+    // (one bit per step: this rare path keeps its scalar registers few)
+    uint64_t v2 = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = v2 | (1ull << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < MERGE_LOADS; ++i)
+        if (64 * i < nb) c += __popcll(__ballot(e[i] >= cand));
+      if (c >= K) v2 = cand;
+    }
+    count = 0;
+    int nlong = 0;
+#pragma unroll
+    for (int i = 0; i < MERGE_LOADS; ++i) {
+      if (64 * i < nb) {
+        const int s = lane + 64 * i;
+        const bool live = e[i] != 0ull && e[i] >= v2;
+        compact_key(sh, count, live, e[i]);
+        if (jb < K) {
+          const bool more = live && (s & (jb - 1)) == jb - 1;
+          const uint64_t mm = __ballot(more);
+          // after the relevant list (<= 64 entries)
+          if (more) sh.cont[64 + lanes_below(mm, static_cast<uint32_t>(nlong))] = sh.cont[s >> lg_jb];
+          nlong += __popcll(mm);
+        }
+      }
+    }
+    wave_lds_sync();
+    // entries jb .. K-1 of at most K / jb <= 4 chunks, 64 lanes per chunk
+    for (int u0 = 0; u0 < nlong; u0 += 4) {
+      uint64_t f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + lane;
+        f[u] = 0ull;
+        if (u0 + u < nlong && j < K) f[u] = src[static_cast<int>(sh.cont[64 + u0 + u]) * K + j];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) compact_key(sh, count, f[u] != 0ull && f[u] >= v2, f[u]);
+    }
+  }
+
+  if (count > CAND) count = CAND;  // not reached: the rounds above bound the survivors
+  wave_lds_sync();
+  if (count > 128) {
+    // ranking costs grow with the square of the survivors: cut them to
+    // exactly K first, at the exact K-th largest of them
+    uint64_t r4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = lane + 64 * r;
+      r4[r] = t < count ? sh.key[t] : 0ull;
+    }
+    const uint64_t v3 = wave_kth_largest<4>(r4, K);
+    wave_lds_sync();  // every lane has its keys before the list is rewritten
+    count = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) compact_key(sh, count, r4[r] != 0ull && r4[r] >= v3, r4[r]);
+    wave_lds_sync();
+  }
+  const float* xrow = X + static_cast<int64_t>(row) * ldx;
+  float* ovals = out_vals + static_cast<int64_t>(row) * ld_out;
+  int32_t* oidx = out_idx + static_cast<int64_t>(row) * ld_out;
+  if (count <= 64)
+    merge_rank_write<1>(sh, count, K, V, xrow, ovals, oidx);
+  else if (count <= 128)
+    merge_rank_write<2>(sh, count, K, V, xrow, ovals, oidx);
+  else
+    merge_rank_write<4>(sh, count, K, V, xrow, ovals, oidx);
+}
+
+// Which chunking a call takes; the workspace size follows from it.
+struct Plan {
+  bool small;  // 1024-element chunks
+  int chunks;
+};
+
+Plan plan_for(int rows, int V) {
+  const int large = (V + LARGE_CHUNK - 1) / LARGE_CHUNK;
+  const bool small = V <= SMALL_CHUNK ||
+                     (large > 1 && static_cast<int64_t>(rows) * large < SMALL_BATCH_UNITS);
+  return {small, small ? (V + SMALL_CHUNK - 1) / SMALL_CHUNK : large};
+}
+
+int log2_floor(int x) { return 31 - __builtin_clz(static_cast<unsigned>(x)); }
+int log2_ceil(int x) { return x <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(x - 1)); }
 
 }  // namespace
 
 extern "C" size_t topk_rows_workspace_bytes(int rows, int V, int K) {
   if (rows < 1 || V < 1 || K < 1) return 0;
-  const int chunks = n_chunks(V);
-  if (chunks <= 1) return 0;
-  return static_cast<size_t>(rows) * chunks * K * sizeof(uint64_t);
+  const Plan p = plan_for(rows, V);
+  if (p.chunks <= 1) return 0;
+  return static_cast<size_t>(rows) * p.chunks * K * sizeof(uint64_t);
 }
 
 extern "C" int topk_rows(const float* X, int64_t ldx, int rows, int V, int K, float* out_vals,
@@ -474,26 +702,29 @@ extern "C" int topk_rows(const float* X, int64_t ldx, int rows, int V, int K, fl
   if (rows < 1 || rows > (1 << 24) || K < 1 || K > VS_POOL || V < K || V > VS_MAX_VOCAB)
     return VS_ERR_SHAPE;
   if (ldx < V || ld_out < K) return VS_ERR_SHAPE;
-  const int chunks = n_chunks(V);
-  static_assert(MAX_CHUNKS * VS_POOL <= CHUNK, "stage 2 holds all candidates of a row");
+  const Plan p = plan_for(rows, V);
+  static_assert(MAX_CHUNKS <= 256, "the merge's threshold entries fit four per lane");
+  static_assert(MAX_CHUNKS * 4 <= 64 * MERGE_LOADS, "the merge reads at least four entries per chunk");
   const size_t need = topk_rows_workspace_bytes(rows, V, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return VS_ERR_WORKSPACE;
   if (need > 0 && !vs::aligned16(workspace)) return VS_ERR_ALIGN;
   uint64_t* ws = static_cast<uint64_t*>(workspace);
-  // Both stage-1 kernels give the same keys: a workgroup per chunk has the
-  // lower latency for a handful of rows, a wavefront per chunk the higher
-  // throughput for batches.
-  const int64_t units = static_cast<int64_t>(rows) * chunks;
-  if (units < 2048) {
-    topk_block_stage1<<<dim3(static_cast<unsigned>(units)), dim3(THREADS), 0, stream>>>(
-        X, ldx, V, K, chunks, ws, out_vals, out_idx, ld_out);
-  } else {
-    topk_wave_stage1<<<dim3(static_cast<unsigned>((units + WAVES - 1) / WAVES)), dim3(64 * WAVES), 0,
-                       stream>>>(X, ldx, rows, V, K, chunks, ws, out_vals, out_idx, ld_out);
-  }
+  const int64_t units = static_cast<int64_t>(rows) * p.chunks;
+  const dim3 grid(static_cast<unsigned>((units + WAVES - 1) / WAVES)), block(64 * WAVES);
+  if (p.small)
+    topk_chunk_kernel<16, 4><<<grid, block, 0, stream>>>(X, ldx, rows, V, K, p.chunks, ws, out_vals,
+                                                          out_idx, ld_out);
+  else
+    topk_chunk_kernel<64, 4><<<grid, block, 0, stream>>>(X, ldx, rows, V, K, p.chunks, ws, out_vals,
+                                                          out_idx, ld_out);
   int st = vs::check_launch();
-  if (st != VS_OK || chunks == 1) return st;
-  topk_stage2<<<dim3(rows), dim3(THREADS), 0, stream>>>(X, ldx, K, chunks, ws, out_vals, out_idx,
-                                                        ld_out);
+  if (st != VS_OK || p.chunks == 1) return st;
+  // threshold entries: jp per chunk with chunks * jp >= K; first read: j2
+  // per chunk, the most that fit one round, and no more than the lists hold
+  const int lg_jp = p.chunks >= K ? 0 : log2_ceil((K + p.chunks - 1) / p.chunks);
+  int lg_j2 = log2_floor((64 * MERGE_LOADS) / p.chunks);
+  if (lg_j2 > log2_ceil(K)) lg_j2 = log2_ceil(K);
+  topk_merge_kernel<<<dim3(static_cast<unsigned>((rows + WAVES - 1) / WAVES)), block, 0, stream>>>(
+      X, ldx, rows, V, K, p.chunks, lg_jp, lg_j2, ws, out_vals, out_idx, ld_out);
   return vs::check_launch();
 }
