@@ -123,11 +123,12 @@ def test_strided_operands():
 @pytest.mark.parametrize("N,K", [(65573, 1064), (6151, 4104), (24576, 4096), (4096, 12288),
                                  (6144, 4096)])
 def test_shared_activation_paths_bit_identical(N, K):
-    """Above 16 rows, wide matrices (N >= 65536) and matrices of >= 48 MB run
-    the shared-activation kernels (the latter with a workspace of K-partition
-    partial sums); up to 16 rows the row-block kernels.  Their rows equal the 1-row call bit for bit, with the
-    workspace and without it, and match the oracle.  Ragged N and a partial
-    last k-block are included."""
+    """Matrices of >= 48 MB run the shared-activation kernels with a
+    workspace of K-partition partial sums above 16 rows, those with long rows
+    (4096 x 12288) from 9 rows; wide matrices whose k-blocks do not fit the
+    staged kernel take all-K sharing above 16 rows.  Their rows equal the
+    1-row call bit for bit, with the workspace and without it, and match the
+    oracle.  Ragged N and a partial last k-block are included."""
     W = torch_bf16_weights((N, K), 3000 + N % 97 + K % 89, "cuda:0")
     x = np.random.default_rng(3100 + N % 97).standard_normal((24, K)).astype(np.float32)
     X = dev(x)
@@ -147,10 +148,12 @@ def test_shared_activation_paths_bit_identical(N, K):
 @pytest.mark.parametrize("N,K", [(4100, 4096), (6150, 4096), (70001, 2048), (1000, 12288),
                                  (17, 4096)])
 def test_staged_row_block_ragged_rows(N, K):
-    """Up to 8 rows (and below 6144 matrix rows at any R) the row-block kernel
-    stages row runs through LDS; ragged N exercises its clamped rows.
-    Matches the oracle on sampled rows, and rows equal 1-row calls bit for
-    bit up to 24 rows (where other kernels take over)."""
+    """Up to 16 rows (below 6144 matrix rows, and for wide matrices, at any
+    R) the row-block kernel stages row runs through LDS; wide matrices take
+    32-row tiles up to 8 rows, 128-row tiles up to 16 and 64-row tiles with
+    two column tiles above.  Ragged N exercises the clamped rows.  Matches
+    the oracle on sampled rows, and rows equal 1-row calls bit for bit up to
+    24 rows."""
     W = torch_bf16_weights((N, K), 3300 + N % 101, "cuda:0")
     x = np.random.default_rng(3310 + N % 101).standard_normal((24, K)).astype(np.float32)
     X = dev(x)

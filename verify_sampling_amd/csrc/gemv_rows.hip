@@ -661,19 +661,34 @@ int splits_for(int N, int K) {
   return s < 1 ? 1 : s;  // <= MAX_SPLITS
 }
 
-// Which kernel runs for (N, K, R).  Chosen by sweeps of the whole verify
-// pass on MI355X: up to 16 rows (one activation column tile) the row-block
-// kernel is fastest; above that its activation traffic dominates and the
-// shared-activation kernels take over (all-K for very wide matrices,
-// partitions across workgroups for matrices of >= 48 MB); small matrices
-// stay on the row-block kernel, whose launch is cheapest.
+// Whether the staged row-block kernel can take (N, K): whole k-blocks, at
+// least two stages per partition, and an even partition count above 8.
+bool staged_fits(int N, int K) {
+  const int nkb = (K + KBLK - 1) / KBLK;
+  const int splits = splits_for(N, K);
+  return K % KBLK == 0 && nkb / splits >= 2 && (splits <= 8 || splits % 2 == 0);
+}
+
+// Which kernel runs for (N, K, R).  Chosen by per-shape sweeps on MI355X.
+// The row-block kernels re-read the activations once per row tile, so their
+// time grows with R; the shared-activation kernels share each activation
+// tile among a workgroup's waves and stay nearly flat in R, from a higher
+// base.  Up to 8 rows the row-block kernel wins everywhere.  Long rows of
+// >= 48 MB (down) cross over at 9 rows: partitions across workgroups.  The
+// very wide LM head stays on the staged row-block kernel at every R, with
+// taller row tiles as R grows (fewer activation re-reads per weight byte);
+// all-K sharing is its fallback above 16 rows where that kernel cannot run.
+// Other matrices of >= 48 MB take partitions across workgroups above 16
+// rows; the rest stay on the row-block kernel, whose launch is cheapest.
 enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK };
 
 Kind kind_for(int N, int K, int R) {
-  if (R <= 16) return Kind::kRowBlock;
-  if (N >= 65536) return Kind::kSharedAllK;
-  if (2.0 * N * K >= 48e6) return Kind::kSharedSplitK;
-  return Kind::kRowBlock;
+  if (R <= 8) return Kind::kRowBlock;
+  if (N >= 65536) return R > 16 && !staged_fits(N, K) ? Kind::kSharedAllK : Kind::kRowBlock;
+  const bool big = 2.0 * N * K >= 48e6;
+  const bool long_rows = (K + KBLK - 1) / KBLK >= 256;
+  if (R <= 16) return big && long_rows ? Kind::kSharedSplitK : Kind::kRowBlock;
+  return big ? Kind::kSharedSplitK : Kind::kRowBlock;
 }
 
 int64_t parts_ld(int N) { return (static_cast<int64_t>(N) + 3) & ~int64_t{3}; }
@@ -724,8 +739,13 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
       kernel<<<grid, dim3(64 * P), 0, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, parts, ldp, nkb,
                                                 splits);
     };
-    if (N >= 16384) launch(gemv_shared_kernel<1, 2, 2, 8, true>, 1, 8);  // R > 16
-    else launch(gemv_shared_kernel<1, 2, 2, 4, true>, 1, 4);
+    if (R > 16) {  // two activation column tiles
+      if (N >= 16384) launch(gemv_shared_kernel<1, 2, 2, 8, true>, 1, 8);
+      else launch(gemv_shared_kernel<1, 2, 2, 4, true>, 1, 4);
+    } else {
+      if (N >= 16384) launch(gemv_shared_kernel<1, 2, 1, 8, true>, 1, 8);
+      else launch(gemv_shared_kernel<1, 2, 1, 4, true>, 1, 4);
+    }
     int st = vs::check_launch();
     if (st != VS_OK) return st;
     const int quads = static_cast<int>((N + 3) / 4);
@@ -736,11 +756,11 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
 
   const dim3 block(64 * splits);
   // Staged row-block kernel where its conditions hold: every row-block
-  // launch up to 16 rows, and the matrices below 6144 rows (o) at any R.
+  // launch up to 16 rows, the matrices below 6144 rows (o) and the LM head
+  // at any R.
   constexpr int STAGE_U = 2;
-  const bool staged_ok = K % KBLK == 0 && nkb / splits >= STAGE_U &&
-                         (splits <= 8 || splits % 2 == 0);
-  if (staged_ok && (R <= 16 || N < 6144)) {
+  static_assert(STAGE_U == 2, "staged_fits assumes two k-blocks per stage");
+  if (staged_fits(N, K) && (R <= 16 || N < 6144 || N >= 65536)) {
     const int ppw = splits > 8 ? 2 : 1;  // partitions per wave: at most 8 waves
     const int waves = splits / ppw;
     auto launch_staged = [&](auto kernel, int T, int CT) {
@@ -758,6 +778,10 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
         if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 2>, 1, 2);
         else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 1>, 1, 2);
       }
+    } else if (N >= 65536 && R > 16) {  // the LM head: 64-row tiles, two column tiles
+      launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 1>, 4, 2);
+    } else if (N >= 65536 && R > 8) {  // 128-row tiles
+      launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1>, 8, 1);
     } else {  // R <= 16
       if (ppw == 2) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2>, 2, 1);
       else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1>, 2, 1);
