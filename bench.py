@@ -565,6 +565,9 @@ def main():
         "ms_per_pass_vs_R": {str(r): round(v, 4) for r, v in sweep.items()},
         "gbs_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9, 1)
                      for r, v in sweep.items()},
+        "frac_of_hbm_peak_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                  for r, v in sweep.items()},
+        "verify_tokens_per_s_vs_R": {str(r): round(r / (v * 1e-3), 1) for r, v in sweep.items()},
         "knee_R": knee,
         "depth_chooser": depth_report(vs, sweep) if sweep else None,
         "prompt_lookup_drafter": lookup_report(vs, synth),
