@@ -60,9 +60,11 @@ __global__ void __launch_bounds__(64 * WINDOWS_PER_BLOCK)
 accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ drafts,
               const int32_t* __restrict__ parent, const float* __restrict__ u,
               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n) {
+  __shared__ double scan[WINDOWS_PER_BLOCK][64];  // each wave's running sums for seq_draw
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * WINDOWS_PER_BLOCK + (threadIdx.x >> 6);
   if (b >= B) return;  // whole wave; no block-wide barriers
+  double* run = scan[threadIdx.x >> 6];
 
   const int32_t* dr = drafts + static_cast<int64_t>(b) * k;
   int32_t my_tok = -1;  // lane j holds emitted token j
@@ -121,7 +123,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const int pl = clamp_len(d.p_len[prow], d.p_ld);
       const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
       const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
-      const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * i + 1]));  // -1 if p is empty
+      const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * i + 1], run));  // -1 if p is empty
       if (lane == n) my_tok = x;
       ++n;
       if (i == k || x < 0 || x != dr[i]) break;  // an empty row's -1 always ends the window
@@ -141,7 +143,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const int pl = clamp_len(d.p_len[prow], d.p_ld);
       const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
       const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
-      const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * row + 1]));
+      const int32_t x = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * row + 1], run));
       if (lane == n) my_tok = x;
       ++n;
       if (x < 0) break;
@@ -167,7 +169,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       // (p - delta(x))+ is p without x
       const double r = (lane < pl && pid != x) ? pp : 0.0;
       const double z = vs::seq_sum(r, pl);
-      const int j = z > 0.0 ? vs::seq_draw(r, pl, ub[2 * i + 1]) : vs::seq_draw(pp, pl, ub[2 * i + 1]);
+      const int j = z > 0.0 ? vs::seq_draw(r, pl, ub[2 * i + 1], run) : vs::seq_draw(pp, pl, ub[2 * i + 1], run);
       const int32_t t = vs::bcast(pid, j);
       if (lane == n) my_tok = t;
       ++n;
@@ -178,7 +180,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const int pl = clamp_len(d.p_len[prow], d.p_ld);
       const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
       const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
-      const int32_t t = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * k + 1]));
+      const int32_t t = vs::bcast(pid, vs::seq_draw(pp, pl, ub[2 * k + 1], run));
       if (lane == n) my_tok = t;
       ++n;
     }
@@ -212,7 +214,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const double diff = pp - qt;
       const double r = (lane < pl && diff > 0.0) ? diff : 0.0;
       const double z = vs::seq_sum(r, pl);
-      const int j = z > 0.0 ? vs::seq_draw(r, pl, ub[2 * i + 1]) : vs::seq_draw(pp, pl, ub[2 * i + 1]);
+      const int j = z > 0.0 ? vs::seq_draw(r, pl, ub[2 * i + 1], run) : vs::seq_draw(pp, pl, ub[2 * i + 1], run);
       const int32_t t = vs::bcast(pid, j);
       if (lane == n) my_tok = t;
       ++n;
@@ -223,7 +225,7 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
       const int pl = clamp_len(d.p_len[prow], d.p_ld);
       const int32_t pid = lane < pl ? d.p_ids[prow * d.p_ld + lane] : -1;
       const double pp = lane < pl ? static_cast<double>(d.p_probs[prow * d.p_ld + lane]) : 0.0;
-      const int j = vs::seq_draw(pp, pl, ub[2 * k + 1]);
+      const int j = vs::seq_draw(pp, pl, ub[2 * k + 1], run);
       const int32_t t = vs::bcast(pid, j);
       if (lane == n) my_tok = t;
       ++n;

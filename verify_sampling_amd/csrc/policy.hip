@@ -35,9 +35,13 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
               int32_t* __restrict__ dist_ids, float* __restrict__ dist_probs,
               int32_t* __restrict__ dist_len, int64_t ld_dist, const float* __restrict__ u,
               int32_t* __restrict__ drawn) {
+  // running sums of the sequential scans, one slot per candidate: lane 0
+  // records each partial sum, every lane reads its own after the loop
+  __shared__ double scan[ROWS_PER_BLOCK][64];
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave; the kernel has no block-wide barriers
+  double* run = scan[threadIdx.x >> 6];
 
   const float* vrow = vals + static_cast<int64_t>(row) * ld;
   const int32_t* irow = ids + static_cast<int64_t>(row) * ld;
@@ -87,11 +91,13 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
         const double w1 = keep1 ? e : 0.0;
         // only the first nk lanes can carry weight
         const int nk = n_real < k_eff ? n_real : k_eff;
-        double acc = 0.0, excl = 0.0;
+        double acc = 0.0;
         for (int j = 0; j < nk; ++j) {
-          if (lane == j) excl = acc;
+          if (lane == 0) run[j] = acc;
           acc += vs::bcast(w1, j);
         }
+        vs::wave_lds_sync();
+        const double excl = lane < nk ? run[lane] : 0.0;
         const double incl = excl + w1;  // the scan's value after this lane, same rounding
         const double tp = static_cast<double>(top_p);
         bool keep2 = keep1;
@@ -135,11 +141,14 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
     if (L > 0) {
       // kept lanes lie below the last kept lane + 1
       const int nl = 64 - __clzll(static_cast<long long>(kmask));
-      double acc = 0.0, mine = 0.0;
+      vs::wave_lds_sync();  // the first scan's slots have been read
+      double acc = 0.0;
       for (int j = 0; j < nl; ++j) {
         acc += vs::bcast(w, j);
-        if (lane == j) mine = acc;
+        if (lane == 0) run[j] = acc;
       }
+      vs::wave_lds_sync();
+      const double mine = lane < nl ? run[lane] : 0.0;
       const double target = static_cast<double>(u[row]) * acc;
       const uint64_t hit = __ballot(keep && target < mine);
       int src;

@@ -47,13 +47,6 @@ struct MergeShared {
   uint32_t cont[MAX_CHUNKS];  // chunk lists: those to read on, the second round's
 };
 
-// Makes this wave's LDS writes visible to its other lanes before they read.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // Number of set bits of m in the lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t add = 0) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -121,7 +114,7 @@ __device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int
                 : 0ull;
     sh.key[s] = k[r];  // empty slots hold 0, which is below every key
   }
-  wave_lds_sync();
+  vs::wave_lds_sync();
   int rank[E];
 #pragma unroll
   for (int r = 0; r < E; ++r) rank[r] = 0;
@@ -348,7 +341,7 @@ topk_chunk_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
 
   // 4: ranks and output
   if (count > CAND) count = CAND;  // not reached: the exact threshold leaves K
-  wave_lds_sync();
+  vs::wave_lds_sync();
   const float* xc = xrow + base;
   if (count <= 64)
     rank_and_write<1>(sh, count, K, base, chunks, row, chunk, xc, exact, ws, out_vals, out_idx, ld_out);
@@ -442,13 +435,13 @@ __device__ __forceinline__ void merge_rank_write(MergeShared& sh, int c, int K, 
     const int s = lane + 64 * r;
     k[r] = s < c ? sh.key[s] : 0ull;
   }
-  wave_lds_sync();  // every lane has its key before the tail is cleared
+  vs::wave_lds_sync();  // every lane has its key before the tail is cleared
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const int s = lane + 64 * r;
     if (s >= c) sh.key[s] = 0ull;  // below every key
   }
-  wave_lds_sync();
+  vs::wave_lds_sync();
   int rank[E];
 #pragma unroll
   for (int r = 0; r < E; ++r) rank[r] = 0;
@@ -546,7 +539,7 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
       }
     }
   }
-  wave_lds_sync();
+  vs::wave_lds_sync();
   if (n_cont > 0 && count <= CAND) {
     // entries j2 .. K-1 of those chunks, P (a power of two >= K - j2) lanes per chunk
     const int tail = K - j2;
@@ -574,7 +567,7 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
     // K read entries are >= v2, so at most K / jb chunks have all jb read
     // entries >= v2, and only those are read on.  That bounds the
     // survivors by K * K / jb <= CAND.
-    wave_lds_sync();  // the first round's survivors are dropped
+    vs::wave_lds_sync();  // the first round's survivors are dropped
     int nrel = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -584,7 +577,7 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
       if (rel) sh.cont[lanes_below(mm, static_cast<uint32_t>(nrel))] = static_cast<uint32_t>(t >> lg_jp);
       nrel += __popcll(mm);
     }
-    wave_lds_sync();
+    vs::wave_lds_sync();
     int lg_jb = 31 - __builtin_clz(static_cast<unsigned>((64 * MERGE_LOADS) / (nrel > 0 ? nrel : 1)));
     const int lg_k = K <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(K - 1));
     lg_jb = lg_jb < lg_k ? lg_jb : lg_k;
@@ -626,7 +619,7 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
         }
       }
     }
-    wave_lds_sync();
+    vs::wave_lds_sync();
     // entries jb .. K-1 of at most K / jb <= 4 chunks, 64 lanes per chunk
     for (int u0 = 0; u0 < nlong; u0 += 4) {
       uint64_t f[4];
@@ -642,7 +635,7 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
   }
 
   if (count > CAND) count = CAND;  // not reached: the rounds above bound the survivors
-  wave_lds_sync();
+  vs::wave_lds_sync();
   if (count > 128) {
     // ranking costs grow with the square of the survivors: cut them to
     // exactly K first, at the exact K-th largest of them
@@ -653,11 +646,11 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
       r4[r] = t < count ? sh.key[t] : 0ull;
     }
     const uint64_t v3 = wave_kth_largest<4>(r4, K);
-    wave_lds_sync();  // every lane has its keys before the list is rewritten
+    vs::wave_lds_sync();  // every lane has its keys before the list is rewritten
     count = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) compact_key(sh, count, r4[r] != 0ull && r4[r] >= v3, r4[r]);
-    wave_lds_sync();
+    vs::wave_lds_sync();
   }
   const float* xrow = X + static_cast<int64_t>(row) * ldx;
   float* ovals = out_vals + static_cast<int64_t>(row) * ld_out;

@@ -26,16 +26,27 @@ __device__ __forceinline__ double seq_sum(double w, int n) {
   return s;
 }
 
+// Makes this wave's LDS writes visible to its other lanes before they read.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // Inverse-CDF draw over lanes [0, n): the first lane j with u * C_n < C_j,
 // C_j the sequential fp64 sum of w over lanes 0..j.  If rounding leaves no
-// such lane, the last lane with positive weight (else 0).
-__device__ __forceinline__ int seq_draw(double w, int n, float u) {
+// such lane, the last lane with positive weight (else 0).  run: this wave's
+// 64 LDS slots, where lane 0 records each C_j for lane j to read back.
+__device__ __forceinline__ int seq_draw(double w, int n, float u, double* run) {
   const int lane = threadIdx.x & 63;
-  double acc = 0.0, mine = 0.0;
+  wave_lds_sync();  // a previous use of the slots has been read
+  double acc = 0.0;
   for (int j = 0; j < n; ++j) {
     acc += bcast(w, j);
-    if (lane == j) mine = acc;
+    if (lane == 0) run[j] = acc;
   }
+  wave_lds_sync();
+  const double mine = lane < n ? run[lane] : 0.0;
   const double target = static_cast<double>(u) * acc;
   const uint64_t hit = __ballot(lane < n && target < mine);
   if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
