@@ -45,13 +45,15 @@ struct Dists {
 
 __device__ __forceinline__ int clamp_len(int n, int ld) { return n < 0 ? 0 : (n > ld ? ld : n); }
 
-// Total probability of token x over the lanes [0, n) of a sparse row.
+// Total probability of token x over the lanes [0, n) of a sparse row: the
+// entries holding x, summed in lane order (one entry in a well-formed row).
 __device__ __forceinline__ double prob_of(int32_t id, double p, int n, int32_t x) {
+  const int lane = threadIdx.x & 63;
+  uint64_t m = __ballot(lane < n && id == x);
   double s = 0.0;
-  for (int j = 0; j < n; ++j) {
-    const int32_t t = vs::bcast(id, j);
-    const double pj = vs::bcast(p, j);
-    if (t == x) s += pj;
+  while (m) {
+    s += vs::bcast(p, __ffsll(static_cast<long long>(m)) - 1);
+    m &= m - 1;
   }
   return s;
 }

@@ -14,8 +14,9 @@
 // filters compare ratios of weights and are evaluated on the unnormalised
 // weights; the kept weights are normalised once and rounded to fp32.
 //
-// One sequential prefix scan over the min-p survivors' weights (zero for
-// the others; adding +0.0 to a non-negative sum is exact) gives every sum
+// One sequential prefix scan over the min-p survivors' weights (the other
+// candidates would add +0.0 to a non-negative sum, which changes nothing, so
+// they are skipped) gives every sum
 // the policy needs: its total is the top-p reference sum, the exclusive
 // prefix at a candidate is the mass kept before it (the scan is
 // non-decreasing, so the top-p survivors are the min-p survivors up to the
@@ -89,20 +90,21 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
         // weight-0 candidates carry no mass; min-p relative to the first
         const bool keep1 = e > 0.0 && e >= static_cast<double>(min_p) * e0;
         const double w1 = keep1 ? e : 0.0;
-        // only the first nk lanes can carry weight
-        const int nk = n_real < k_eff ? n_real : k_eff;
+        // the scan runs over the min-p survivors only: lanes of weight 0 add
+        // nothing and their prefixes are never used
+        const uint64_t k1 = __ballot(keep1);
         double acc = 0.0;
-        for (int j = 0; j < nk; ++j) {
+        for (uint64_t m = k1; m; m &= m - 1) {
+          const int j = __ffsll(static_cast<long long>(m)) - 1;
           if (lane == 0) run[j] = acc;
           acc += vs::bcast(w1, j);
         }
         vs::wave_lds_sync();
-        const double excl = lane < nk ? run[lane] : 0.0;
+        const double excl = keep1 ? run[lane] : 0.0;
         const double incl = excl + w1;  // the scan's value after this lane, same rounding
         const double tp = static_cast<double>(top_p);
         bool keep2 = keep1;
         if (tp < 1.0) {
-          const uint64_t k1 = __ballot(keep1);
           const int first = k1 ? __ffsll(static_cast<long long>(k1)) - 1 : -1;
           keep2 = keep1 && (excl < tp * acc || lane == first);
         }
@@ -141,14 +143,18 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
     if (L > 0) {
       // kept lanes lie below the last kept lane + 1
       const int nl = 64 - __clzll(static_cast<long long>(kmask));
+      // lanes of weight 0 are skipped: they add nothing and are never the
+      // first lane to pass
+      const bool live = lane < nl && w != 0.0;
       vs::wave_lds_sync();  // the first scan's slots have been read
       double acc = 0.0;
-      for (int j = 0; j < nl; ++j) {
+      for (uint64_t m = __ballot(live); m; m &= m - 1) {
+        const int j = __ffsll(static_cast<long long>(m)) - 1;
         acc += vs::bcast(w, j);
         if (lane == 0) run[j] = acc;
       }
       vs::wave_lds_sync();
-      const double mine = lane < nl ? run[lane] : 0.0;
+      const double mine = live ? run[lane] : 0.0;
       const double target = static_cast<double>(u[row]) * acc;
       const uint64_t hit = __ballot(keep && target < mine);
       int src;

@@ -19,10 +19,18 @@ __device__ __forceinline__ double bcast(double v, int src) {
 }
 __device__ __forceinline__ int bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
-// Sequential sum of w over lanes [0, n), lane order, fp64.
+// Sequential sum of w over lanes [0, n), lane order, fp64.  Lanes holding
+// zero are skipped: the sum starts at +0 and adding a zero of either sign to
+// it never changes it (it cannot become -0), so the result is the same as
+// adding every lane.
 __device__ __forceinline__ double seq_sum(double w, int n) {
+  const int lane = threadIdx.x & 63;
+  uint64_t m = __ballot(lane < n && w != 0.0);
   double s = 0.0;
-  for (int j = 0; j < n; ++j) s += bcast(w, j);
+  while (m) {
+    s += bcast(w, __ffsll(static_cast<long long>(m)) - 1);
+    m &= m - 1;
+  }
   return s;
 }
 
@@ -37,16 +45,22 @@ __device__ __forceinline__ void wave_lds_sync() {
 // C_j the sequential fp64 sum of w over lanes 0..j.  If rounding leaves no
 // such lane, the last lane with positive weight (else 0).  run: this wave's
 // 64 LDS slots, where lane 0 records each C_j for lane j to read back.
+// Zero lanes are skipped as in seq_sum; one is never the first lane to pass
+// (C_j equals the previous lane's sum, which then passes first, or 0).
 __device__ __forceinline__ int seq_draw(double w, int n, float u, double* run) {
   const int lane = threadIdx.x & 63;
+  const bool live = lane < n && w != 0.0;
+  uint64_t m = __ballot(live);
   wave_lds_sync();  // a previous use of the slots has been read
   double acc = 0.0;
-  for (int j = 0; j < n; ++j) {
+  while (m) {
+    const int j = __ffsll(static_cast<long long>(m)) - 1;
     acc += bcast(w, j);
     if (lane == 0) run[j] = acc;
+    m &= m - 1;
   }
   wave_lds_sync();
-  const double mine = lane < n ? run[lane] : 0.0;
+  const double mine = live ? run[lane] : 0.0;
   const double target = static_cast<double>(u) * acc;
   const uint64_t hit = __ballot(lane < n && target < mine);
   if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
