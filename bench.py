@@ -552,8 +552,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("verify_gemv_rows: gemv_rows_kernel (row-block)" if R <= 8 else
-                       "verify_gemv_rows: gemv_shared_kernel (shared activations) and gemv_rows_kernel"),
+            "kernel": ("verify_gemv_rows: gemv_rows_staged_kernel (staged row-block)" if R <= 8 else
+                       "verify_gemv_rows: gemv_rows_staged_kernel and gemv_shared_kernel (split-K) with reduce_partials_kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
