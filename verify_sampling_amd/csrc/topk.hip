@@ -68,6 +68,26 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // condition register.
 __device__ __forceinline__ void pin3(uint64_t a, uint64_t b, uint64_t c) { asm volatile("" ::"s"(a), "s"(b), "s"(c)); }
 
+// The bits every valid lane's value shares, as (prefix, top): prefix holds
+// the common bits above the highest bit in which two valid values differ,
+// zeros from that bit down; top is that bit (-1 if all agree, i.e. prefix
+// is the common value, or if no lane is valid).  a and o are the lane's own
+// AND and OR over its valid values (~0 and 0 if none).
+__device__ __forceinline__ uint32_t common_prefix(uint32_t a, uint32_t o, int& top) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), off, 64));
+    o |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(o), off, 64));
+  }
+  const uint32_t d = a ^ o;
+  if (o == 0u && a == ~0u) {  // no valid lane
+    top = 31;
+    return 0u;
+  }
+  top = d ? 31 - __builtin_clz(d) : -1;
+  return d ? (o & ~((2u << top) - 1u)) : o;
+}
+
 // The float whose value key is v (v >= 1 and the key of a number).
 __device__ __forceinline__ uint32_t key_bits(uint32_t v) { return (v & 0x80000000u) ? (v ^ 0x80000000u) : ~v; }
 
@@ -365,8 +385,20 @@ __device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int
     hi[i] = static_cast<uint32_t>(k[i] >> 32);
     lo[i] = static_cast<uint32_t>(k[i]);
   }
-  uint32_t vh = 0;
-  for (int bit = 30; bit >= 0; bit -= 2) {
+  // the search starts below the bits all real keys share: the K-th largest
+  // shares them too (a candidate that sets a shared bit is either unchanged
+  // or above every key, so the choice at each step is the same)
+  uint32_t la = ~0u, lo_or = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (k[i] != 0ull) {
+      la &= hi[i];
+      lo_or |= hi[i];
+    }
+  }
+  int top;
+  uint32_t vh = common_prefix(la, lo_or, top);
+  for (int bit = (top | 1) - 1; bit >= 0; bit -= 2) {
     const uint32_t c1 = vh | (1u << bit), c2 = vh | (2u << bit), c3 = vh | (3u << bit);
     int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
@@ -396,8 +428,17 @@ __device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int
   if (need > ties) return 0ull;  // fewer than K keys
   const uint64_t base = static_cast<uint64_t>(vh) << 32;
   if (need == ties) return base;
-  uint32_t vl = 0;
-  for (int bit = 30; bit >= 0; bit -= 2) {
+  la = ~0u;
+  lo_or = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (lo[i] != 0u) {
+      la &= lo[i];
+      lo_or |= lo[i];
+    }
+  }
+  uint32_t vl = common_prefix(la, lo_or, top);
+  for (int bit = (top | 1) - 1; bit >= 0; bit -= 2) {
     const uint32_t c1 = vl | (1u << bit), c2 = vl | (2u << bit), c3 = vl | (3u << bit);
     int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
