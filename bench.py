@@ -458,8 +458,9 @@ def cpu_baseline(synth, R, budget_s=12.0):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the verify step would shard)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the verify step would shard the projections by output rows and the "
+              "top-K by vocabulary slices)", file=sys.stderr)
         sys.exit(2)
     import torch
 

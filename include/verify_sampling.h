@@ -44,7 +44,7 @@ enum vs_status {
   VS_ERR_NULL = -1,        /* a required pointer is NULL                     */
   VS_ERR_SHAPE = -2,       /* a size or leading dimension is out of range    */
   VS_ERR_PARAM = -3,       /* a scalar parameter is out of range             */
-  VS_ERR_UNSUPPORTED = -4, /* a valid combination this build does not handle */
+  VS_ERR_UNSUPPORTED = -4, /* a valid combination the library does not handle */
   VS_ERR_WORKSPACE = -5,   /* workspace missing or too small                 */
   VS_ERR_ALIGN = -6,       /* a pointer or leading dimension is misaligned   */
   VS_ERR_HIP = -7          /* the HIP runtime reported an error at launch    */
