@@ -294,7 +294,7 @@ struct RunStage {
   float4 x[U][CT][2];
 };
 
-template <int T, int U, int CT, int LB, int PPW>
+template <int T, int U, int CT, int LB, int PPW, bool XL>
 __global__ void __launch_bounds__(LB)
 gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
                         const float* __restrict__ X, int64_t ldx, int R,
@@ -311,7 +311,12 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   const int g = lane >> 4;
   const int col = lane & 15;
   const int n0 = blockIdx.x * TILE * T;
-  uint8_t* stg = reinterpret_cast<uint8_t*>(red) + static_cast<size_t>(wave) * (T * TILE * RS);
+  // XL: activations go through LDS as well (XB bytes per wave after the
+  // weights), loaded as whole rows of a k-block
+  constexpr int XS = KBLK * 4 + 16;                 // LDS stride of an activation row
+  constexpr int XB = XL ? U * CT * TILE * XS : 0;   // activation stage bytes per wave
+  uint8_t* stg = reinterpret_cast<uint8_t*>(red) + static_cast<size_t>(wave) * (T * TILE * RS + XB);
+  uint8_t* xstg = stg + T * TILE * RS;
 
   const uint8_t* wsrc[NI];  // this lane's rows, at its 16-byte column of the stage
 #pragma unroll
@@ -320,14 +325,21 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
     if (wr >= N) wr = N - 1;  // ragged tile: load a valid row, discard its results
     wsrc[i] = reinterpret_cast<const uint8_t*>(W + static_cast<int64_t>(wr) * ldw) + (lane % LPR) * 16;
   }
-  // activation row of this lane's column; columns >= R read row R - 1, and
-  // their (independent) MFMA outputs are never stored
-  const float* xrow[CT];
+  // Activation rows; rows >= R read row R - 1, and their (independent)
+  // MFMA outputs are never stored.  Direct: the lane's own column, its two
+  // 16-byte pieces at 8g and 8g + 4, loaded in the operand layout (16 rows
+  // per instruction, half of each row's 128 bytes).  XL: 8 lanes per row
+  // cover the row's whole 128 bytes, 8 rows per instruction, and the
+  // operand layout is read back from LDS, which moves fewer partly used
+  // cache lines per activation byte once R is large.
+  const float* xrow[CT][2];
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    const int r = c * 16 + col;
-    xrow[c] = X + static_cast<int64_t>(r < R ? r : R - 1) * ldx + g * 8;
-  }
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = XL ? c * 16 + h * 8 + (lane >> 3) : c * 16 + col;
+      xrow[c][h] = X + static_cast<int64_t>(r < R ? r : R - 1) * ldx + (XL ? (lane & 7) * 4 : g * 8 + h * 4);
+    }
   static_assert(PPW == 1 || PPW == 2, "partitions per wave");
   const int p0 = wave * PPW;
   const int kb0 = static_cast<int>((static_cast<int64_t>(p0) * nkb) / splits);
@@ -352,8 +364,8 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
       const int64_t off = static_cast<int64_t>(kb + u < kb1 ? kb + u : kb1 - 1) * KBLK;
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        st.x[u][c][0] = *reinterpret_cast<const float4*>(xrow[c] + off);
-        st.x[u][c][1] = *reinterpret_cast<const float4*>(xrow[c] + off + 4);
+        st.x[u][c][0] = *reinterpret_cast<const float4*>(xrow[c][0] + off);
+        st.x[u][c][1] = *reinterpret_cast<const float4*>(xrow[c][1] + off);
       }
     }
     const int64_t woff = static_cast<int64_t>(first_block(kb)) * (KBLK * 2);
@@ -365,6 +377,16 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<u32x4*>(stg + (i * RPI + lane / LPR) * RS + (lane % LPR) * 16) = st.w[i];
+    if constexpr (XL) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<float4*>(xstg + ((u * CT + c) * TILE + h * 8 + (lane >> 3)) * XS + (lane & 7) * 16) =
+                st.x[u][c][h];
+    }
     wave_lds_sync();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -377,8 +399,13 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
       auto accumulate = [&](f32x4 (&ac)[T][CT]) {
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          const float xv[8] = {st.x[u][c][0].x, st.x[u][c][0].y, st.x[u][c][0].z, st.x[u][c][0].w,
-                               st.x[u][c][1].x, st.x[u][c][1].y, st.x[u][c][1].z, st.x[u][c][1].w};
+          float4 x0 = st.x[u][c][0], x1 = st.x[u][c][1];
+          if constexpr (XL) {
+            const uint8_t* xa = xstg + ((u * CT + c) * TILE + col) * XS + g * 32;
+            x0 = *reinterpret_cast<const float4*>(xa);
+            x1 = *reinterpret_cast<const float4*>(xa + 16);
+          }
+          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           u32x4 hi, mid, lo;
           split3(xv, hi, mid, lo);
 #pragma unroll
@@ -763,28 +790,44 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   if (staged_fits(N, K) && (R <= 16 || N < 6144 || N >= 65536)) {
     const int ppw = splits > 8 ? 2 : 1;  // partitions per wave: at most 8 waves
     const int waves = splits / ppw;
-    auto launch_staged = [&](auto kernel, int T, int CT) {
+    auto launch_staged = [&](auto kernel, int T, int CT, bool xl) {
       const dim3 grid((N + TILE * T - 1) / (TILE * T));
       size_t shm = static_cast<size_t>(splits) * T * CT * 256 * sizeof(float);
-      const size_t stage = static_cast<size_t>(waves) * T * TILE * (STAGE_U * KBLK * 2 + 16);
+      const size_t stage = static_cast<size_t>(waves) *
+                           (T * TILE * (STAGE_U * KBLK * 2 + 16) + (xl ? STAGE_U * CT * TILE * (KBLK * 4 + 16) : 0));
       if (stage > shm) shm = stage;
       kernel<<<grid, dim3(64 * waves), shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
     };
-    if (N < 6144) {
+    // Activations through LDS (XL) where a sweep on MI355X found it faster:
+    // once the activation bytes per weight byte, R / (8 T), are large, and
+    // for the q|k|v-sized matrices at every R.
+    if (N < 6144) {  // 16-row tiles
+      const bool xl = R >= 6;
       if (R <= 16) {
-        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 2>, 1, 1);
-        else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 1>, 1, 1);
+        if (ppw == 2) {
+          if (xl) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 2, true>, 1, 1, true);
+          else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 2, false>, 1, 1, false);
+        } else {
+          if (xl) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 1, true>, 1, 1, true);
+          else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 1, false>, 1, 1, false);
+        }
       } else {
-        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 2>, 1, 2);
-        else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 1>, 1, 2);
+        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 2, true>, 1, 2, true);
+        else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 1, true>, 1, 2, true);
       }
     } else if (N >= 65536 && R > 16) {  // the LM head: 64-row tiles, two column tiles
-      launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 1>, 4, 2);
+      launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 1, true>, 4, 2, true);
     } else if (N >= 65536 && R > 8) {  // 128-row tiles
-      launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1>, 8, 1);
-    } else {  // R <= 16
-      if (ppw == 2) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2>, 2, 1);
-      else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1>, 2, 1);
+      launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1, false>, 8, 1, false);
+    } else {  // 32-row tiles, R <= 16
+      const bool xl = N < 16384 || (N >= 65536 ? R >= 8 : R >= 10);
+      if (ppw == 2) {
+        if (xl) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2, true>, 2, 1, true);
+        else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2, false>, 2, 1, false);
+      } else {
+        if (xl) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1, true>, 2, 1, true);
+        else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1, false>, 2, 1, false);
+      }
     }
     return vs::check_launch();
   }
