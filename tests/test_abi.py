@@ -54,12 +54,15 @@ def test_gemv_rejects_before_launch():
     assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 4) == 0
     assert lib.verify_gemv_rows_workspace_bytes(151936, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 4) == 0
-    # long rows of >= 48 MB take partitions across workgroups from 9 rows,
-    # other matrices of >= 48 MB above 16 rows
+    # long rows of >= 48 MB take partitions across workgroups from 9 rows;
+    # other matrices of >= 48 MB only where the staged kernel cannot run
+    # (here K % 32 != 0), above 16 rows
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 8) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 16) == 16 * 16 * 4096 * 4
-    assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 16) == 0
-    assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 17) == 8 * 17 * 6144 * 4
+    assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 24) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(24576, 4096, 24) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(6152, 4104, 16) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(6152, 4104, 17) == 8 * 17 * 6152 * 4
     # 4096 x 12288 at 24 rows: 16 K partitions of 24 x 4096 fp32 partial sums
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 24) == 16 * 24 * 4096 * 4
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 25) == 0

@@ -700,22 +700,21 @@ bool staged_fits(int N, int K) {
 // The row-block kernels re-read the activations once per row tile, so their
 // time grows with R; the shared-activation kernels share each activation
 // tile among a workgroup's waves and stay nearly flat in R, from a higher
-// base.  Up to 8 rows the row-block kernel wins everywhere.  Long rows of
-// >= 48 MB (down) cross over at 9 rows: partitions across workgroups.  The
-// very wide LM head stays on the staged row-block kernel at every R, with
-// taller row tiles as R grows (fewer activation re-reads per weight byte);
-// all-K sharing is its fallback above 16 rows where that kernel cannot run.
-// Other matrices of >= 48 MB take partitions across workgroups above 16
-// rows; the rest stay on the row-block kernel, whose launch is cheapest.
+// base (and the split-K form adds a dependent partition-sum launch).  The
+// staged row-block kernel, with taller tiles and activations through LDS
+// as R grows, wins at every R except on long rows of >= 48 MB (down),
+// which cross over to partitions across workgroups at 9 rows.  Where the
+// staged kernel cannot run, matrices of >= 48 MB take the shared kernels
+// above 16 rows (all-K for very wide ones).
 enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK };
 
 Kind kind_for(int N, int K, int R) {
   if (R <= 8) return Kind::kRowBlock;
-  if (N >= 65536) return R > 16 && !staged_fits(N, K) ? Kind::kSharedAllK : Kind::kRowBlock;
   const bool big = 2.0 * N * K >= 48e6;
   const bool long_rows = (K + KBLK - 1) / KBLK >= 256;
-  if (R <= 16) return big && long_rows ? Kind::kSharedSplitK : Kind::kRowBlock;
-  return big ? Kind::kSharedSplitK : Kind::kRowBlock;
+  if (N < 65536 && big && long_rows) return Kind::kSharedSplitK;
+  if (staged_fits(N, K) || R <= 16 || !big) return Kind::kRowBlock;
+  return N >= 65536 ? Kind::kSharedAllK : Kind::kSharedSplitK;
 }
 
 int64_t parts_ld(int N) { return (static_cast<int64_t>(N) + 3) & ~int64_t{3}; }
@@ -782,12 +781,10 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   }
 
   const dim3 block(64 * splits);
-  // Staged row-block kernel where its conditions hold: every row-block
-  // launch up to 16 rows, the matrices below 6144 rows (o) and the LM head
-  // at any R.
+  // Staged row-block kernel wherever its conditions hold.
   constexpr int STAGE_U = 2;
   static_assert(STAGE_U == 2, "staged_fits assumes two k-blocks per stage");
-  if (staged_fits(N, K) && (R <= 16 || N < 6144 || N >= 65536)) {
+  if (staged_fits(N, K)) {
     const int ppw = splits > 8 ? 2 : 1;  // partitions per wave: at most 8 waves
     const int waves = splits / ppw;
     auto launch_staged = [&](auto kernel, int T, int CT, bool xl) {
@@ -815,8 +812,12 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
         if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 2, true>, 1, 2, true);
         else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 1, true>, 1, 2, true);
       }
-    } else if (N >= 65536 && R > 16) {  // the LM head: 64-row tiles, two column tiles
-      launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 1, true>, 4, 2, true);
+    } else if (R > 16 && N < 16384) {  // q|k|v-sized: 32-row tiles, two column tiles
+      if (ppw == 2) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 2, 512, 2, true>, 2, 2, true);
+      else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 2, 512, 1, true>, 2, 2, true);
+    } else if (R > 16) {  // gate|up and the LM head: 64-row tiles, two column tiles
+      if (ppw == 2) launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 2, true>, 4, 2, true);
+      else launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 1, true>, 4, 2, true);
     } else if (N >= 65536 && R > 8) {  // 128-row tiles
       launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1, false>, 8, 1, false);
     } else {  // 32-row tiles, R <= 16
