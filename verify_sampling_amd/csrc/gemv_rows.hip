@@ -46,6 +46,8 @@
 //    workgroup takes one partition (grid.y) and writes its partial sums to a
 //    caller workspace, which a second small kernel adds in partition order.
 
+#include <type_traits>
+
 #include "vs_internal.h"
 
 namespace {
@@ -288,13 +290,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int T, int U, int CT>
+template <int T, int U, int CT, int XL>
 struct RunStage {
   u32x4 w[T * TILE * U * 64 / 1024];  // this lane's 16-byte pieces of the stage
-  float4 x[U][CT][2];
+  // activations: XL, one 16-byte piece per load instruction (at most
+  // CT * 16 rows x U k-blocks x 128 bytes); direct, the lane's own column
+  float4 x[XL > 0 ? XL : U * CT * 2];
 };
 
-template <int T, int U, int CT, int LB, int PPW, bool XL>
+template <int T, int U, int CT, int LB, int PPW, int XL>
 __global__ void __launch_bounds__(LB)
 gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
                         const float* __restrict__ X, int64_t ldx, int R,
@@ -312,9 +316,11 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   const int col = lane & 15;
   const int n0 = blockIdx.x * TILE * T;
   // XL: activations go through LDS as well (XB bytes per wave after the
-  // weights), loaded as whole rows of a k-block
+  // weights), loaded as whole 128-byte rows of a k-block
+  constexpr int XR = CT * TILE;                     // activation rows per k-block in LDS
   constexpr int XS = KBLK * 4 + 16;                 // LDS stride of an activation row
-  constexpr int XB = XL ? U * CT * TILE * XS : 0;   // activation stage bytes per wave
+  constexpr bool kXL = XL > 0;                      // XL activation loads per stage, or 0
+  constexpr int XB = kXL ? U * XR * XS : 0;         // activation stage bytes per wave
   uint8_t* stg = reinterpret_cast<uint8_t*>(red) + static_cast<size_t>(wave) * (T * TILE * RS + XB);
   uint8_t* xstg = stg + T * TILE * RS;
 
@@ -328,18 +334,31 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   // Activation rows; rows >= R read row R - 1, and their (independent)
   // MFMA outputs are never stored.  Direct: the lane's own column, its two
   // 16-byte pieces at 8g and 8g + 4, loaded in the operand layout (16 rows
-  // per instruction, half of each row's 128 bytes).  XL: 8 lanes per row
-  // cover the row's whole 128 bytes, 8 rows per instruction, and the
-  // operand layout is read back from LDS, which moves fewer partly used
-  // cache lines per activation byte once R is large.
+  // per instruction, half of each row's 128 bytes).  XL: only the R rows
+  // are loaded, as whole 128-byte rows of a k-block: instruction j carries
+  // the (row, k-block) pairs 8j .. 8j + 7 (pair q is row q / U, k-block
+  // q % U of the stage; 8 lanes per pair), so a stage takes ceil(R U / 8)
+  // instructions, and the operand layout is read back from LDS.
+  static_assert(!kXL || (8 % U == 0 && XL <= XR * U / 8), "whole k-block pairs, at most XR rows");
+  const int xu = (lane >> 3) % U;            // XL: this lane's k-block within the stage
+  const int xq = (lane >> 3) / U;            // XL: its row in instruction 0
+  const float* xbase = X + (lane & 7) * 4;
+  const int xdbase = xu * XR * XS + (lane & 7) * 16;  // XL: LDS byte offset of row 0
+  // XL: the row of this lane's pair in instruction j (rows >= R repeat row R - 1)
+  auto xrow_of = [&](int j) {
+    const int r = (8 / U) * j + xq;
+    return r < R ? r : R - 1;
+  };
   const float* xrow[CT][2];
+  if constexpr (!kXL) {
 #pragma unroll
-  for (int c = 0; c < CT; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = XL ? c * 16 + h * 8 + (lane >> 3) : c * 16 + col;
-      xrow[c][h] = X + static_cast<int64_t>(r < R ? r : R - 1) * ldx + (XL ? (lane & 7) * 4 : g * 8 + h * 4);
-    }
+      for (int h = 0; h < 2; ++h) {
+        const int r = c * 16 + col;
+        xrow[c][h] = X + static_cast<int64_t>(r < R ? r : R - 1) * ldx + g * 8 + h * 4;
+      }
+  }
   static_assert(PPW == 1 || PPW == 2, "partitions per wave");
   const int p0 = wave * PPW;
   const int kb0 = static_cast<int>((static_cast<int64_t>(p0) * nkb) / splits);
@@ -357,35 +376,37 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   // the wave's range: a stage issued past its end re-reads the range's last
   // blocks (cache hits) instead of the next wave's
   auto first_block = [&](int kb) { return kb + U <= kb1 ? kb : kb1 - U; };
-  auto issue = [&](RunStage<T, U, CT>& st, int kb) {
+  auto issue = [&](RunStage<T, U, CT, XL>& st, int kb) {
     // activations first: memory returns in issue order
+    if constexpr (kXL) {  // ceil(R U / 8) == XL loads, none of them conditional
+      const int64_t off = static_cast<int64_t>(kb + xu < kb1 ? kb + xu : kb1 - 1) * KBLK;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t off = static_cast<int64_t>(kb + u < kb1 ? kb + u : kb1 - 1) * KBLK;
+      for (int j = 0; j < XL; ++j)
+        st.x[j] = *reinterpret_cast<const float4*>(xbase + static_cast<int64_t>(xrow_of(j)) * ldx + off);
+    } else {
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        st.x[u][c][0] = *reinterpret_cast<const float4*>(xrow[c][0] + off);
-        st.x[u][c][1] = *reinterpret_cast<const float4*>(xrow[c][1] + off);
+      for (int u = 0; u < U; ++u) {
+        const int64_t off = static_cast<int64_t>(kb + u < kb1 ? kb + u : kb1 - 1) * KBLK;
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          st.x[(u * CT + c) * 2] = *reinterpret_cast<const float4*>(xrow[c][0] + off);
+          st.x[(u * CT + c) * 2 + 1] = *reinterpret_cast<const float4*>(xrow[c][1] + off);
+        }
       }
     }
     const int64_t woff = static_cast<int64_t>(first_block(kb)) * (KBLK * 2);
 #pragma unroll
     for (int i = 0; i < NI; ++i) st.w[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + woff);
   };
-  auto compute = [&](const RunStage<T, U, CT>& st, int kb) {
+  auto compute = [&](const RunStage<T, U, CT, XL>& st, int kb) {
     const int kl = first_block(kb);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<u32x4*>(stg + (i * RPI + lane / LPR) * RS + (lane % LPR) * 16) = st.w[i];
-    if constexpr (XL) {
+    if constexpr (kXL) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            *reinterpret_cast<float4*>(xstg + ((u * CT + c) * TILE + h * 8 + (lane >> 3)) * XS + (lane & 7) * 16) =
-                st.x[u][c][h];
+      for (int j = 0; j < XL; ++j)
+        *reinterpret_cast<float4*>(xstg + xdbase + xrow_of(j) * XS) = st.x[j];
     }
     wave_lds_sync();
 #pragma unroll
@@ -399,11 +420,15 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
       auto accumulate = [&](f32x4 (&ac)[T][CT]) {
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          float4 x0 = st.x[u][c][0], x1 = st.x[u][c][1];
-          if constexpr (XL) {
-            const uint8_t* xa = xstg + ((u * CT + c) * TILE + col) * XS + g * 32;
+          float4 x0, x1;
+          if constexpr (kXL) {
+            const int r = c * TILE + col < R ? c * TILE + col : R - 1;  // rows >= R: never stored
+            const uint8_t* xa = xstg + (u * XR + r) * XS + g * 32;
             x0 = *reinterpret_cast<const float4*>(xa);
             x1 = *reinterpret_cast<const float4*>(xa + 16);
+          } else {
+            x0 = st.x[(u * CT + c) * 2];
+            x1 = st.x[(u * CT + c) * 2 + 1];
           }
           const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           u32x4 hi, mid, lo;
@@ -422,7 +447,7 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
     wave_lds_sync();  // every lane has read the stage before the next one is written
   };
   if (kb0 < kb1) {
-    RunStage<T, U, CT> sa, sb;
+    RunStage<T, U, CT, XL> sa, sb;
     issue(sa, kb0);
     for (int kb = kb0; kb < kb1; kb += 2 * U) {
       issue(sb, kb + U);
@@ -795,40 +820,43 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
       if (stage > shm) shm = stage;
       kernel<<<grid, dim3(64 * waves), shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
     };
-    // Activations through LDS (XL) where a sweep on MI355X found it faster:
-    // once the activation bytes per weight byte, R / (8 T), are large, and
-    // for the q|k|v-sized matrices at every R.
+    // T row tiles, CT column tiles, partitions per wave; xl: activations
+    // through LDS, ceil(R U / 8) loads per stage
+    const int nx = (R * STAGE_U + 7) / 8;
+    auto staged = [&](auto t_c, auto ct_c, bool xl) {
+      constexpr int T = decltype(t_c)::value, CT = decltype(ct_c)::value;
+      auto go = [&](auto xl_c) {
+        constexpr int XL = decltype(xl_c)::value;
+        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<T, STAGE_U, CT, 512, 2, XL>, T, CT, XL > 0);
+        else launch_staged(gemv_rows_staged_kernel<T, STAGE_U, CT, 512, 1, XL>, T, CT, XL > 0);
+      };
+      using I = std::integral_constant<int, 0>;
+      if constexpr (CT == 1) {
+        if (!xl) go(I{});
+        else if (nx == 1) go(std::integral_constant<int, 1>{});
+        else if (nx == 2) go(std::integral_constant<int, 2>{});
+        else if (nx == 3) go(std::integral_constant<int, 3>{});
+        else go(std::integral_constant<int, 4>{});
+      } else {  // R > 16: always through LDS
+        if (nx == 5) go(std::integral_constant<int, 5>{});
+        else go(std::integral_constant<int, 6>{});
+      }
+    };
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    using Four = std::integral_constant<int, 4>;
+    // Activations through LDS where a sweep on MI355X found it faster.
     if (N < 6144) {  // 16-row tiles
-      const bool xl = R >= 6;
-      if (R <= 16) {
-        if (ppw == 2) {
-          if (xl) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 2, true>, 1, 1, true);
-          else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 2, false>, 1, 1, false);
-        } else {
-          if (xl) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 1, true>, 1, 1, true);
-          else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 1, 512, 1, false>, 1, 1, false);
-        }
-      } else {
-        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 2, true>, 1, 2, true);
-        else launch_staged(gemv_rows_staged_kernel<1, STAGE_U, 2, 512, 1, true>, 1, 2, true);
-      }
+      if (R <= 16) staged(One{}, One{}, true);
+      else staged(One{}, Two{}, true);
     } else if (R > 16 && N < 16384) {  // q|k|v-sized: 32-row tiles, two column tiles
-      if (ppw == 2) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 2, 512, 2, true>, 2, 2, true);
-      else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 2, 512, 1, true>, 2, 2, true);
+      staged(Two{}, Two{}, true);
     } else if (R > 16) {  // gate|up and the LM head: 64-row tiles, two column tiles
-      if (ppw == 2) launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 2, true>, 4, 2, true);
-      else launch_staged(gemv_rows_staged_kernel<4, STAGE_U, 2, 512, 1, true>, 4, 2, true);
+      staged(Four{}, Two{}, true);
     } else if (N >= 65536 && R > 8) {  // 128-row tiles
-      launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1, false>, 8, 1, false);
+      launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1, 0>, 8, 1, false);
     } else {  // 32-row tiles, R <= 16
-      const bool xl = N < 16384 || (N >= 65536 ? R >= 8 : R >= 10);
-      if (ppw == 2) {
-        if (xl) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2, true>, 2, 1, true);
-        else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 2, false>, 2, 1, false);
-      } else {
-        if (xl) launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1, true>, 2, 1, true);
-        else launch_staged(gemv_rows_staged_kernel<2, STAGE_U, 1, 512, 1, false>, 2, 1, false);
-      }
+      staged(Two{}, One{}, N < 65536 || R >= 8);
     }
     return vs::check_launch();
   }
