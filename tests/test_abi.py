@@ -54,11 +54,14 @@ def test_gemv_rejects_before_launch():
     assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 4) == 0
     assert lib.verify_gemv_rows_workspace_bytes(151936, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 4) == 0
-    # long rows of >= 48 MB take partitions across workgroups from 9 rows;
-    # other matrices of >= 48 MB only where the staged kernel cannot run
-    # (here K % 32 != 0), above 16 rows
+    # long rows of >= 48 MB take partitions across workgroups above 16 rows,
+    # and from 9 rows where the staged kernel cannot run (K % 32 != 0); other
+    # matrices of >= 48 MB only where the staged kernel cannot run, above 16
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 8) == 0
-    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 16) == 16 * 16 * 4096 * 4
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 16) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 17) == 16 * 17 * 4096 * 4
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12296, 8) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(4096, 12296, 9) == 16 * 9 * 4096 * 4
     assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(24576, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(6152, 4104, 16) == 0

@@ -20,6 +20,12 @@ inline int check_launch() {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The wavefront's index within its workgroup (64-lane waves), marked uniform
+// so that loops and addresses derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------- ordering keys
 //
 // The pool order (value descending, index ascending, NaN below -inf, -0 == +0)
