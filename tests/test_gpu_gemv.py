@@ -121,14 +121,16 @@ def test_strided_operands():
 
 
 @pytest.mark.parametrize("N,K", [(65573, 1064), (6151, 4104), (24576, 4096), (4096, 12288),
-                                 (4096, 12296), (6144, 4096)])
+                                 (4100, 12288), (4096, 12296), (6144, 4096), (6150, 4096)])
 def test_shared_activation_paths_bit_identical(N, K):
-    """Long rows of >= 48 MB run the shared-activation kernel with a
-    workspace of K-partition partial sums above 16 rows (4096 x 12288), or
-    from 9 rows where their k-blocks do not fit the staged kernel
-    (4096 x 12296); other matrices of >= 48 MB whose k-blocks do not fit
-    the staged kernel do above 16 rows (all-K sharing for the wide ones);
-    the rest stay on the staged kernel, with two column tiles above 16.  Their rows equal the 1-row call bit for bit,
+    """Partitions across workgroups with a workspace of partial sums: long
+    rows of >= 48 MB from 9 rows (the staged split-K kernel for 4096 and
+    4100 x 12288, the older shared kernel for 4096 x 12296, whose k-blocks
+    do not fit the staged kernels), q|k|v-sized matrices of >= 48 MB above
+    16 rows (6144 and 6150 x 4096), and other matrices of >= 48 MB whose
+    k-blocks do not fit the staged kernels above 16 rows (all-K sharing for
+    the wide ones); the rest stay on the staged row-block kernel, with two
+    column tiles above 16.  Their rows equal the 1-row call bit for bit,
     with the workspace and without it, and match the oracle.  Ragged N and a
     partial last k-block are included."""
     W = torch_bf16_weights((N, K), 3000 + N % 97 + K % 89, "cuda:0")

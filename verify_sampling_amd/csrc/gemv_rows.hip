@@ -37,14 +37,17 @@
 //    stage through the wave's own LDS region into the operand layout.  The
 //    plain variant (operands loaded in place) covers the shapes the staged
 //    one does not (K % 32 != 0, short partitions, more than 8 waves).
-//  * Shared-activation kernels (R > 16): a workgroup of P wavefronts along N
-//    loads each activation tile once, splits it once into the three bf16
-//    planes in LDS, and all P waves read their MFMA operand from there.
+//  * Shared-activation kernels (many rows): a workgroup of P wavefronts
+//    along N loads each activation tile once, splits it once into the three
+//    bf16 planes in LDS, and all P waves read their MFMA operand from there.
 //    This divides the activation traffic per weight byte by P, which is what
-//    makes a row-block pass slow down with R.  Either every wave walks all
-//    of K and adds its partition sums in registers (wide matrices), or each
-//    workgroup takes one partition (grid.y) and writes its partial sums to a
-//    caller workspace, which a second small kernel adds in partition order.
+//    makes a row-block pass slow down with R.  Each workgroup takes one
+//    partition (grid.y) and writes its partial sums to a caller workspace,
+//    which a second small kernel adds in partition order; the staged form
+//    loads its weights as the staged row-block kernel does.  Where the
+//    staged kernels cannot run, an older form loads weights in the operand
+//    layout and may instead walk all of K per wave, adding its partition sums
+//    in registers (very wide matrices).
 
 #include <type_traits>
 
@@ -680,6 +683,166 @@ gemv_shared_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
   }
 }
 
+// Staged split-K kernel: the shared kernel's activation planes (each
+// k-block's activations split once per workgroup into LDS) with the staged
+// kernel's weight path (row runs of 8 rows x 128 bytes per load,
+// non-temporal, no per-lane guards, restaged through the wave's own LDS
+// region into the operand layout).  Workgroup = P wavefronts along N, wave p
+// owning T 16-row tiles, over partition blockIdx.y, whose sums go to
+// parts[(s * R + r) * ldp + n] for reduce_partials_kernel.  Every wave loads
+// one activation image per stage (images past the stage's count are loaded
+// but not stored, so that no load is conditional).  Requires K % 32 == 0
+// and at least U k-blocks per partition.
+template <int T, int CT, int P>
+__global__ void __launch_bounds__(64 * P)
+gemv_staged_split_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
+                         const float* __restrict__ X, int64_t ldx, int R,
+                         float* __restrict__ parts, int64_t ldp, int nkb, int splits) {
+  constexpr int U = 2;                    // k-blocks per stage
+  constexpr int RB = U * KBLK * 2;        // bytes of one weight row per stage
+  constexpr int RS = RB + 16;             // LDS row stride
+  constexpr int LPR = RB / 16;            // lanes per row in one load
+  constexpr int RPI = 64 / LPR;           // rows per load instruction
+  constexpr int NI = T * TILE / RPI;      // weight loads per stage
+  constexpr int IMG = U * CT;             // activation images per stage
+  constexpr int IPW = (IMG + P - 1) / P;  // images each wave loads
+  static_assert(64 % LPR == 0 && (T * TILE) % RPI == 0, "stage shape");
+  __shared__ XTile<U, CT> xs[2];
+  extern __shared__ float wst[];          // [P][T * TILE * RS bytes]
+  const int lane = threadIdx.x & 63;
+  const int p = vs::wave_index();
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int n0 = (blockIdx.x * P + p) * TILE * T;
+  const int kb0 = static_cast<int>((static_cast<int64_t>(blockIdx.y) * nkb) / splits);
+  const int kb1 = static_cast<int>((static_cast<int64_t>(blockIdx.y + 1) * nkb) / splits);
+  uint8_t* stg = reinterpret_cast<uint8_t*>(wst) + static_cast<size_t>(p) * (T * TILE * RS);
+
+  const uint8_t* wsrc[NI];  // this lane's rows, at its 16-byte column of the stage
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    int wr = n0 + i * RPI + lane / LPR;
+    if (wr >= N) wr = N - 1;  // ragged tile: load a valid row, discard its results
+    wsrc[i] = reinterpret_cast<const uint8_t*>(W + static_cast<int64_t>(wr) * ldw) + (lane % LPR) * 16;
+  }
+  // this wave's activation images: (k-block u, column tile c) = img / CT,
+  // img % CT; the lane's row (rows >= R repeat row R - 1, never stored) and
+  // its 8 values at k = 32 (kb + u) + 8 g
+  const float* xsrc[IPW];
+  int ximg[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    ximg[i] = p + i * P;
+    const int img = ximg[i] % IMG;
+    const int c = img % CT;
+    const int r = c * TILE + col < R ? c * TILE + col : R - 1;
+    xsrc[i] = X + static_cast<int64_t>(r) * ldx + g * 8;
+  }
+
+  f32x4 acc[T][CT];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // a stage starting at k-block kb holds blocks [kl, kl + U), kept inside the
+  // range: a stage issued past the end re-reads the range's last blocks
+  auto first_block = [&](int kb) { return kb + U <= kb1 ? kb : kb1 - U; };
+  auto issue = [&](float (&x)[IPW][8], u32x4 (&w)[NI], int kb) {
+    // activations first: memory returns in issue order
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int u = (ximg[i] % IMG) / CT;
+      const int64_t off = static_cast<int64_t>(kb + u < kb1 ? kb + u : kb1 - 1) * KBLK;
+      const float4 a = *reinterpret_cast<const float4*>(xsrc[i] + off);
+      const float4 b = *reinterpret_cast<const float4*>(xsrc[i] + off + 4);
+      x[i][0] = a.x; x[i][1] = a.y; x[i][2] = a.z; x[i][3] = a.w;
+      x[i][4] = b.x; x[i][5] = b.y; x[i][6] = b.z; x[i][7] = b.w;
+    }
+    const int64_t woff = static_cast<int64_t>(first_block(kb)) * (KBLK * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) w[i] = load_weights(wsrc[i] + woff);
+  };
+  auto store_x = [&](const float (&x)[IPW][8], int buf) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      if (ximg[i] < IMG) {  // uniform across the wave
+        const int u = ximg[i] / CT, c = ximg[i] % CT;
+        u32x4 hi, mid, lo;
+        split3(x[i], hi, mid, lo);
+        xs[buf].v[u][0][c][lane] = hi;
+        xs[buf].v[u][1][c][lane] = mid;
+        xs[buf].v[u][2][c][lane] = lo;
+      }
+    }
+  };
+  // one stage: weights w (k-blocks from kb) against activation buffer buf;
+  // the next stage's loads (xn, wn) are issued first
+  float x[IPW][8];
+  auto stage = [&](const u32x4 (&w)[NI], u32x4 (&wn)[NI], int kb, int buf) {
+    issue(x, wn, kb + U);
+    const int kl = first_block(kb);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<u32x4*>(stg + (i * RPI + lane / LPR) * RS + (lane % LPR) * 16) = w[i];
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb + u >= kb1) break;  // uniform across the workgroup
+      const int uu = kb + u - kl;
+      u32x4 a[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        a[t] = *reinterpret_cast<const u32x4*>(stg + (t * TILE + col) * RS + uu * (KBLK * 2) + g * 16);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const u32x4 hi = xs[buf].v[u][0][c][lane];
+        const u32x4 mid = xs[buf].v[u][1][c][lane];
+        const u32x4 lo = xs[buf].v[u][2][c][lane];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          acc[t][c] = mfma(a[t], hi, acc[t][c]);
+          acc[t][c] = mfma(a[t], mid, acc[t][c]);
+          acc[t][c] = mfma(a[t], lo, acc[t][c]);
+        }
+      }
+    }
+    wave_lds_sync();  // every lane has read the weights before the next stage's are written
+    store_x(x, buf ^ 1);  // that buffer was last read before the previous barrier
+    __syncthreads();
+  };
+
+  u32x4 wa[NI], wb[NI];
+  issue(x, wa, kb0);
+  store_x(x, 0);
+  __syncthreads();
+  for (int kb = kb0; kb < kb1; kb += 2 * U) {  // uniform over the workgroup
+    stage(wa, wb, kb, 0);
+    if (kb + U >= kb1) break;
+    stage(wb, wa, kb + U, 1);
+  }
+
+  // MFMA 16x16 output layout: lane l, element e holds weight row 4*(l/16)+e
+  // of the tile and activation row l%16 of the column tile.
+  const int64_t pbase = static_cast<int64_t>(blockIdx.y) * R;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int r = c * 16 + col;
+      const int n = n0 + t * TILE + 4 * g;
+      if (r >= R || n >= N) continue;
+      float* dst = parts + (pbase + r) * ldp + n;
+      if (n + 3 < N) {
+        *reinterpret_cast<f32x4*>(dst) = acc[t][c];  // ldp % 4 == 0, n % 4 == 0
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) dst[e] = acc[t][c][e];
+      }
+    }
+}
+
 // Y[r][n..n+3] = the partition sums of parts added left to right.  All
 // partition loads are issued before the first add (the add order is fixed,
 // the load order is not), so the kernel costs one memory round trip.
@@ -732,23 +895,27 @@ bool staged_fits(int N, int K) {
 
 // Which kernel runs for (N, K, R).  Chosen by per-shape sweeps on MI355X.
 // The row-block kernels re-read the activations once per row tile, so their
-// time grows with R; the shared-activation kernels share each activation
-// tile among a workgroup's waves and stay nearly flat in R, from a higher
-// base (and the split-K form adds a dependent partition-sum launch).  The
-// staged row-block kernel, with taller tiles and activations through LDS
-// as R grows, wins at every R up to 16 and above 16 everywhere except on
-// long rows of >= 48 MB (down), which take partitions across workgroups.
-// Where the staged kernel cannot run, matrices of >= 48 MB take the shared
-// kernels from 9 rows (long rows) or above 16 rows (all-K for very wide
-// ones).
-enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK };
+// time grows with R; the split-K kernels share each activation tile among a
+// workgroup's waves and stay nearly flat in R, from a higher base (a
+// dependent partition-sum launch).  The staged row-block kernel wins up to 8
+// rows everywhere and beyond on wide matrices (gate|up, the LM head) and on
+// matrices under 48 MB; long rows of >= 48 MB (down) take the staged split-K
+// kernel from 9 rows, q|k|v-sized matrices above 16.  Where the staged
+// kernels cannot run (K % 32 != 0), matrices of >= 48 MB take the older
+// shared kernels from 9 rows (long rows) or above 16 rows (all-K for very
+// wide ones).
+enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK, kStagedSplitK };
 
 Kind kind_for(int N, int K, int R) {
   if (R <= 8) return Kind::kRowBlock;
   const bool big = 2.0 * N * K >= 48e6;
   const bool long_rows = (K + KBLK - 1) / KBLK >= 256;
-  if (N < 65536 && big && long_rows && (R > 16 || !staged_fits(N, K))) return Kind::kSharedSplitK;
-  if (staged_fits(N, K) || R <= 16 || !big) return Kind::kRowBlock;
+  if (staged_fits(N, K)) {
+    if (big && N < 65536 && (long_rows || (R > 16 && N < 16384))) return Kind::kStagedSplitK;
+    return Kind::kRowBlock;
+  }
+  if (N < 65536 && big && long_rows) return Kind::kSharedSplitK;
+  if (R <= 16 || !big) return Kind::kRowBlock;
   return N >= 65536 ? Kind::kSharedAllK : Kind::kSharedSplitK;
 }
 
@@ -762,7 +929,8 @@ size_t split_workspace_bytes(int N, int K, int R) {
 
 extern "C" size_t verify_gemv_rows_workspace_bytes(int N, int K, int R) {
   if (N < 1 || K < 1 || R < 1 || R > VS_MAX_ROWS) return 0;
-  return kind_for(N, K, R) == Kind::kSharedSplitK ? split_workspace_bytes(N, K, R) : 0;
+  const Kind kind = kind_for(N, K, R);
+  return kind == Kind::kSharedSplitK || kind == Kind::kStagedSplitK ? split_workspace_bytes(N, K, R) : 0;
 }
 
 extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, const float* X,
@@ -779,10 +947,27 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   Kind kind = kind_for(N, K, R);
   // without a (large enough, aligned) workspace the row-block kernel runs:
   // same summation order, same bits
-  if (kind == Kind::kSharedSplitK &&
+  if ((kind == Kind::kSharedSplitK || kind == Kind::kStagedSplitK) &&
       (!workspace || workspace_bytes < split_workspace_bytes(N, K, R) || !vs::aligned16(workspace)))
     kind = Kind::kRowBlock;
 
+  if (kind == Kind::kStagedSplitK) {
+    float* parts = static_cast<float*>(workspace);
+    const int64_t ldp = parts_ld(N);
+    auto launch = [&](auto kernel, int T, int P) {
+      const dim3 grid((N + TILE * T * P - 1) / (TILE * T * P), splits);
+      const size_t shm = static_cast<size_t>(P) * T * TILE * (2 * KBLK * 2 + 16);
+      kernel<<<grid, dim3(64 * P), shm, stream>>>(W, ldw, N, K, X, ldx, R, parts, ldp, nkb, splits);
+    };
+    if (R > 16) launch(gemv_staged_split_kernel<1, 2, 4>, 1, 4);
+    else launch(gemv_staged_split_kernel<1, 1, 4>, 1, 4);
+    int st = vs::check_launch();
+    if (st != VS_OK) return st;
+    const int quads = static_cast<int>((N + 3) / 4);
+    reduce_partials_kernel<<<dim3((quads + 255) / 256, R), dim3(256), 0, stream>>>(parts, ldp, splits,
+                                                                                   R, N, Y, ldy);
+    return vs::check_launch();
+  }
   if (kind == Kind::kSharedAllK) {
     auto launch = [&](auto kernel, int T, int P) {
       const dim3 grid((N + TILE * T * P - 1) / (TILE * T * P));
