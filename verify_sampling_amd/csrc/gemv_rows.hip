@@ -158,10 +158,10 @@ __device__ __forceinline__ void compute_stage(const Stage<T, U, CT>& st, int kb,
 }
 
 // T: 16-row weight tiles per wave (the activations are loaded and split once
-// for all T); U: k-blocks per stage; CT: 16-column activation tiles; PIPE:
-// load stage s+1 while computing stage s.  None of these changes the order in
-// which a row is summed.
-template <int T, int U, int CT, bool PIPE, bool XF = false>
+// for all T); U: k-blocks per stage; CT: 16-column activation tiles; XF: a
+// stage's activations are loaded ahead of its weights.  None of these changes
+// the order in which a row is summed.
+template <int T, int U, int CT, bool XF>
 __global__ void __launch_bounds__(1024)
 gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
                  const float* __restrict__ X, int64_t ldx, int R,
@@ -198,17 +198,7 @@ gemv_rows_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int K,
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (PIPE) {
-    Stage<T, U, CT> sa, sb;
-    load_stage(sa, kb0, kb1, K, g, wrow, xrow, xon);
-    for (int kb = kb0; kb < kb1; kb += 2 * U) {
-      if (kb + U < kb1) load_stage(sb, kb + U, kb1, K, g, wrow, xrow, xon);
-      compute_stage(sa, kb, kb1, acc);
-      if (kb + U >= kb1) break;
-      if (kb + 2 * U < kb1) load_stage(sa, kb + 2 * U, kb1, K, g, wrow, xrow, xon);
-      compute_stage(sb, kb + U, kb1, acc);
-    }
-  } else if (XF) {
+  if (XF) {
     // activations of the stage first, then its weights (see load_stage)
     for (int kb = kb0; kb < kb1; kb += U) {
       Stage<T, U, CT> st;
@@ -1015,24 +1005,22 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
       if (stage > shm) shm = stage;
       kernel<<<grid, dim3(64 * waves), shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
     };
-    // T row tiles, CT column tiles, partitions per wave; xl: activations
-    // through LDS, ceil(R U / 8) loads per stage
+    // T row tiles and CT column tiles, activations through LDS with
+    // ceil(R U / 8) loads per stage (a compile-time count)
     const int nx = (R * STAGE_U + 7) / 8;
-    auto staged = [&](auto t_c, auto ct_c, bool xl) {
+    auto staged = [&](auto t_c, auto ct_c) {
       constexpr int T = decltype(t_c)::value, CT = decltype(ct_c)::value;
       auto go = [&](auto xl_c) {
         constexpr int XL = decltype(xl_c)::value;
-        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<T, STAGE_U, CT, 512, 2, XL>, T, CT, XL > 0);
-        else launch_staged(gemv_rows_staged_kernel<T, STAGE_U, CT, 512, 1, XL>, T, CT, XL > 0);
+        if (ppw == 2) launch_staged(gemv_rows_staged_kernel<T, STAGE_U, CT, 512, 2, XL>, T, CT, true);
+        else launch_staged(gemv_rows_staged_kernel<T, STAGE_U, CT, 512, 1, XL>, T, CT, true);
       };
-      using I = std::integral_constant<int, 0>;
       if constexpr (CT == 1) {
-        if (!xl) go(I{});
-        else if (nx == 1) go(std::integral_constant<int, 1>{});
+        if (nx == 1) go(std::integral_constant<int, 1>{});
         else if (nx == 2) go(std::integral_constant<int, 2>{});
         else if (nx == 3) go(std::integral_constant<int, 3>{});
         else go(std::integral_constant<int, 4>{});
-      } else {  // R > 16: always through LDS
+      } else {  // R > 16
         if (nx == 5) go(std::integral_constant<int, 5>{});
         else go(std::integral_constant<int, 6>{});
       }
@@ -1040,18 +1028,19 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
     using One = std::integral_constant<int, 1>;
     using Two = std::integral_constant<int, 2>;
     using Four = std::integral_constant<int, 4>;
-    // Activations through LDS where a sweep on MI355X found it faster.
     if (N < 6144) {  // 16-row tiles
-      if (R <= 16) staged(One{}, One{}, true);
-      else staged(One{}, Two{}, true);
+      if (R <= 16) staged(One{}, One{});
+      else staged(One{}, Two{});
     } else if (R > 16 && N < 16384) {  // q|k|v-sized: 32-row tiles, two column tiles
-      staged(Two{}, Two{}, true);
+      staged(Two{}, Two{});
     } else if (R > 16) {  // gate|up and the LM head: 64-row tiles, two column tiles
-      staged(Four{}, Two{}, true);
-    } else if (N >= 65536 && R > 8) {  // 128-row tiles
+      staged(Four{}, Two{});
+    } else if (N >= 65536 && R > 8) {
+      // 128-row tiles, activations loaded in the operand layout (through LDS
+      // they were 2-3% slower here)
       launch_staged(gemv_rows_staged_kernel<8, STAGE_U, 1, 512, 1, 0>, 8, 1, false);
     } else {  // 32-row tiles, R <= 16
-      staged(Two{}, One{}, N < 65536 || R >= 8);
+      staged(Two{}, One{});
     }
     return vs::check_launch();
   }
@@ -1067,15 +1056,15 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
     kernel<<<grid, block, shm, stream>>>(W, ldw, N, K, X, ldx, R, Y, ldy, nkb, splits);
   };
   if (R <= 16) {
-    if (N >= 65536 && R > 8) launch(gemv_rows_kernel<4, 1, 1, false, true>, 4, 1);
-    else if (N >= 65536) launch(gemv_rows_kernel<2, 4, 1, false, true>, 2, 1);
-    else if (N >= 16384 && R > 8) launch(gemv_rows_kernel<2, 2, 1, false, false>, 2, 1);
-    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 1, false, true>, 2, 1);
-    else launch(gemv_rows_kernel<1, 4, 1, false, true>, 1, 1);
+    if (N >= 65536 && R > 8) launch(gemv_rows_kernel<4, 1, 1, true>, 4, 1);
+    else if (N >= 65536) launch(gemv_rows_kernel<2, 4, 1, true>, 2, 1);
+    else if (N >= 16384 && R > 8) launch(gemv_rows_kernel<2, 2, 1, false>, 2, 1);
+    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 1, true>, 2, 1);
+    else launch(gemv_rows_kernel<1, 4, 1, true>, 1, 1);
   } else {
-    if (N >= 65536) launch(gemv_rows_kernel<4, 1, 2, false, true>, 4, 2);
-    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 2, false, true>, 2, 2);
-    else launch(gemv_rows_kernel<1, 2, 2, false, true>, 1, 2);
+    if (N >= 65536) launch(gemv_rows_kernel<4, 1, 2, true>, 4, 2);
+    else if (N >= 6144) launch(gemv_rows_kernel<2, 2, 2, true>, 2, 2);
+    else launch(gemv_rows_kernel<1, 2, 2, true>, 1, 2);
   }
   return vs::check_launch();
 }
