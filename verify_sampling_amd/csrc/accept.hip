@@ -64,9 +64,10 @@ accept_kernel(int mode, int B, int k, Dists d, const int32_t* __restrict__ draft
               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n) {
   __shared__ double scan[WINDOWS_PER_BLOCK][64];  // each wave's running sums for seq_draw
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * WINDOWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int wave = vs::wave_index();
+  const int b = blockIdx.x * WINDOWS_PER_BLOCK + wave;
   if (b >= B) return;  // whole wave; no block-wide barriers
-  double* run = scan[threadIdx.x >> 6];
+  double* run = scan[wave];
 
   const int32_t* dr = drafts + static_cast<int64_t>(b) * k;
   int32_t my_tok = -1;  // lane j holds emitted token j

@@ -40,9 +40,10 @@ policy_kernel(const float* __restrict__ vals, const int32_t* __restrict__ ids, i
   // records each partial sum, every lane reads its own after the loop
   __shared__ double scan[ROWS_PER_BLOCK][64];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int wave = vs::wave_index();
+  const int row = blockIdx.x * ROWS_PER_BLOCK + wave;
   if (row >= rows) return;  // whole wave; the kernel has no block-wide barriers
-  double* run = scan[threadIdx.x >> 6];
+  double* run = scan[wave];
 
   const float* vrow = vals + static_cast<int64_t>(row) * ld;
   const int32_t* irow = ids + static_cast<int64_t>(row) * ld;

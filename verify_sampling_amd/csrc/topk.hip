@@ -208,11 +208,13 @@ topk_chunk_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
   static_assert(NPL % 4 == 0 && GL >= 3, "chunk shape");
   __shared__ WaveShared shared[WAVES];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * WAVES + w;
-  if (unit >= static_cast<int64_t>(rows) * chunks) return;  // whole wave; no block barriers
-  const int row = static_cast<int>(unit / chunks);
-  const int chunk = static_cast<int>(unit - static_cast<int64_t>(row) * chunks);
+  const int w = vs::wave_index();
+  // rows * chunks < 2^30 (rows <= 2^24, chunks <= 64 for many rows): 32-bit
+  // scalar arithmetic
+  const uint32_t unit = blockIdx.x * WAVES + static_cast<uint32_t>(w);
+  if (unit >= static_cast<uint32_t>(rows) * static_cast<uint32_t>(chunks)) return;  // whole wave; no block barriers
+  const int row = chunks == 1 ? static_cast<int>(unit) : static_cast<int>(unit / static_cast<uint32_t>(chunks));
+  const int chunk = static_cast<int>(unit - static_cast<uint32_t>(row) * static_cast<uint32_t>(chunks));
   WaveShared& sh = shared[w];
   const float* xrow = X + static_cast<int64_t>(row) * ldx;
   const int base = chunk * CH;
@@ -532,7 +534,7 @@ topk_merge_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
                   int32_t* __restrict__ out_idx, int64_t ld_out) {
   __shared__ MergeShared shared[WAVES];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = vs::wave_index();
   const int row = blockIdx.x * WAVES + w;
   if (row >= rows) return;  // whole wave; no block barriers
   MergeShared& sh = shared[w];
