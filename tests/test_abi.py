@@ -54,9 +54,10 @@ def test_gemv_rejects_before_launch():
     assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 4) == 0
     assert lib.verify_gemv_rows_workspace_bytes(151936, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 4) == 0
-    # partitions across workgroups: long rows of >= 48 MB from 9 rows,
-    # q|k|v-sized matrices of >= 48 MB above 16 rows, and other matrices of
-    # >= 48 MB above 16 rows where the staged kernels cannot run (K % 32 != 0)
+    # partitions across workgroups: long rows of >= 48 MB from 9 rows, other
+    # matrices of >= 48 MB below 65536 rows above 16 rows, and wider ones of
+    # >= 48 MB above 16 rows only where the staged kernels cannot run
+    # (K % 32 != 0)
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 8) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 9) == 16 * 9 * 4096 * 4
     assert lib.verify_gemv_rows_workspace_bytes(4096, 12288, 16) == 16 * 16 * 4096 * 4
@@ -65,7 +66,9 @@ def test_gemv_rejects_before_launch():
     assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 16) == 0
     assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 17) == 8 * 17 * 6144 * 4
     assert lib.verify_gemv_rows_workspace_bytes(6144, 4096, 24) == 8 * 24 * 6144 * 4
-    assert lib.verify_gemv_rows_workspace_bytes(24576, 4096, 24) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(24576, 4096, 16) == 0
+    assert lib.verify_gemv_rows_workspace_bytes(24576, 4096, 24) == 4 * 24 * 24576 * 4
+    assert lib.verify_gemv_rows_workspace_bytes(151936, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 24) == 0
     assert lib.verify_gemv_rows_workspace_bytes(6152, 4104, 16) == 0
     assert lib.verify_gemv_rows_workspace_bytes(6152, 4104, 17) == 8 * 17 * 6152 * 4

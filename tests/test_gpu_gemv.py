@@ -120,17 +120,19 @@ def test_strided_operands():
     assert (y[:, 300:] == -7.0).all()
 
 
-@pytest.mark.parametrize("N,K", [(65573, 1064), (6151, 4104), (24576, 4096), (4096, 12288),
-                                 (4100, 12288), (4096, 12296), (6144, 4096), (6150, 4096)])
+@pytest.mark.parametrize("N,K", [(65573, 1064), (6151, 4104), (24576, 4096), (24580, 4096),
+                                 (4096, 12288), (4100, 12288), (4096, 12296), (6144, 4096),
+                                 (6150, 4096)])
 def test_shared_activation_paths_bit_identical(N, K):
     """Partitions across workgroups with a workspace of partial sums: long
-    rows of >= 48 MB from 9 rows (the staged split-K kernel for 4096 and
-    4100 x 12288, the older shared kernel for 4096 x 12296, whose k-blocks
-    do not fit the staged kernels), q|k|v-sized matrices of >= 48 MB above
-    16 rows (6144 and 6150 x 4096), and other matrices of >= 48 MB whose
-    k-blocks do not fit the staged kernels above 16 rows (all-K sharing for
-    the wide ones); the rest stay on the staged row-block kernel, with two
-    column tiles above 16.  Their rows equal the 1-row call bit for bit,
+    rows of >= 48 MB from 9 rows (the staged split-K kernel, 32-row tiles,
+    for 4096 and 4100 x 12288; the older shared kernel for 4096 x 12296,
+    whose k-blocks do not fit the staged kernels), other matrices of
+    >= 48 MB below 65536 rows above 16 rows (staged split-K: 16-row tiles
+    for 6144 and 6150 x 4096, 32-row tiles for 24576 and 24580 x 4096), and
+    wider matrices of >= 48 MB whose k-blocks do not fit the staged kernels
+    above 16 rows (all-K sharing); below those row counts the staged
+    row-block kernel runs.  Their rows equal the 1-row call bit for bit,
     with the workspace and without it, and match the oracle.  Ragged N and a
     partial last k-block are included."""
     W = torch_bf16_weights((N, K), 3000 + N % 97 + K % 89, "cuda:0")

@@ -888,9 +888,11 @@ bool staged_fits(int N, int K) {
 // time grows with R; the split-K kernels share each activation tile among a
 // workgroup's waves and stay nearly flat in R, from a higher base (a
 // dependent partition-sum launch).  The staged row-block kernel wins up to 8
-// rows everywhere and beyond on wide matrices (gate|up, the LM head) and on
-// matrices under 48 MB; long rows of >= 48 MB (down) take the staged split-K
-// kernel from 9 rows, q|k|v-sized matrices above 16.  Where the staged
+// rows everywhere, up to 16 below 65536 rows, at every R on matrices under
+// 48 MB and on the LM head (whose partial sums would cost more than the
+// shared activations save); long rows of >= 48 MB (down) take the staged
+// split-K kernel from 9 rows, the other matrices of >= 48 MB below 65536
+// rows (q|k|v, gate|up) above 16.  Where the staged
 // kernels cannot run (K % 32 != 0), matrices of >= 48 MB take the older
 // shared kernels from 9 rows (long rows) or above 16 rows (all-K for very
 // wide ones).
@@ -901,7 +903,7 @@ Kind kind_for(int N, int K, int R) {
   const bool big = 2.0 * N * K >= 48e6;
   const bool long_rows = (K + KBLK - 1) / KBLK >= 256;
   if (staged_fits(N, K)) {
-    if (big && N < 65536 && (long_rows || (R > 16 && N < 16384))) return Kind::kStagedSplitK;
+    if (big && N < 65536 && (long_rows || R > 16)) return Kind::kStagedSplitK;
     return Kind::kRowBlock;
   }
   if (N < 65536 && big && long_rows) return Kind::kSharedSplitK;
@@ -949,8 +951,16 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
       const size_t shm = static_cast<size_t>(P) * T * TILE * (2 * KBLK * 2 + 16);
       kernel<<<grid, dim3(64 * P), shm, stream>>>(W, ldw, N, K, X, ldx, R, parts, ldp, nkb, splits);
     };
-    if (R > 16) launch(gemv_staged_split_kernel<1, 2, 4>, 1, 4);
-    else launch(gemv_staged_split_kernel<1, 1, 4>, 1, 4);
+    // 32-row tiles per wave for long rows and wide matrices, 16 for the
+    // q|k|v-sized ones (chosen by sweep)
+    const bool tall = (K + KBLK - 1) / KBLK >= 256 || N >= 16384;
+    if (tall) {
+      if (R > 16) launch(gemv_staged_split_kernel<2, 2, 4>, 2, 4);
+      else launch(gemv_staged_split_kernel<2, 1, 4>, 2, 4);
+    } else {
+      if (R > 16) launch(gemv_staged_split_kernel<1, 2, 4>, 1, 4);
+      else launch(gemv_staged_split_kernel<1, 1, 4>, 1, 4);
+    }
     int st = vs::check_launch();
     if (st != VS_OK) return st;
     const int quads = static_cast<int>((N + 3) / 4);
