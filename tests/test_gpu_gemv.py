@@ -173,3 +173,22 @@ def test_staged_row_block_ragged_rows(N, K):
     y8 = host(vs.verify_gemv_rows(W, X[:8].contiguous()))
     err = np.abs(y8[:, rows].astype(np.float64) - ref)
     assert (err <= TOL * s).all()
+
+
+def test_workspace_fallbacks_and_stale_contents():
+    """The split-K path's workspace: a buffer one byte too small or
+    misaligned selects the single-launch path, and a workspace holding stale
+    bytes (all 0xFF, NaN as fp32) is simply overwritten; every variant gives
+    the same bits as the call with a fresh workspace."""
+    N, K, R = 4096, 12288, 12  # long rows: split-K from 9 rows
+    W = torch_bf16_weights((N, K), 3400, "cuda:0")
+    X = dev(np.random.default_rng(3401).standard_normal((R, K)).astype(np.float32))
+    need = vs.verify_gemv_rows_workspace_bytes(N, K, R)
+    assert need > 0
+    ref = host(vs.verify_gemv_rows(W, X))
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda:0")
+    big = torch.empty(need + 64, dtype=torch.uint8, device="cuda:0")
+    stale = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    for ws in (small, big[4:4 + need], stale, None):
+        y = host(vs.verify_gemv_rows(W, X, workspace=ws))
+        assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
