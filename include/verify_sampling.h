@@ -79,8 +79,8 @@ const char* vs_last_error_detail(void);
  * not depend on the workspace: with or without one the bits are the same.
  *
  *   W    bf16 bit patterns, row-major [N][ldw] (nn.Linear layout, out x in);
- *        16-byte aligned, ldw % 8 == 0, ldw >= K.
- *   X    fp32 [R][ldx]; 16-byte aligned, ldx % 4 == 0, ldx >= K.
+ *        16-byte aligned, ldw % 8 == 0, K <= ldw < 2^24.
+ *   X    fp32 [R][ldx]; 16-byte aligned, ldx % 4 == 0, K <= ldx < 2^24.
  *   Y    fp32 [R][ldy]; ldy >= N.  Must not overlap W, X or the workspace.
  *   N >= 1, 1 <= K with K % 8 == 0, 1 <= R <= VS_MAX_ROWS.
  *   workspace  optional device scratch (16-byte aligned) of at least

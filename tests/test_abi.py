@@ -49,6 +49,8 @@ def test_gemv_rejects_before_launch():
     assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 25, FAKE, 4, None, 0, None) == -2     # R > 24
     assert lib.verify_gemv_rows(FAKE, 12, 4, 12, FAKE, 12, 1, FAKE, 4, None, 0, None) == -2   # K % 8
     assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 8, 1, FAKE, 3, None, 0, None) == -2      # ldy < N
+    assert lib.verify_gemv_rows(FAKE, 1 << 24, 4, 8, FAKE, 8, 1, FAKE, 4, None, 0, None) == -2  # ldw >= 2^24
+    assert lib.verify_gemv_rows(FAKE, 8, 4, 8, FAKE, 1 << 24, 1, FAKE, 4, None, 0, None) == -2  # ldx >= 2^24
     assert lib.verify_gemv_rows(ctypes.c_void_p(0x100008), 8, 4, 8, FAKE, 8, 1, FAKE, 4, None, 0, None) == -6
     # the workspace is optional; its size is zero where no path uses one
     assert lib.verify_gemv_rows_workspace_bytes(4096, 4096, 4) == 0

@@ -350,12 +350,16 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   uint8_t* stg = reinterpret_cast<uint8_t*>(red) + static_cast<size_t>(wave) * (T * TILE * RS + XB);
   uint8_t* xstg = stg + T * TILE * RS;
 
-  const uint8_t* wsrc[NI];  // this lane's rows, at its 16-byte column of the stage
+  // addresses: a uniform base plus this lane's 32-bit byte offset, so that
+  // the per-stage step is a scalar add (the tile's rows span T * 16 * ldw * 2
+  // < 2^32 bytes: ldw < 2^26 is checked on the host)
+  const uint8_t* wtile = reinterpret_cast<const uint8_t*>(W + static_cast<int64_t>(n0) * ldw);
+  uint32_t woffs[NI];  // this lane's rows, at its 16-byte column of the stage
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     int wr = n0 + i * RPI + lane / LPR;
     if (wr >= N) wr = N - 1;  // ragged tile: load a valid row, discard its results
-    wsrc[i] = reinterpret_cast<const uint8_t*>(W + static_cast<int64_t>(wr) * ldw) + (lane % LPR) * 16;
+    woffs[i] = static_cast<uint32_t>((wr - n0) * ldw * 2) + static_cast<uint32_t>((lane % LPR) * 16);
   }
   // Activation rows; rows >= R read row R - 1, and their (independent)
   // MFMA outputs are never stored.  Direct: the lane's own column, its two
@@ -369,7 +373,6 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
   static_assert(!kXL || (8 % U == 0 && XL <= XR * U / 8), "whole k-block pairs, at most XR rows");
   const int xu = (lane >> 3) % U;            // XL: this lane's k-block within the stage
   const int xq = (lane >> 3) / U;            // XL: its row in instruction 0
-  const float* xbase = X + (lane & 7) * 4;
   const int xdbase = XP ? xu * XR * PS + (lane & 7) * 8    // XP: plane byte offset of row 0
                        : xu * XR * XS + (lane & 7) * 16;  // XL: LDS byte offset of row 0
   // XL: the row of this lane's pair in instruction j (rows >= R repeat row R - 1)
@@ -377,6 +380,12 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
     const int r = (8 / U) * j + xq;
     return r < R ? r : R - 1;
   };
+  // XL: byte offsets of this lane's piece in each load from X (R * ldx * 4
+  // < 2^32: ldx < 2^24 is checked on the host)
+  uint32_t xoffs[kXL ? XL : 1];
+#pragma unroll
+  for (int j = 0; j < (kXL ? XL : 1); ++j)
+    xoffs[j] = static_cast<uint32_t>(xrow_of(j)) * static_cast<uint32_t>(ldx) * 4u + static_cast<uint32_t>((lane & 7) * 16);
   const float* xrow[CT][2];
   if constexpr (!kXL) {
 #pragma unroll
@@ -410,7 +419,7 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
       const int64_t off = static_cast<int64_t>(kb + xu < kb1 ? kb + xu : kb1 - 1) * KBLK;
 #pragma unroll
       for (int j = 0; j < XL; ++j)
-        st.x[j] = *reinterpret_cast<const float4*>(xbase + static_cast<int64_t>(xrow_of(j)) * ldx + off);
+        st.x[j] = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(X + off) + xoffs[j]);
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -423,8 +432,9 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
       }
     }
     const int64_t woff = static_cast<int64_t>(first_block(kb)) * (KBLK * 2);
+    const uint8_t* wstage = wtile + woff;  // uniform
 #pragma unroll
-    for (int i = 0; i < NI; ++i) st.w[i] = load_weights(wsrc[i] + woff);
+    for (int i = 0; i < NI; ++i) st.w[i] = load_weights(wstage + woffs[i]);
   };
   auto compute = [&](const RunStage<T, U, CT, XL>& st, int kb) {
     const int kl = first_block(kb);
@@ -978,6 +988,7 @@ extern "C" int verify_gemv_rows(const uint16_t* W, int64_t ldw, int N, int K, co
   if (K % 8 != 0 || ldw < K || ldx < K || ldy < N) return VS_ERR_SHAPE;
   if (ldw % 8 != 0 || ldx % 4 != 0 || !vs::aligned16(W) || !vs::aligned16(X)) return VS_ERR_ALIGN;
   if (static_cast<int64_t>(N) > (int64_t{1} << 31) - 1024) return VS_ERR_SHAPE;
+  if (ldw >= (int64_t{1} << 24) || ldx >= (int64_t{1} << 24)) return VS_ERR_SHAPE;  // 32-bit tile offsets
 
   const int nkb = (K + KBLK - 1) / KBLK;
   const int splits = splits_for(N, K);
