@@ -332,3 +332,89 @@ def test_naive_tree_walk_on_drafted_trees():
         assert list(tok[b, :n[b]]) == want, b
     print(f"mean emitted per window {np.mean(n):.2f}")
     assert np.mean(n) > 1.5
+
+
+def test_maximum_depth_every_mode():
+    """k = 63 drafts, the most a window takes (64 rows), in every mode.  Some
+    windows accept every draft and the bonus row, others stop at a planted
+    position; tokens and counts equal the oracle's."""
+    from oracle.accept import accept_naive, accept_naive_tree, accept_point_mass
+
+    g = np.random.default_rng(1880)
+    B, k = 128, 63
+
+    # greedy chain: window b disagrees first at draft b (b = 63 and above: never)
+    am = g.integers(0, 50, (B, k + 1)).astype(np.int32)
+    drafts = am[:, :k].copy()
+    for b in range(min(B, k)):
+        drafts[b, b] = am[b, b] + 1
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY, dev(drafts),
+                                 (dev(am.reshape(-1, 1).copy()), None, None))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        assert list(tok[b, :n[b]]) == accept_greedy_chain(am[b], drafts[b]), b
+        assert n[b] == min(b, k) + 1
+    assert (tok[k:, :] == am[k:, :]).all()  # all 63 drafts and the bonus
+
+    # greedy tree: window 0 a 63-node path that agrees everywhere, the rest random
+    parents = np.array([[-1 if j == 0 else int(g.integers(-1, j)) for j in range(k)]
+                        for _ in range(B)], dtype=np.int32)
+    parents[0] = np.arange(-1, k - 1)
+    tokens = g.integers(0, 3, (B, k)).astype(np.int32)
+    am = g.integers(0, 3, (B, k + 1)).astype(np.int32)
+    tokens[0] = am[0, :k]
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY_TREE, dev(tokens),
+                                 (dev(am.reshape(-1, 1).copy()), None, None), parent=dev(parents))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        assert list(tok[b, :n[b]]) == accept_greedy_tree(am[b], tokens[b], parents[b]), b
+    assert n[0] == k + 1
+
+    # per-window p and q rows: even windows one-hot on a shared token (every
+    # draft accepted), odd windows random supports over 10 tokens
+    def row(b):
+        if b % 2 == 0:
+            t = np.array([int(g.integers(0, 10))], dtype=np.int32)
+            return t, np.ones(1, dtype=np.float32)
+        t = g.permutation(10)[: int(g.integers(1, 8))].astype(np.int32)
+        w = g.random(len(t)) + 0.01
+        return t, (w / w.sum()).astype(np.float32)
+
+    p_rows = [row(b) for b in range(B) for _ in range(k + 1)]
+    q_rows = [p_rows[b * (k + 1) + i] if b % 2 == 0 else row(b) for b in range(B) for i in range(k)]
+    drafts = np.array([[int(q_rows[b * k + i][0][draw(q_rows[b * k + i][1], g.random())])
+                        for i in range(k)] for b in range(B)], dtype=np.int32)
+    u = g.random((B, k + 1, 2)).astype(np.float32)
+    pi, pp, pln = pack(p_rows, 8)
+    qi, qp, qln = pack(q_rows, 8)
+    P = (dev(pi), dev(pp), dev(pln))
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_SAMPLED, dev(drafts), P, (dev(qi), dev(qp), dev(qln)),
+                                 u=dev(u))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        want = accept_sampled(p_rows[b * (k + 1):(b + 1) * (k + 1)], q_rows[b * k:(b + 1) * k],
+                              drafts[b], u[b])
+        assert list(tok[b, :n[b]]) == want, b
+    assert (n[0::2] == k + 1).all()
+
+    # deterministic drafts on the same p rows: point mass and naive sampling
+    for mode, ref in ((vs.ACCEPT_POINT_MASS, accept_point_mass), (vs.ACCEPT_NAIVE, accept_naive)):
+        tok, n = vs.spec_accept_rows(mode, dev(drafts), P, u=dev(u))
+        tok, n = host(tok), host(n)
+        for b in range(B):
+            want = ref(p_rows[b * (k + 1):(b + 1) * (k + 1)], drafts[b], u[b])
+            assert list(tok[b, :n[b]]) == want, (mode, b)
+            assert (tok[b, n[b]:] == -1).all(), (mode, b)
+        assert (n[0::2] == k + 1).all()
+
+    # naive sampling down a 63-node tree, per-window rows; window 0 a path
+    # whose one-hot rows agree with every node
+    par = parents.copy()
+    tk = np.array([[int(p_rows[b * (k + 1) + (par[b, j] + 1)][0][0]) for j in range(k)]
+                   for b in range(B)], dtype=np.int32)
+    tok, n = vs.spec_accept_rows(vs.ACCEPT_NAIVE_TREE, dev(tk), P, u=dev(u), parent=dev(par))
+    tok, n = host(tok), host(n)
+    for b in range(B):
+        want = accept_naive_tree(p_rows[b * (k + 1):(b + 1) * (k + 1)], tk[b], par[b], u[b])
+        assert list(tok[b, :n[b]]) == want, b
+    assert n[0] == k + 1
