@@ -352,7 +352,7 @@ gemv_rows_staged_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N, int 
 
   // addresses: a uniform base plus this lane's 32-bit byte offset, so that
   // the per-stage step is a scalar add (the tile's rows span T * 16 * ldw * 2
-  // < 2^32 bytes: ldw < 2^26 is checked on the host)
+  // < 2^32 bytes: ldw < 2^24 is checked on the host)
   const uint8_t* wtile = reinterpret_cast<const uint8_t*>(W + static_cast<int64_t>(n0) * ldw);
   uint32_t woffs[NI];  // this lane's rows, at its 16-byte column of the stage
 #pragma unroll
