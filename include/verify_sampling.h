@@ -11,10 +11,10 @@
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller (the host
  *     functions vs_choose_depth and vs_lookup_tree take host arrays).  The
- *     library allocates no device memory and keeps no mutable global state;
- *     scratch space,
- *     where needed, is a caller-provided workspace whose size a companion
- *     *_workspace_bytes() call reports.
+ *     library allocates no device memory and keeps no mutable global state
+ *     apart from a per-thread copy of the last HIP error text; scratch
+ *     space, where needed, is a caller-provided workspace whose size a
+ *     companion *_workspace_bytes() call reports.
  *   - Every call only enqueues work on `stream` and returns; it never
  *     synchronises the device.  Outputs are valid once the stream has
  *     reached the call.
