@@ -20,8 +20,9 @@
  *     reached the call.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     negative status means nothing was launched and no output was
- *     touched.  VS_ERR_HIP means the launch itself failed (see
- *     vs_last_error_detail()).
+ *     touched.  VS_ERR_HIP means a launch failed (see
+ *     vs_last_error_detail()); in a call of two launches the first may
+ *     already be enqueued, and it writes only the workspace.
  *   - Data are never errors: NaN and +-inf logits follow the documented
  *     orders, token ids outside [0, vocab) in a history are ignored.
  *   - Calls on distinct streams with disjoint outputs may run concurrently;
@@ -82,7 +83,7 @@ const char* vs_last_error_detail(void);
  *        16-byte aligned, ldw % 8 == 0, K <= ldw < 2^24.
  *   X    fp32 [R][ldx]; 16-byte aligned, ldx % 4 == 0, K <= ldx < 2^24.
  *   Y    fp32 [R][ldy]; ldy >= N.  Must not overlap W, X or the workspace.
- *   N >= 1, 1 <= K with K % 8 == 0, 1 <= R <= VS_MAX_ROWS.
+ *   1 <= N <= 2^31 - 1024, 1 <= K with K % 8 == 0, 1 <= R <= VS_MAX_ROWS.
  *   workspace  optional device scratch (16-byte aligned) of at least
  *        verify_gemv_rows_workspace_bytes(N, K, R) bytes.  Some (N, K, R)
  *        run faster with it (partial sums of K partitions are kept there
