@@ -67,16 +67,28 @@ def sampled_rows(N, n, seed):
     return rows
 
 
-def test_lm_head_r4_sampled_rows():
+@pytest.fixture(scope="module")
+def lm_head_weights():
     N, K = LM_HEAD_SHAPE
     W = torch_bf16_weights((N, K), 1300, "cuda:0")
-    x = np.random.default_rng(1301).standard_normal((4, K)).astype(np.float32)
-    y = host(vs.verify_gemv_rows(W, dev(x)))
     rows = sampled_rows(N, 3000, 1302)
     w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
+    return W, rows, w_rows
+
+
+@pytest.mark.parametrize("R", [1, 4, 8, 12, 16, 17, 24])
+def test_lm_head_sampled_rows(lm_head_weights, R):
+    """The 151936 x 4096 LM head at every tile configuration it takes (32-row
+    tiles up to 8 rows, 128-row tiles at 9-16, two column tiles above 16)."""
+    W, rows, w_rows = lm_head_weights
+    x = np.random.default_rng(1301 + R).standard_normal((R, W.shape[1])).astype(np.float32)
+    X = dev(x)
+    y = host(vs.verify_gemv_rows(W, X))
     ref, s = gemv_rows(w_rows, x)
     err = np.abs(y[:, rows].astype(np.float64) - ref)
     assert (err <= TOL * s).all()
+    y1 = host(vs.verify_gemv_rows(W, X[R - 1:R]))
+    assert np.array_equal(y1[0].view(np.uint32), y[R - 1].view(np.uint32))
 
 
 @pytest.mark.parametrize("R", [1, 2, 4, 8, 16, 24])
