@@ -87,16 +87,19 @@ def penalize_dense(logits: np.ndarray, ctx: np.ndarray, drafts: np.ndarray, wind
 
 
 def penalize_sparse(ids: np.ndarray, vals: np.ndarray, ctx: np.ndarray, drafts: np.ndarray,
-                    window: int, repeat: float, presence: float, frequency: float) -> np.ndarray:
+                    window: int, repeat: float, presence: float, frequency: float, *,
+                    vocab: int) -> np.ndarray:
     """Candidate lists: row i holds ids[i][m] with logits vals[i][m].
 
     Each candidate slot whose id occurs in H_i is penalised with that id's
-    count.  Used for the draft's re-scored candidates, which get the same
-    H_i as the target row.  Returns a copy of vals.
+    count; tokens of H_i outside [0, vocab) are ignored, as for dense rows,
+    so a slot holding such an id (an empty slot, for instance) is never
+    penalised.  Used for the draft's re-scored candidates, which get the
+    same H_i as the target row.  Returns a copy of vals.
     """
     out = np.array(vals, dtype=np.float32, copy=True)
     for i in range(out.shape[0]):
-        counts = Counter(history(ctx, drafts, i, window))
+        counts = Counter(t for t in history(ctx, drafts, i, window) if 0 <= t < vocab)
         for m in range(out.shape[1]):
             c = counts.get(int(ids[i, m]), 0)
             if c >= 1:
@@ -118,11 +121,12 @@ def penalize_tree_dense(logits, ctx, tokens, parent, window: int, repeat: float,
 
 
 def penalize_tree_sparse(ids, vals, ctx, tokens, parent, window: int, repeat: float,
-                         presence: float, frequency: float) -> np.ndarray:
-    """Candidate lists per tree row, penalised with tree_history(r).  Returns a copy of vals."""
+                         presence: float, frequency: float, *, vocab: int) -> np.ndarray:
+    """Candidate lists per tree row, penalised with tree_history(r) (its
+    tokens outside [0, vocab) ignored).  Returns a copy of vals."""
     out = np.array(vals, dtype=np.float32, copy=True)
     for r in range(out.shape[0]):
-        counts = Counter(tree_history(ctx, tokens, parent, r, window))
+        counts = Counter(t for t in tree_history(ctx, tokens, parent, r, window) if 0 <= t < vocab)
         for m in range(out.shape[1]):
             c = counts.get(int(ids[r, m]), 0)
             if c >= 1:

@@ -21,14 +21,15 @@ from .policy import POOL, draw, policy_row
 from .topk import topk_rows
 
 
-def draft_chain(q_ids, q_vals, ctx, u_draft, *, window, repeat, presence, frequency,
+def draft_chain(q_ids, q_vals, ctx, u_draft, *, vocab, window, repeat, presence, frequency,
                 temperature, top_k, top_p, min_p):
     """Draw d_0..d_{k-1}; d_i ~ q_i, with q_i penalised by H_i (which holds d_0..d_{i-1})."""
     k = q_ids.shape[0]
     drafts = np.zeros(k, dtype=np.int32)
     for i in range(k):
         # row i of the candidates is penalised by H_i = ctx || drafts[:i]
-        pen = penalize_sparse(q_ids, q_vals, ctx, drafts[:i], window, repeat, presence, frequency)[i]
+        pen = penalize_sparse(q_ids, q_vals, ctx, drafts[:i], window, repeat, presence, frequency,
+                              vocab=vocab)[i]
         ids, probs = policy_row(pen, q_ids[i], temperature, top_k, top_p, min_p)
         drafts[i] = ids[draw(probs, u_draft[i])]
     return drafts
@@ -50,7 +51,8 @@ def acceptance_stage(target_logits, ctx, drafts, u, *, q_ids=None, q_vals=None, 
     if float(np.float32(temperature)) <= 0.0:
         out["tokens"] = accept_greedy_chain(pool_ids[:, 0], drafts)
         return out
-    q_pen = penalize_sparse(q_ids, q_vals, ctx, drafts, window, repeat, presence, frequency)
+    q_pen = penalize_sparse(q_ids, q_vals, ctx, drafts, window, repeat, presence, frequency,
+                            vocab=target_logits.shape[1])
     q_rows = [policy_row(q_pen[i], q_ids[i], temperature, top_k, top_p, min_p) for i in range(k)]
     out["q_penalized"] = q_pen
     out["q_rows"] = q_rows

@@ -45,7 +45,7 @@ def test_draft_candidates_sparse():
     drafts = ids[:, 0].copy()
     t = dev(vals)
     vs.penalize_rows(t, dev(ctx), dev(drafts), window=64, ids=dev(ids), vocab=VOCAB, **P)
-    want = penalize_sparse(ids, vals, ctx, drafts, 64, **P)
+    want = penalize_sparse(ids, vals, ctx, drafts, 64, **P, vocab=VOCAB)
     assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))
 
 
@@ -119,5 +119,5 @@ def test_tree_rows_dense_and_sparse(case, window):
     vals = logits(1650 + case, (rows, 8))
     t = dev(vals)
     vs.penalize_tree_rows(t, dev(ctx), dev(tk), dev(par), window=window, ids=dev(ids), vocab=V, **P)
-    want = penalize_tree_sparse(ids, vals, ctx, tk, par, window, **P)
+    want = penalize_tree_sparse(ids, vals, ctx, tk, par, window, **P, vocab=V)
     assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))

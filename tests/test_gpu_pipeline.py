@@ -79,7 +79,7 @@ def window_inputs(y_ref, seed):
     ctx = penalty_history(seed, logits_ref.shape[1], 2048, 32, hot)
     q_ids, q_vals = draft_candidates(seed + 1, logits_ref[:k], 8)
     ud = uniforms(seed + 2, k)
-    drafts = draft_chain(q_ids, q_vals, ctx, ud, **PEN, **CFG)
+    drafts = draft_chain(q_ids, q_vals, ctx, ud, vocab=LM_HEAD_SHAPE[0], **PEN, **CFG)
     u = uniforms(seed + 3, (k + 1, 2))
     return logits_ref, ctx, q_ids, q_vals, drafts, u
 

@@ -104,9 +104,28 @@ def test_sparse_matches_dense_on_the_same_ids():
     dense = penalize_dense(logits, ctx, d, 16, 1.1, 1.5, 0.2)
     ids = np.stack([rng.permutation(V)[:8] for _ in range(4)]).astype(np.int32)
     vals = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
-    sparse = penalize_sparse(ids, vals, ctx, d, 16, 1.1, 1.5, 0.2)
+    sparse = penalize_sparse(ids, vals, ctx, d, 16, 1.1, 1.5, 0.2, vocab=V)
     assert np.array_equal(sparse, np.take_along_axis(dense, ids.astype(np.int64), axis=1))
 
+
+
+def test_sparse_ignores_ids_outside_the_vocabulary():
+    """History tokens outside [0, vocab) are ignored for sparse rows as for
+    dense ones, so slots holding such ids (empty slots are negative) keep
+    their logits even when the same id sits in the history."""
+    V = 12
+    ctx = np.array([-3, V + 2, 5, 5, -1, V], dtype=np.int32)
+    d = np.array([5], dtype=np.int32)
+    ids = np.array([[-3, V + 2, 5, 6, -1, V]] * 2, dtype=np.int32)
+    vals = np.array([[2.0, -1.0, 3.0, 4.0, 0.5, 1.5]] * 2, dtype=np.float32)
+    out = penalize_sparse(ids, vals, ctx, d, 16, 1.1, 1.5, 0.2, vocab=V)
+    keep = np.array([0, 1, 3, 4, 5])
+    assert np.array_equal(out[:, keep], vals[:, keep])
+    dense = np.zeros((2, V), dtype=np.float32)
+    dense[:, 5] = 3.0
+    want = penalize_dense(dense, ctx, d, 16, 1.1, 1.5, 0.2)[:, 5]
+    assert np.array_equal(out[:, 2], want)
+    assert out[0, 2] != out[1, 2]  # row 1 also sees the draft: count 3 against 2
 
 # ----------------------------------------------------------- token trees
 
@@ -151,5 +170,5 @@ def test_tree_penalties_equal_chain_penalties_on_a_chain():
                           penalize_dense(logits, ctx, drafts, *args))
     ids = g.integers(0, V, size=(k + 1, 8)).astype(np.int32)
     vals = logits[:, :8].copy()
-    assert np.array_equal(penalize_tree_sparse(ids, vals, ctx, drafts, parent, *args),
-                          penalize_sparse(ids, vals, ctx, drafts, *args))
+    assert np.array_equal(penalize_tree_sparse(ids, vals, ctx, drafts, parent, *args, vocab=V),
+                          penalize_sparse(ids, vals, ctx, drafts, *args, vocab=V))
