@@ -51,8 +51,12 @@ def test_draft_candidates_sparse():
 
 @pytest.mark.parametrize("ctx_len,n_drafts,window,rows", [
     (0, 3, 64, 4), (10, 3, 64, 4), (5000, 0, 4096, 2), (100, 5, 3, 7), (64, 2, 1, 3),
-    (300, 10, 200, 12)])
+    (300, 10, 200, 12), (600, 4, 128, 5), (600, 4, 129, 5), (3000, 7, 1000, 8),
+    (4090, 9, 4096, 10)])
 def test_windows_and_edges(ctx_len, n_drafts, window, rows):
+    """Dense and sparse rows.  Dense histories of up to 128 tokens are
+    scanned, longer ones sorted first (the threshold sits between the 128-
+    and 129-token windows)."""
     V = 3000
     g = np.random.default_rng(ctx_len + 7 * window + rows)
     x = logits(1605 + rows, (rows, V))
@@ -64,6 +68,32 @@ def test_windows_and_edges(ctx_len, n_drafts, window, rows):
     got = run_dense(x, ctx, drafts, window, **P)
     want = penalize_dense(x, ctx, drafts, window, **P)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # sparse: slots holding repeated, single, absent and out-of-range ids
+    ids = np.where(g.random((rows, 16)) < 0.5, g.integers(0, 40, (rows, 16)),
+                   g.integers(-3, V + 3, (rows, 16))).astype(np.int32)
+    vals = logits(1615 + rows, (rows, 16))
+    t = dev(vals)
+    vs.penalize_rows(t, dev(ctx), dev(drafts), window=window, ids=dev(ids), vocab=V, **P)
+    want = penalize_sparse(ids, vals, ctx, drafts, window, **P, vocab=V)
+    assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))
+
+
+def test_long_history_of_one_token():
+    """A 4096-token history of a single id: in dense rows one run covering
+    the sorted history, counted once; in sparse rows counted per slot."""
+    V = 1000
+    x = logits(1620, (4, V))
+    ctx = np.full(5000, 7, dtype=np.int32)
+    drafts = np.array([7, 8, 7], dtype=np.int32)
+    got = run_dense(x, ctx, drafts, 4096, **P)
+    want = penalize_dense(x, ctx, drafts, 4096, **P)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    ids = np.tile(np.array([7, 8, 9, 7], dtype=np.int32), (4, 1))
+    vals = logits(1621, (4, 4))
+    t = dev(vals)
+    vs.penalize_rows(t, dev(ctx), dev(drafts), window=4096, ids=dev(ids), vocab=V, **P)
+    want = penalize_sparse(ids, vals, ctx, drafts, 4096, **P, vocab=V)
+    assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))
 
 
 def test_window_zero_and_neutral_are_noops():

@@ -11,9 +11,14 @@
 //
 // One workgroup per row.  The row's history (<= VS_MAX_WINDOW ids) is staged
 // in LDS; each thread owns history positions (dense mode) or candidate slots
-// (sparse mode) and counts occurrences by scanning the history.  In dense
-// mode only the first occurrence of a token applies its penalty, so distinct
-// threads write distinct logits.  The arithmetic is fp32, one rounding per
+// (sparse mode).  A slot counts its id over the history.  In dense mode a
+// short history is scanned: a position applies its token's penalty if it
+// is the token's first occurrence, with the count of the positions after
+// it (quadratic in the history length); a longer one is first sorted in LDS
+// (bitonic), so that a token's occurrences form one run, and the first
+// position of a run applies the penalty with the run's length.  The counts
+// are the same either way, and each distinct token is written by exactly
+// one thread.  The arithmetic is fp32, one rounding per
 // operation, in the documented order (the library is built without
 // floating-point contraction and with a correctly rounded divide).
 
@@ -22,6 +27,7 @@
 namespace {
 
 constexpr int THREADS = 256;
+constexpr int SORT_MIN = 128;  // longer histories of dense rows are sorted before counting
 
 __device__ __forceinline__ float penalize_one(float l, int c, float rep, float pres, float freq) {
   const float l1 = (l > 0.f) ? (l / rep) : (l * rep);
@@ -78,16 +84,50 @@ penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int
   }
   __syncthreads();
 
+  // dense rows, long histories: ascending sort of hist[0, n), n the next
+  // power of two >= hlen (<= VS_MAX_WINDOW), padded with INT32_MAX, which no
+  // id below vocab <= 2^31 - 1 equals; the pads sort after every id
+  const bool sorted = ids == nullptr && hlen > SORT_MIN;  // uniform across the workgroup
+  if (sorted) {
+    int n = 1;
+    while (n < hlen) n <<= 1;
+    for (int j = hlen + threadIdx.x; j < n; j += blockDim.x) hist[j] = 0x7fffffff;
+    __syncthreads();
+    for (int k = 2; k <= n; k <<= 1)
+      for (int s = k >> 1; s > 0; s >>= 1) {
+        // each pair (i, i ^ s) is handled by its lower index alone
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+          const int q = i ^ s;
+          if (q > i) {
+            const int32_t a = hist[i], b = hist[q];
+            if ((a > b) == ((i & k) == 0)) {
+              hist[i] = b;
+              hist[q] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  }
+
   float* lrow = logits + static_cast<int64_t>(row) * ld;
   if (ids == nullptr) {
     for (int j = threadIdx.x; j < hlen; j += blockDim.x) {
       const int32_t t = hist[j];
       if (t < 0) continue;
-      bool first = true;
-      for (int i = 0; i < j && first; ++i) first = hist[i] != t;
-      if (!first) continue;
-      int c = 1;
-      for (int i = j + 1; i < hlen; ++i) c += hist[i] == t;
+      int c;
+      if (sorted) {
+        if (j > 0 && hist[j - 1] == t) continue;  // not the first of its run
+        int e = j + 1;
+        while (e < hlen && hist[e] == t) ++e;
+        c = e - j;
+      } else {
+        bool first = true;
+        for (int i = 0; i < j && first; ++i) first = hist[i] != t;
+        if (!first) continue;
+        c = 1;
+        for (int i = j + 1; i < hlen; ++i) c += hist[i] == t;
+      }
       lrow[t] = penalize_one(lrow[t], c, rep, pres, freq);
     }
   } else {
