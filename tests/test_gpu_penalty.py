@@ -151,3 +151,21 @@ def test_tree_rows_dense_and_sparse(case, window):
     vs.penalize_tree_rows(t, dev(ctx), dev(tk), dev(par), window=window, ids=dev(ids), vocab=V, **P)
     want = penalize_tree_sparse(ids, vals, ctx, tk, par, window, **P, vocab=V)
     assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32))
+
+
+def test_sparse_rows_wider_than_one_chunk():
+    """300 candidate slots per row: two chunks of slots (256, then 44), each
+    slot's count split over several threads."""
+    V = 2000
+    g = np.random.default_rng(1625)
+    ctx = g.integers(0, V, 3000).astype(np.int32)
+    ctx[::2] = g.integers(0, 30, len(ctx[::2]))
+    drafts = g.integers(0, 30, 4).astype(np.int32)
+    ids = np.where(g.random((5, 300)) < 0.5, g.integers(0, 30, (5, 300)),
+                   g.integers(-2, V + 2, (5, 300))).astype(np.int32)
+    vals = logits(1626, (5, 300))
+    for window in (64, 1000):
+        t = dev(vals)
+        vs.penalize_rows(t, dev(ctx), dev(drafts), window=window, ids=dev(ids), vocab=V, **P)
+        want = penalize_sparse(ids, vals, ctx, drafts, window, **P, vocab=V)
+        assert np.array_equal(host(t).view(np.uint32), want.view(np.uint32)), window

@@ -11,7 +11,10 @@
 //
 // One workgroup per row.  The row's history (<= VS_MAX_WINDOW ids) is staged
 // in LDS; each thread owns history positions (dense mode) or candidate slots
-// (sparse mode).  A slot counts its id over the history.  In dense mode a
+// (sparse mode).  In sparse mode the slots are taken up to 256 at a time,
+// each by 256 / (slots in the chunk) threads that count its id over
+// interleaved shares of the history; the shares' counts are added in LDS.
+// In dense mode a
 // short history is scanned: a position applies its token's penalty if it
 // is the token's first occurrence, with the count of the positions after
 // it (quadratic in the history length); a longer one is first sorted in LDS
@@ -131,13 +134,27 @@ penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int
       lrow[t] = penalize_one(lrow[t], c, rep, pres, freq);
     }
   } else {
+    __shared__ int part[THREADS];  // per-thread counts of the current chunk
     const int32_t* irow = ids + static_cast<int64_t>(row) * ld;
-    for (int m = threadIdx.x; m < width; m += blockDim.x) {
-      const int32_t t = irow[m];
-      if (t < 0 || t >= vocab) continue;
+    for (int base = 0; base < width; base += THREADS) {  // uniform trip count
+      const int nslot = width - base < THREADS ? width - base : THREADS;
+      const int tps = THREADS / nslot;  // threads per slot; nslot * tps <= THREADS
+      const int slot = threadIdx.x / tps;
       int c = 0;
-      for (int i = 0; i < hlen; ++i) c += hist[i] == t;
-      if (c > 0) lrow[m] = penalize_one(lrow[m], c, rep, pres, freq);
+      if (slot < nslot) {
+        const int32_t t = irow[base + slot];
+        if (t >= 0 && t < vocab)
+          for (int i = threadIdx.x % tps; i < hlen; i += tps) c += hist[i] == t;
+      }
+      part[threadIdx.x] = c;
+      __syncthreads();
+      if (threadIdx.x < nslot) {
+        int total = 0;
+        for (int j = 0; j < tps; ++j) total += part[threadIdx.x * tps + j];
+        float* l = lrow + base + threadIdx.x;
+        if (total > 0) *l = penalize_one(*l, total, rep, pres, freq);
+      }
+      __syncthreads();  // part is reused by the next chunk
     }
   }
 }
