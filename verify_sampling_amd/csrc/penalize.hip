@@ -17,11 +17,10 @@
 // In dense mode a
 // short history is scanned: a position applies its token's penalty if it
 // is the token's first occurrence, with the count of the positions after
-// it (quadratic in the history length); a longer one is first sorted in LDS
-// (bitonic), so that a token's occurrences form one run, and the first
-// position of a run applies the penalty with the run's length.  The counts
-// are the same either way, and each distinct token is written by exactly
-// one thread.  The arithmetic is fp32, one rounding per
+// it (quadratic in the history length); a longer one is counted in an LDS
+// hash table (open addressing, linear probing, integer atomic counts), whose
+// slots then apply one penalty per distinct token.  The counts are the same
+// either way, and each distinct token is written by exactly one thread.  The arithmetic is fp32, one rounding per
 // operation, in the documented order (the library is built without
 // floating-point contraction and with a correctly rounded divide).
 
@@ -30,7 +29,11 @@
 namespace {
 
 constexpr int THREADS = 256;
-constexpr int SORT_MIN = 128;  // longer histories of dense rows are sorted before counting
+constexpr int HASH_MIN = 128;  // longer histories of dense rows are counted in a hash table
+constexpr int TABLE_BITS = 13;
+constexpr int TABLE = 1 << TABLE_BITS;  // hash slots: at least twice the longest history
+static_assert(TABLE >= 2 * VS_MAX_WINDOW, "the table never fills");
+constexpr size_t TABLE_BYTES = 2 * TABLE * sizeof(int32_t);  // keys, then counts
 
 __device__ __forceinline__ float penalize_one(float l, int c, float rep, float pres, float freq) {
   const float l1 = (l > 0.f) ? (l / rep) : (l * rep);
@@ -46,6 +49,7 @@ penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int
                 bool tree, const int32_t* __restrict__ parent, int window, float rep,
                 float pres, float freq) {
   __shared__ int32_t hist[VS_MAX_WINDOW];
+  extern __shared__ int32_t table[];  // TABLE_BYTES when a dense row's history may exceed HASH_MIN
   __shared__ int32_t path[VS_MAX_DRAFTS + 1];
   __shared__ int path_len;
   const int row = blockIdx.x;
@@ -87,50 +91,43 @@ penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int
   }
   __syncthreads();
 
-  // dense rows, long histories: ascending sort of hist[0, n), n the next
-  // power of two >= hlen (<= VS_MAX_WINDOW), padded with INT32_MAX, which no
-  // id below vocab <= 2^31 - 1 equals; the pads sort after every id
-  const bool sorted = ids == nullptr && hlen > SORT_MIN;  // uniform across the workgroup
-  if (sorted) {
-    int n = 1;
-    while (n < hlen) n <<= 1;
-    for (int j = hlen + threadIdx.x; j < n; j += blockDim.x) hist[j] = 0x7fffffff;
-    __syncthreads();
-    for (int k = 2; k <= n; k <<= 1)
-      for (int s = k >> 1; s > 0; s >>= 1) {
-        // each pair (i, i ^ s) is handled by its lower index alone
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-          const int q = i ^ s;
-          if (q > i) {
-            const int32_t a = hist[i], b = hist[q];
-            if ((a > b) == ((i & k) == 0)) {
-              hist[i] = b;
-              hist[q] = a;
-            }
-          }
-        }
-        __syncthreads();
-      }
-  }
-
   float* lrow = logits + static_cast<int64_t>(row) * ld;
+  if (ids == nullptr && hlen > HASH_MIN) {  // uniform; the launch provides the table
+    int32_t* key = table;
+    int32_t* cnt = table + TABLE;
+    for (int q = threadIdx.x; q < TABLE; q += blockDim.x) {
+      key[q] = -1;
+      cnt[q] = 0;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < hlen; j += blockDim.x) {
+      const int32_t t = hist[j];
+      if (t < 0) continue;
+      uint32_t q = (static_cast<uint32_t>(t) * 2654435761u) >> (32 - TABLE_BITS);
+      // at most hlen <= TABLE / 2 distinct keys: an empty slot is always found
+      for (;;) {
+        const int32_t prev = atomicCAS(&key[q], -1, t);
+        if (prev == -1 || prev == t) break;
+        q = (q + 1) & (TABLE - 1);
+      }
+      atomicAdd(&cnt[q], 1);
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < TABLE; q += blockDim.x) {
+      const int32_t t = key[q];
+      if (t >= 0) lrow[t] = penalize_one(lrow[t], cnt[q], rep, pres, freq);
+    }
+    return;
+  }
   if (ids == nullptr) {
     for (int j = threadIdx.x; j < hlen; j += blockDim.x) {
       const int32_t t = hist[j];
       if (t < 0) continue;
-      int c;
-      if (sorted) {
-        if (j > 0 && hist[j - 1] == t) continue;  // not the first of its run
-        int e = j + 1;
-        while (e < hlen && hist[e] == t) ++e;
-        c = e - j;
-      } else {
-        bool first = true;
-        for (int i = 0; i < j && first; ++i) first = hist[i] != t;
-        if (!first) continue;
-        c = 1;
-        for (int i = j + 1; i < hlen; ++i) c += hist[i] == t;
-      }
+      bool first = true;
+      for (int i = 0; i < j && first; ++i) first = hist[i] != t;
+      if (!first) continue;
+      int c = 1;
+      for (int i = j + 1; i < hlen; ++i) c += hist[i] == t;
       lrow[t] = penalize_one(lrow[t], c, rep, pres, freq);
     }
   } else {
@@ -175,10 +172,15 @@ extern "C" int penalize_rows(float* logits, const int32_t* ids, int64_t ld, int 
       !__builtin_isfinite(frequency))
     return VS_ERR_PARAM;
   if (window == 0 || (ctx_len == 0 && n_drafts == 0)) return VS_OK;  // nothing to penalise
-  penalize_kernel<<<dim3(rows), dim3(THREADS), 0, stream>>>(logits, ids, ld, width, vocab, ctx,
-                                                            ctx_len, drafts, n_drafts, false,
-                                                            nullptr, window, repeat, presence,
-                                                            frequency);
+  // no row's history is longer than min(window, ctx_len + n_drafts)
+  const size_t shm = ids == nullptr && window > HASH_MIN &&
+                             static_cast<int64_t>(ctx_len) + n_drafts > HASH_MIN
+                         ? TABLE_BYTES
+                         : 0;
+  penalize_kernel<<<dim3(rows), dim3(THREADS), shm, stream>>>(logits, ids, ld, width, vocab, ctx,
+                                                              ctx_len, drafts, n_drafts, false,
+                                                              nullptr, window, repeat, presence,
+                                                              frequency);
   return vs::check_launch();
 }
 
@@ -197,7 +199,12 @@ extern "C" int penalize_tree_rows(float* logits, const int32_t* ids, int64_t ld,
       !__builtin_isfinite(frequency))
     return VS_ERR_PARAM;
   if (window == 0 || (ctx_len == 0 && n_nodes == 0)) return VS_OK;  // nothing to penalise
-  penalize_kernel<<<dim3(n_nodes + 1), dim3(THREADS), 0, stream>>>(
+  // a node's path holds at most n_nodes tokens
+  const size_t shm = ids == nullptr && window > HASH_MIN &&
+                             static_cast<int64_t>(ctx_len) + n_nodes > HASH_MIN
+                         ? TABLE_BYTES
+                         : 0;
+  penalize_kernel<<<dim3(n_nodes + 1), dim3(THREADS), shm, stream>>>(
       logits, ids, ld, width, vocab, ctx, ctx_len, tokens, n_nodes, true, parent, window, repeat,
       presence, frequency);
   return vs::check_launch();
