@@ -55,8 +55,8 @@ def test_draft_candidates_sparse():
     (4090, 9, 4096, 10)])
 def test_windows_and_edges(ctx_len, n_drafts, window, rows):
     """Dense and sparse rows.  Dense histories of up to 128 tokens are
-    scanned, longer ones sorted first (the threshold sits between the 128-
-    and 129-token windows)."""
+    scanned, longer ones counted in a hash table (the threshold sits between
+    the 128- and 129-token windows)."""
     V = 3000
     g = np.random.default_rng(ctx_len + 7 * window + rows)
     x = logits(1605 + rows, (rows, V))
@@ -79,8 +79,8 @@ def test_windows_and_edges(ctx_len, n_drafts, window, rows):
 
 
 def test_long_history_of_one_token():
-    """A 4096-token history of a single id: in dense rows one run covering
-    the sorted history, counted once; in sparse rows counted per slot."""
+    """A 4096-token history of a single id: in dense rows one hash slot
+    takes every occurrence; in sparse rows counted per slot."""
     V = 1000
     x = logits(1620, (4, V))
     ctx = np.full(5000, 7, dtype=np.int32)
