@@ -279,6 +279,31 @@ def time_region(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def time_each(torch, fn, reps, warmup):
+    """Per-call times in ms (HIP events around each call on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of nbytes (torch copy_): GB/s counting bytes read plus written."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ms = float(np.median(time_each(torch, lambda: dst.copy_(src), reps, 2)))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "ms": round(ms, 4), "gbs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, warmup=1):
     """Batched acceptance stage, one set of rows per window (config: vocab 4096, k = 3)."""
     R = k + 1
@@ -411,30 +436,60 @@ def lookup_report(vs, synth, length=32768, calls=200):
             "mean_nodes": round(float(np.mean(sizes)), 2), "host": "one core"}
 
 
-def cpu_baseline(synth, R, budget_s=12.0):
-    """The oracle (as it stands) on a bounded sample of the same pass, on the host cores."""
+def host_cpu():
+    """(logical CPUs, model name) of this host."""
+    model = None
+    try:
+        import subprocess
+
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:  # pragma: no cover
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:  # pragma: no cover
+            pass
+    return os.cpu_count(), model
+
+
+def oracle_gemv_leg(synth, R, budget_s, threads):
+    """GB/s of the fp64 projection oracle over one fused layer, repeated for budget_s."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    shapes = list(synth.LAYER_SHAPES_FUSED.values())
+    mats = [synth.gemv_case(8000 + i, N, K, R) for i, (N, K) in enumerate(shapes)]
+    with threadpool_limits(limits=threads):
+        used = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        done_bytes, spent, calls = 0, 0.0, 0
+        while spent < budget_s:
+            for (N, K), (w, x) in zip(shapes, mats):
+                t0 = time.perf_counter()
+                oracle.gemv.gemv_rows(w, x)
+                spent += time.perf_counter() - t0
+                done_bytes += 2 * N * K + 4 * R * (K + N)
+                calls += 1
+    return {"gbs": done_bytes / spent / 1e9, "threads": int(used), "calls": calls,
+            "gb": done_bytes / 1e9, "seconds": spent}
+
+
+def cpu_baseline(synth, R, budget_s=8.0):
+    """The oracle (as it stands) on a bounded sample of the same pass, on the
+    host cores: the projection oracle with every core and with one thread,
+    and the acceptance-stage oracle on one window."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    shapes = list(synth.LAYER_SHAPES_FUSED.values())
-    # one fused layer's four projections, generated once and timed repeatedly
-    mats = [synth.gemv_case(8000 + i, N, K, R) for i, (N, K) in enumerate(shapes)]
-    done_bytes, spent, calls = 0, 0.0, 0
-    while spent < budget_s:
-        for (N, K), (w, x) in zip(shapes, mats):
-            t0 = time.perf_counter()
-            oracle.gemv.gemv_rows(w, x)
-            spent += time.perf_counter() - t0
-            done_bytes += 2 * N * K + 4 * R * (K + N)
-            calls += 1
-    layer = calls // len(shapes)
-    mats_n = calls
-    gbs = done_bytes / spent / 1e9
-    # the acceptance stage of one window over the LM-head vocabulary
+    ncpu, model = host_cpu()
+    allc = oracle_gemv_leg(synth, R, budget_s, ncpu)
+    one = oracle_gemv_leg(synth, R, budget_s, 1)
     V = synth.VOCAB
     lg = synth.logits(8100, (R, V))
     hot = np.unique(np.argsort(-lg, axis=1)[:, :64])
@@ -445,14 +500,18 @@ def cpu_baseline(synth, R, budget_s=12.0):
     t0 = time.perf_counter()
     oracle.pipeline.acceptance_stage(lg, ctx, drafts, u, q_ids=q_ids, q_vals=q_vals, **PEN, **CFG)
     acc_s = time.perf_counter() - t0
-    return {"value": gbs, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": allc["gbs"], "unit": "GB/s", "cores": allc["threads"], "kind": "oracle",
             "sample": f"fp64 projection oracle on one fused 8B-class layer (qkv, o, gate|up, "
-                      f"down) repeated {layer} times ({mats_n} calls, {done_bytes / 1e9:.2f} GB of "
-                      f"bf16 weights streamed, R={R}); "
-                      f"acceptance-stage oracle on one window (R={R}, vocab {V}): "
-                      f"{acc_s * 1e3:.0f} ms",
-            "seconds": spent + acc_s,
-            "accept_window_ms": acc_s * 1e3}
+                      f"down), repeated for ~{budget_s:.0f} s per leg ({allc['calls']} calls, "
+                      f"{allc['gb']:.2f} GB of bf16 weights with every core; {one['calls']} calls, "
+                      f"{one['gb']:.2f} GB on one thread; R={R}); acceptance-stage oracle on one "
+                      f"window (R={R}, vocab {V}, single-threaded Python): {acc_s * 1e3:.0f} ms",
+            "host_logical_cpus": ncpu,
+            "host_cpu_model": model,
+            "single_thread": {"value": one["gbs"], "unit": "GB/s", "threads": one["threads"]},
+            "seconds": allc["seconds"] + one["seconds"] + acc_s,
+            "accept_window_ms": acc_s * 1e3,
+            "accept_rows_per_s": R / acc_s}
 
 
 def main():
@@ -508,16 +567,20 @@ def main():
     bytes_per_launch = step_bytes / vp.n_launches()
     achieved = bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
 
-    sweep = {}
+    sweep, spread = {}, {}
     if not args.no_sweep:
         for r in range(1, 25):
-            sweep[r] = time_region(torch, lambda: vp.projections(r), max(3, args.steps // 4), 1)
+            ts = time_each(torch, lambda: vp.projections(r), max(10, args.steps // 2), 2)
+            sweep[r] = float(np.median(ts))
+            spread[r] = (float(np.min(ts)), float(np.max(ts)), len(ts))
         log("sweep done")
     knee = None
     if sweep:
         t1 = sweep[1]
         knee = next((r for r in sorted(sweep) if sweep[r] > 1.1 * t1), None)
 
+    copy = copy_bandwidth(torch, dev)
+    log(f"device copy: {copy['gbs_read_plus_write']} GB/s (read + write)")
     sampling = None if args.no_sampling else sampling_batch(torch, vs, synth, dev)
     if sampling:
         log(f"sampling: {sampling['rows_per_s']:.3e} rows/s")
@@ -559,19 +622,33 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
+            "frac_of_measured_copy": achieved / copy["gbs_read_plus_write"],
             "traffic": measured_traffic(R),
             "launches_per_pass": vp.n_launches(),
             "avg_launch_us": per_launch_ms * 1e3,
         },
         "ms_projections": ms_proj,
         "ms_acceptance": ms_accept,
-        "verify_tokens_per_s": R / (ms_step * 1e-3),
+        "verify_rows_per_s": R / (ms_step * 1e-3),
+        "emitted_tokens_per_s": (sampling["mean_emitted_per_window"] / (ms_step * 1e-3)
+                                 if sampling else None),
+        "emitted_tokens_note": "verify windows per second times the mean tokens emitted per window "
+                               "of the batched sampling stage (synthetic q with correlation 0.9 "
+                               "to p; no trained draft model)",
+        "device_copy": copy,
+        "sweep_timing": "median of per-pass HIP-event times, "
+                        f"{max(10, args.steps // 2)} passes after 2 warm-ups per R",
         "ms_per_pass_vs_R": {str(r): round(v, 4) for r, v in sweep.items()},
+        "ms_per_pass_min_max_vs_R": {str(r): [round(a, 4), round(b, 4)]
+                                     for r, (a, b, _) in spread.items()},
         "gbs_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9, 1)
                      for r, v in sweep.items()},
         "frac_of_hbm_peak_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                                   for r, v in sweep.items()},
-        "verify_tokens_per_s_vs_R": {str(r): round(r / (v * 1e-3), 1) for r, v in sweep.items()},
+        "frac_of_measured_copy_vs_R": {
+            str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9 / copy["gbs_read_plus_write"], 4)
+            for r, v in sweep.items()},
+        "verify_rows_per_s_vs_R": {str(r): round(r / (v * 1e-3), 1) for r, v in sweep.items()},
         "knee_R": knee,
         "depth_chooser": depth_report(vs, sweep) if sweep else None,
         "prompt_lookup_drafter": lookup_report(vs, synth),

@@ -227,7 +227,9 @@ def test_prompt_lookup_trees_greedy_walk():
     the context really does next: the root row and every node whose path is
     a prefix of the true continuation predict its next token, other rows a
     token of their own.  Trees shorter than 24 nodes are padded with nodes
-    that never agree (token -2).  GPU tokens equal the oracle's."""
+    that never agree (token -2).  Every drafted tree equals the oracle
+    drafter's (oracle.lookup) and the GPU tokens equal the oracle's."""
+    from oracle.lookup import lookup_tree
     from synth import lookup_context
 
     ctx = lookup_context(1870, 40000)
@@ -240,6 +242,8 @@ def test_prompt_lookup_trees_greedy_walk():
     for b in range(B):
         e = int(g.integers(1000, len(ctx) - 16))
         tk, par = vs.lookup_tree(ctx[:e], 3, 3, 8, K)
+        want_t, want_p = lookup_tree(list(ctx[:e]), 3, 3, 8, K)
+        assert list(tk) == want_t and list(par) == want_p, b
         truth = ctx[e:e + 10]
         sizes.append(len(tk))
         tokens[b, :len(tk)], parents[b, :len(tk)] = tk, par

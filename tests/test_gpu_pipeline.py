@@ -9,6 +9,16 @@ agree exactly, except at near-ties, which are listed:
   * pool order: two candidates whose oracle logits differ by <= 4 * delta;
   * policy and acceptance: a threshold or cumulative boundary within
     1e-5 of the decision.
+A window whose decisions sit at such a near-tie is listed in the test's
+output and is then checked stage by stage instead (below); nothing is
+skipped.
+
+The stage-isolated test feeds every oracle stage the GPU's own output of
+the stage before it (the downloaded projection, penalised rows, pools and
+distributions), so each stage must match exactly: penalised rows and pools
+bit for bit, policy ids and lengths exactly with probabilities within 1
+fp32 ulp, tokens exactly, with no near-tie exception.
+
 Penalties follow section 04 of "Speculative decoding on RDNA", the policy
 section 03 ("how hipfire does it"), acceptance sections 01-03.
 """
@@ -18,9 +28,13 @@ import pytest
 import torch
 
 import verify_sampling_amd as vs
-from gpu_common import host
+from gpu_common import host, ulp_diff_f32
+from oracle.accept import accept_greedy_chain, accept_sampled
 from oracle.gemv import gemv_rows
+from oracle.penalty import penalize_dense, penalize_sparse
 from oracle.pipeline import acceptance_stage, draft_chain
+from oracle.policy import policy_row
+from oracle.topk import topk_rows as oracle_topk_rows
 from synth import LM_HEAD_SHAPE, draft_candidates, penalty_history, torch_bf16_weights, uniforms
 
 pytestmark = pytest.mark.gpu
@@ -56,7 +70,8 @@ def gpu_window(W, x, ctx, drafts, q_ids, q_vals, u, cfg):
     mode = vs.ACCEPT_SAMPLED if cfg["temperature"] > 0 else vs.ACCEPT_GREEDY
     tok, n = vs.spec_accept_rows(mode, D[None, :], p[:3], q[:3], u=U)
     return dict(logits=host(logits), penalized=host(L), pool_ids=host(pi), pool_vals=host(pv),
-                p=[host(t) for t in p[:3]], tokens=list(host(tok)[0, :int(host(n)[0])]))
+                p=[host(t) for t in p[:3]], q=[host(t) for t in q[:3]], q_penalized=host(QV),
+                tokens=list(host(tok)[0, :int(host(n)[0])]))
 
 
 def pool_near_ties(o_vals, o_ids, g_ids, tol):
@@ -98,7 +113,9 @@ def test_lm_head_window_end_to_end(lm_head, seed, temperature):
     ties = pool_near_ties(want["pool_vals"], want["pool_ids"], got["pool_ids"], 4 * delta + 1e-7)
     print(f"seed {seed}: projection delta {delta:.3g}; pool near-ties {ties}")
     if ties:
-        pytest.skip(f"pool differs only at listed near-ties {ties}")
+        # listed above; the GPU's own rows then go through the oracle stage by stage
+        check_stages(got, ctx, drafts, q_ids, q_vals, u, cfg)
+        return
     # policy over identical pools: ids and lengths exact, probabilities close
     g_ids, g_probs, g_len = got["p"]
     for i, (oi, op) in enumerate(want["p_rows"]):
@@ -109,8 +126,60 @@ def test_lm_head_window_end_to_end(lm_head, seed, temperature):
         # only a decision within 1e-5 of its boundary may differ
         m = decision_margin(want, drafts, u, temperature)
         assert m <= 1e-5, f"tokens differ: gpu {got['tokens']} oracle {want['tokens']}, margin {m}"
-        pytest.skip(f"tokens differ at a listed near-tie (margin {m:.3g})")
+        print(f"seed {seed}: tokens differ at a near-tie (margin {m:.3g}): gpu {got['tokens']} "
+              f"oracle {want['tokens']}; checked stage by stage")
+        check_stages(got, ctx, drafts, q_ids, q_vals, u, cfg)
     assert 1 <= len(got["tokens"]) <= 4
+
+
+def check_stages(got, ctx, drafts, q_ids, q_vals, u, cfg):
+    """Every oracle stage fed the GPU's output of the stage before; exact."""
+    k = len(drafts)
+    vocab = got["logits"].shape[1]
+    # penalties on the GPU's own projection: bit for bit
+    pen = penalize_dense(got["logits"], ctx, drafts, **PEN)
+    assert np.array_equal(pen.view(np.uint32), got["penalized"].view(np.uint32))
+    q_pen = penalize_sparse(q_ids, q_vals, ctx, drafts, **PEN, vocab=vocab)
+    assert np.array_equal(q_pen.view(np.uint32), got["q_penalized"].view(np.uint32))
+    # the pool of the GPU's penalised rows: values and ids byte for byte
+    o_vals, o_ids = oracle_topk_rows(got["penalized"], 64)
+    assert np.array_equal(o_ids, got["pool_ids"])
+    assert np.array_equal(o_vals.view(np.uint32), got["pool_vals"].view(np.uint32))
+
+    def check_policy(rows_vals, rows_ids, dist, n_rows):
+        g_ids, g_probs, g_len = dist
+        for i in range(n_rows):
+            oi, op = policy_row(rows_vals[i], rows_ids[i], **cfg)
+            assert g_len[i] == len(oi), i
+            assert np.array_equal(g_ids[i, :len(oi)], oi), i
+            assert (ulp_diff_f32(g_probs[i, :len(oi)], op) <= 1).all(), i
+
+    check_policy(got["pool_vals"], got["pool_ids"], got["p"], k + 1)
+    check_policy(got["q_penalized"], q_ids, got["q"], k)
+
+    # acceptance on the GPU's own distributions: tokens exactly
+    def rows(dist, n_rows):
+        g_ids, g_probs, g_len = dist
+        return [(g_ids[i, :g_len[i]], g_probs[i, :g_len[i]]) for i in range(n_rows)]
+
+    if cfg["temperature"] > 0:
+        want = accept_sampled(rows(got["p"], k + 1), rows(got["q"], k), drafts, u)
+    else:
+        want = accept_greedy_chain(got["pool_ids"][:, 0], drafts)
+    assert got["tokens"] == want, (got["tokens"], want)
+
+
+@pytest.mark.parametrize("seed,temperature", [(1950, 0.7), (1960, 0.7), (1970, 0.7), (1980, 0.7),
+                                              (1990, 0.0), (2000, 1.0)])
+def test_lm_head_window_stage_isolated(lm_head, seed, temperature):
+    """[SD] §04: only the already-penalised row is downloaded, and the host
+    stages run on it.  Here the oracle's top-K, policy and acceptance run on
+    the GPU's downloaded rows and must agree exactly."""
+    W, x, y_ref, s = lm_head
+    logits_ref, ctx, q_ids, q_vals, drafts, u = window_inputs(y_ref, seed)
+    cfg = dict(CFG, temperature=temperature)
+    got = gpu_window(W, x, ctx, drafts, q_ids, q_vals, u, cfg)
+    check_stages(got, ctx, drafts, q_ids, q_vals, u, cfg)
 
 
 def decision_margin(want, drafts, u, temperature):

@@ -126,7 +126,8 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
-def _ptr(t, dtype, name, allow_none=False):
+def _ptr(t, dtype, name, allow_none=False, device=None):
+    """Device pointer of t after checking its type, dtype and device."""
     import torch
 
     if t is None:
@@ -139,6 +140,8 @@ def _ptr(t, dtype, name, allow_none=False):
         raise VerifySamplingError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise VerifySamplingError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise VerifySamplingError(f"{name} is on {t.device}, the call's tensors on {device}")
     return t.data_ptr()
 
 
@@ -147,6 +150,57 @@ def _ld(t, name):
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
         raise VerifySamplingError(f"{name} must be 2-D with contiguous rows")
     return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _mat(t, name, rows, cols, dtype, device, *, exact_rows=True):
+    """Checks a 2-D row-major operand of at least rows x cols (exactly `rows`
+    rows unless exact_rows is False) and returns (pointer, leading dimension)."""
+    ptr = _ptr(t, dtype, name, device=device)
+    ld = _ld(t, name)
+    r, c = t.shape
+    if (r != rows if exact_rows else r < rows) or c < cols:
+        want = f"[{rows}]" if exact_rows else f"[>= {rows}]"
+        raise VerifySamplingError(f"{name} must be {want}[>= {cols}], got {list(t.shape)}")
+    return ptr, ld
+
+
+def _vec(t, name, n, dtype, device, allow_none=False):
+    """Checks a contiguous tensor of at least n elements; returns its pointer."""
+    if t is None:
+        if allow_none:
+            return None
+        raise VerifySamplingError(f"{name} is required")
+    ptr = _ptr(t, dtype, name, device=device)
+    if not t.is_contiguous():
+        raise VerifySamplingError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise VerifySamplingError(f"{name} has {t.numel()} elements, needs {n}")
+    return ptr
+
+
+def _ids1d(t, name, dtype, device):
+    """(pointer or None, length) of an optional 1-D contiguous id array."""
+    if t is None or t.numel() == 0:
+        if t is not None:
+            _ptr(t, dtype, name, device=device)
+        return None, 0
+    if t.dim() != 1:
+        raise VerifySamplingError(f"{name} must be 1-D")
+    return _vec(t, name, t.numel(), dtype, device), int(t.numel())
+
+
+def _workspace(t, name, device):
+    """(pointer, bytes) of an optional uint8 workspace (1-D, contiguous)."""
+    if t is None:
+        return None, 0
+    ptr = _vec(t, name, 0, _torch().uint8, device)
+    return ptr, int(t.numel())
+
+
+def _torch():
+    import torch
+
+    return torch
 
 
 def verify_gemv_rows_workspace_bytes(N: int, K: int, R: int) -> int:
@@ -164,31 +218,55 @@ def verify_gemv_rows(W, X, Y=None, stream=None, workspace="auto"):
     """
     import torch
 
+    if not isinstance(W, torch.Tensor) or not isinstance(X, torch.Tensor):
+        raise VerifySamplingError("W and X must be torch tensors")
     if W.dtype in (torch.int16, torch.uint16):
         W = W.view(torch.bfloat16)
-    if W.dtype != torch.bfloat16:
-        raise VerifySamplingError("W must be bfloat16")
+    if W.dim() != 2 or X.dim() != 2:
+        raise VerifySamplingError("W and X must be 2-D")
     N, K = W.shape
     R = X.shape[0]
-    if X.dim() != 2 or X.shape[1] != K:
-        raise VerifySamplingError(f"X must be [R][{K}]")
+    dev = X.device
+    w_ptr, ldw = _mat(W, "W", N, K, torch.bfloat16, dev)
+    x_ptr, ldx = _mat(X, "X", R, K, torch.float32, dev)
+    if X.shape[1] != K:
+        raise VerifySamplingError(f"X must be [R][{K}], got {list(X.shape)}")
     if Y is None:
-        Y = torch.empty((R, N), dtype=torch.float32, device=X.device)
-    if tuple(Y.shape) != (R, N):
-        raise VerifySamplingError(f"Y must be [{R}][{N}]")
+        Y = torch.empty((R, N), dtype=torch.float32, device=dev)
+    y_ptr, ldy = _mat(Y, "Y", R, N, torch.float32, dev)
+    if Y.shape[1] != N:
+        raise VerifySamplingError(f"Y must be [{R}][{N}], got {list(Y.shape)}")
     if isinstance(workspace, str):
         if workspace != "auto":
             raise VerifySamplingError('workspace must be "auto", None or a uint8 tensor')
         nbytes = verify_gemv_rows_workspace_bytes(N, K, R)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device) if nbytes else None
-    ws_ptr = _ptr(workspace, torch.uint8, "workspace", allow_none=True)
-    ws_bytes = workspace.numel() if workspace is not None else 0
-    st = library().verify_gemv_rows(_ptr(W, torch.bfloat16, "W"), _ld(W, "W"), N, K,
-                                    _ptr(X, torch.float32, "X"), _ld(X, "X"), R,
-                                    _ptr(Y, torch.float32, "Y"), _ld(Y, "Y"), ws_ptr, ws_bytes,
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    ws_ptr, ws_bytes = _workspace(workspace, "workspace", dev)
+    st = library().verify_gemv_rows(w_ptr, ldw, N, K, x_ptr, ldx, R, y_ptr, ldy, ws_ptr, ws_bytes,
                                     _stream(stream))
     _check(st, "verify_gemv_rows")
     return Y
+
+
+def _logit_rows(logits, ids, vocab):
+    """(logits ptr, ids ptr or None, ld, rows, width, vocab) of a dense or sparse call."""
+    import torch
+
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise VerifySamplingError("logits must be a 2-D torch tensor")
+    rows, width = logits.shape
+    dev = logits.device
+    l_ptr, ld = _mat(logits, "logits", rows, width, torch.float32, dev)
+    i_ptr = None
+    if ids is None:
+        vocab = width if vocab is None else vocab
+    else:
+        if vocab is None:
+            raise VerifySamplingError("vocab is required in sparse mode")
+        i_ptr, _ = _mat(ids, "ids", rows, width, torch.int32, dev)
+        if tuple(ids.shape) != (rows, width) or ids.stride() != logits.stride():
+            raise VerifySamplingError("ids must match logits in shape and strides")
+    return l_ptr, i_ptr, ld, rows, width, int(vocab)
 
 
 def penalize_rows(logits, ctx, drafts, *, window, repeat, presence, frequency, vocab=None,
@@ -197,25 +275,17 @@ def penalize_rows(logits, ctx, drafts, *, window, repeat, presence, frequency, v
 
     Dense: logits float32 [rows][V] (vocab defaults to V).  Sparse: `ids`
     int32 [rows][M] and logits [rows][M] candidate slots, `vocab` required.
-    ctx, drafts: int32 1-D device tensors (may be empty).
+    ctx, drafts: int32 1-D contiguous device tensors (may be empty or None).
     """
     import torch
 
-    rows, width = logits.shape
-    if ids is None:
-        vocab = width if vocab is None else vocab
-    elif vocab is None:
-        raise VerifySamplingError("vocab is required in sparse mode")
-    if ids is not None and (tuple(ids.shape) != (rows, width) or ids.stride() != logits.stride()):
-        raise VerifySamplingError("ids must match logits in shape and strides")
-    n_ctx = int(ctx.numel()) if ctx is not None else 0
-    n_d = int(drafts.numel()) if drafts is not None else 0
-    st = library().penalize_rows(
-        _ptr(logits, torch.float32, "logits"), _ptr(ids, torch.int32, "ids", True),
-        _ld(logits, "logits"), rows, width, int(vocab),
-        _ptr(ctx, torch.int32, "ctx", True) if n_ctx else None, n_ctx,
-        _ptr(drafts, torch.int32, "drafts", True) if n_d else None, n_d,
-        int(window), float(repeat), float(presence), float(frequency), _stream(stream))
+    l_ptr, i_ptr, ld, rows, width, vocab = _logit_rows(logits, ids, vocab)
+    dev = logits.device
+    c_ptr, n_ctx = _ids1d(ctx, "ctx", torch.int32, dev)
+    d_ptr, n_d = _ids1d(drafts, "drafts", torch.int32, dev)
+    st = library().penalize_rows(l_ptr, i_ptr, ld, rows, width, vocab, c_ptr, n_ctx, d_ptr, n_d,
+                                 int(window), float(repeat), float(presence), float(frequency),
+                                 _stream(stream))
     _check(st, "penalize_rows")
     return logits
 
@@ -226,29 +296,23 @@ def penalize_tree_rows(logits, ctx, tokens, parent, *, window, repeat, presence,
 
     Row 0 (root) uses the last `window` of ctx; row 1 + j (node j) the last
     `window` of ctx || the path from the root down to node j.  tokens,
-    parent: int32 [n_nodes] device tensors (parent -1 = root).  Dense or
-    sparse as penalize_rows.
+    parent: int32 [n_nodes] 1-D contiguous device tensors (parent -1 =
+    root).  Dense or sparse as penalize_rows.
     """
     import torch
 
-    rows, width = logits.shape
-    n_nodes = int(tokens.numel()) if tokens is not None else 0
+    l_ptr, i_ptr, ld, rows, width, vocab = _logit_rows(logits, ids, vocab)
+    dev = logits.device
+    t_ptr, n_nodes = _ids1d(tokens, "tokens", torch.int32, dev)
+    p_ptr, n_par = _ids1d(parent, "parent", torch.int32, dev)
+    if n_par != n_nodes:
+        raise VerifySamplingError(f"parent has {n_par} entries, tokens {n_nodes}")
     if rows != n_nodes + 1:
         raise VerifySamplingError(f"a tree of {n_nodes} nodes has {n_nodes + 1} rows, got {rows}")
-    if ids is None:
-        vocab = width if vocab is None else vocab
-    elif vocab is None:
-        raise VerifySamplingError("vocab is required in sparse mode")
-    if ids is not None and (tuple(ids.shape) != (rows, width) or ids.stride() != logits.stride()):
-        raise VerifySamplingError("ids must match logits in shape and strides")
-    n_ctx = int(ctx.numel()) if ctx is not None else 0
-    st = library().penalize_tree_rows(
-        _ptr(logits, torch.float32, "logits"), _ptr(ids, torch.int32, "ids", True),
-        _ld(logits, "logits"), width, int(vocab),
-        _ptr(ctx, torch.int32, "ctx", True) if n_ctx else None, n_ctx,
-        _ptr(tokens, torch.int32, "tokens", True) if n_nodes else None,
-        _ptr(parent, torch.int32, "parent", True) if n_nodes else None, n_nodes,
-        int(window), float(repeat), float(presence), float(frequency), _stream(stream))
+    c_ptr, n_ctx = _ids1d(ctx, "ctx", torch.int32, dev)
+    st = library().penalize_tree_rows(l_ptr, i_ptr, ld, width, vocab, c_ptr, n_ctx, t_ptr, p_ptr,
+                                      n_nodes, int(window), float(repeat), float(presence),
+                                      float(frequency), _stream(stream))
     _check(st, "penalize_tree_rows")
     return logits
 
@@ -258,25 +322,34 @@ def topk_rows_workspace_bytes(rows: int, V: int, K: int) -> int:
 
 
 def topk_rows(X, K, out_vals=None, out_idx=None, workspace=None, stream=None):
-    """Per-row top-K of float32 X [rows][V] in pool order -> (vals [rows][K], idx int32)."""
+    """Per-row top-K of float32 X [rows][V] in pool order -> (vals [rows][K], idx int32).
+
+    out_vals / out_idx: optional [rows][>= K] outputs with equal strides;
+    workspace: optional uint8 device tensor (allocated here when needed and
+    not given).
+    """
     import torch
 
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise VerifySamplingError("X must be a 2-D torch tensor")
     rows, V = X.shape
+    K = int(K)
+    dev = X.device
+    x_ptr, ldx = _mat(X, "X", rows, V, torch.float32, dev)
     if out_vals is None:
-        out_vals = torch.empty((rows, K), dtype=torch.float32, device=X.device)
+        out_vals = torch.empty((rows, K), dtype=torch.float32, device=dev)
     if out_idx is None:
-        out_idx = torch.empty((rows, K), dtype=torch.int32, device=X.device)
+        out_idx = torch.empty((rows, K), dtype=torch.int32, device=dev)
+    v_ptr, ld_out = _mat(out_vals, "out_vals", rows, K, torch.float32, dev)
+    o_ptr, _ = _mat(out_idx, "out_idx", rows, K, torch.int32, dev)
+    if out_vals.stride() != out_idx.stride() or out_vals.shape != out_idx.shape:
+        raise VerifySamplingError("out_vals and out_idx must share shape and strides")
     need = topk_rows_workspace_bytes(rows, V, K)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
-    ws_ptr = _ptr(workspace, torch.uint8, "workspace", True) if workspace is not None else None
-    ws_bytes = int(workspace.numel()) if workspace is not None else 0
-    if out_vals.stride() != out_idx.stride():
-        raise VerifySamplingError("out_vals and out_idx must share strides")
-    st = library().topk_rows(_ptr(X, torch.float32, "X"), _ld(X, "X"), rows, V, int(K),
-                             _ptr(out_vals, torch.float32, "out_vals"),
-                             _ptr(out_idx, torch.int32, "out_idx"), _ld(out_vals, "out_vals"),
-                             ws_ptr, ws_bytes, _stream(stream))
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _workspace(workspace, "workspace", dev)
+    st = library().topk_rows(x_ptr, ldx, rows, V, K, v_ptr, o_ptr, ld_out, ws_ptr, ws_bytes,
+                             _stream(stream))
     _check(st, "topk_rows")
     return out_vals, out_idx
 
@@ -286,73 +359,121 @@ def sample_policy_rows(vals, ids, *, temperature, top_k, top_p, min_p, u=None, o
     """Policy over candidate rows vals float32 [rows][M], ids int32 [rows][M] (M <= 64).
 
     Returns (dist_ids int32 [rows][M], dist_probs float32 [rows][M],
-    dist_len int32 [rows], drawn int32 [rows] or None).
+    dist_len int32 [rows], drawn int32 [rows] or None).  u: optional float32
+    [rows] uniforms (then drawn is returned).  out: optional preallocated
+    (dist_ids, dist_probs, dist_len, drawn) with drawn None when u is None.
     """
     import torch
 
+    if not isinstance(vals, torch.Tensor) or vals.dim() != 2:
+        raise VerifySamplingError("vals must be a 2-D torch tensor")
     rows, M = vals.shape
+    dev = vals.device
+    v_ptr, ld = _mat(vals, "vals", rows, M, torch.float32, dev)
+    i_ptr, _ = _mat(ids, "ids", rows, M, torch.int32, dev)
     if tuple(ids.shape) != (rows, M) or ids.stride() != vals.stride():
         raise VerifySamplingError("ids must match vals in shape and strides")
-    dev = vals.device
     if out is None:
         out = (torch.empty((rows, M), dtype=torch.int32, device=dev),
                torch.empty((rows, M), dtype=torch.float32, device=dev),
                torch.empty((rows,), dtype=torch.int32, device=dev),
                torch.empty((rows,), dtype=torch.int32, device=dev) if u is not None else None)
     d_ids, d_probs, d_len, drawn = out
-    if d_ids.stride() != d_probs.stride():
-        raise VerifySamplingError("dist_ids and dist_probs must share strides")
-    st = library().sample_policy_rows(
-        _ptr(vals, torch.float32, "vals"), _ptr(ids, torch.int32, "ids"), _ld(vals, "vals"), rows, M,
-        float(temperature), int(top_k), float(top_p), float(min_p),
-        _ptr(d_ids, torch.int32, "dist_ids"), _ptr(d_probs, torch.float32, "dist_probs"),
-        _ptr(d_len, torch.int32, "dist_len"), _ld(d_ids, "dist_ids"),
-        _ptr(u, torch.float32, "u", True), _ptr(drawn, torch.int32, "drawn", True),
-        _stream(stream))
+    di_ptr, ld_dist = _mat(d_ids, "dist_ids", rows, M, torch.int32, dev)
+    dp_ptr, _ = _mat(d_probs, "dist_probs", rows, M, torch.float32, dev)
+    if d_ids.stride() != d_probs.stride() or d_ids.shape != d_probs.shape:
+        raise VerifySamplingError("dist_ids and dist_probs must share shape and strides")
+    dl_ptr = _vec(d_len, "dist_len", rows, torch.int32, dev)
+    if (u is None) != (drawn is None):
+        raise VerifySamplingError("u and drawn must be given together")
+    u_ptr = _vec(u, "u", rows, torch.float32, dev, allow_none=True)
+    dr_ptr = _vec(drawn, "drawn", rows, torch.int32, dev, allow_none=True)
+    st = library().sample_policy_rows(v_ptr, i_ptr, ld, rows, M, float(temperature), int(top_k),
+                                      float(top_p), float(min_p), di_ptr, dp_ptr, dl_ptr, ld_dist,
+                                      u_ptr, dr_ptr, _stream(stream))
     _check(st, "sample_policy_rows")
     return d_ids, d_probs, d_len, drawn
+
+
+_TREE_MODES = (ACCEPT_GREEDY_TREE, ACCEPT_NAIVE_TREE)
+_UNIFORM_MODES = (ACCEPT_SAMPLED, ACCEPT_POINT_MASS, ACCEPT_NAIVE, ACCEPT_NAIVE_TREE)
+_GREEDY_MODES = (ACCEPT_GREEDY, ACCEPT_GREEDY_TREE)
+
+
+def _dist_rows(dist, name, rows, dev, need_probs):
+    """Pointers (ids, probs, len) and the row width of one side's sparse rows.
+
+    ids [>= rows][w] with rows of exactly w entries (the kernel reads up to
+    w per row), probs of the same shape and strides, len [>= rows]."""
+    import torch
+
+    ids, probs, length = dist
+    i_ptr, ld = _mat(ids, f"{name}_ids", rows, 1, torch.int32, dev, exact_rows=False)
+    w = ids.shape[1]
+    if ids.shape[0] > 1 and ld != w:
+        raise VerifySamplingError(f"{name}_ids rows must be dense (stride {w}), got stride {ld}")
+    if w > POOL:
+        raise VerifySamplingError(f"{name}_ids rows hold at most {POOL} entries, got {w}")
+    if need_probs and (probs is None or length is None):
+        raise VerifySamplingError(f"{name}_probs and {name}_len are required in this mode")
+    p_ptr = None
+    if probs is not None:
+        p_ptr, _ = _mat(probs, f"{name}_probs", ids.shape[0], w, torch.float32, dev)
+        if probs.shape != ids.shape or probs.stride() != ids.stride():
+            raise VerifySamplingError(f"{name}_probs must match {name}_ids in shape and strides")
+    l_ptr = _vec(length, f"{name}_len", rows, torch.int32, dev, allow_none=True)
+    return i_ptr, p_ptr, l_ptr, w
 
 
 def spec_accept_rows(mode, drafts, p, q=None, *, u=None, parent=None, p_win_stride=None,
                      q_win_stride=None, out=None, stream=None):
     """Accept drafts of B windows.
 
-    drafts: int32 [B][k].  p = (ids int32 [P][p_ld], probs float32 [P][p_ld] or
+    drafts: int32 [B][k].  p = (ids int32 [P][w], probs float32 [P][w] or
     None, len int32 [P] or None) with window b's row i at row
     b * p_win_stride + i (default stride k + 1); q likewise with k rows per
     window (default stride k; sampled mode only).  u: float32 [B][k+1][2]
-    (sampled, point-mass and naive modes);
-    parent: int32 [B][k] (tree mode).  Returns (tokens int32 [B][k+1],
-    n_emitted int32 [B]).
+    (sampled, point-mass and naive modes); parent: int32 [B][k] (tree
+    modes).  Returns (tokens int32 [B][k+1], n_emitted int32 [B]).
     """
     import torch
 
+    mode = int(mode)
+    if not isinstance(drafts, torch.Tensor) or drafts.dim() != 2:
+        raise VerifySamplingError("drafts must be a 2-D torch tensor [B][k]")
     B, k = drafts.shape
-    p_ids, p_probs, p_len = p
-    q_ids, q_probs, q_len = q if q is not None else (None, None, None)
+    dev = drafts.device
+    d_ptr = _vec(drafts, "drafts", B * k, torch.int32, dev)
     p_ws = k + 1 if p_win_stride is None else int(p_win_stride)
     q_ws = k if q_win_stride is None else int(q_win_stride)
-    dev = drafts.device
+    if p_ws < 0 or q_ws < 0:
+        raise VerifySamplingError("window strides must be >= 0")
+    p_rows = (B - 1) * p_ws + k + 1
+    pi_ptr, pp_ptr, pl_ptr, p_ld = _dist_rows(p, "p", p_rows, dev, mode not in _GREEDY_MODES)
+    q_ptrs, q_ld = (None, None, None), 1
+    if mode == ACCEPT_SAMPLED and k > 0:
+        if q is None:
+            raise VerifySamplingError("q is required in sampled mode")
+        *q_ptrs, q_ld = _dist_rows(q, "q", (B - 1) * q_ws + k, dev, True)
+    u_ptr = None
+    if mode in _UNIFORM_MODES:
+        if u is None:
+            raise VerifySamplingError("u is required in this mode")
+        u_ptr = _vec(u, "u", B * (k + 1) * 2, torch.float32, dev)
+    par_ptr = None
+    if mode in _TREE_MODES:
+        if parent is None:
+            raise VerifySamplingError("parent is required in the tree modes")
+        par_ptr = _vec(parent, "parent", B * k, torch.int32, dev)
     if out is None:
         out = (torch.empty((B, k + 1), dtype=torch.int32, device=dev),
                torch.empty((B,), dtype=torch.int32, device=dev))
     tokens, n_emitted = out
-    if not drafts.is_contiguous() or (u is not None and not u.is_contiguous()) or \
-            (parent is not None and not parent.is_contiguous()):
-        raise VerifySamplingError("drafts, u and parent must be contiguous")
-    for name, t, rows_needed in (("p_ids", p_ids, (B - 1) * p_ws + k + 1),
-                                 ("q_ids", q_ids, (B - 1) * q_ws + k)):
-        if t is not None and t.shape[0] < rows_needed:
-            raise VerifySamplingError(f"{name} has {t.shape[0]} rows, needs {rows_needed}")
-    st = library().spec_accept_rows(
-        int(mode), B, k,
-        _ptr(p_ids, torch.int32, "p_ids"), _ptr(p_probs, torch.float32, "p_probs", True),
-        _ptr(p_len, torch.int32, "p_len", True), _ld(p_ids, "p_ids"), p_ws,
-        _ptr(q_ids, torch.int32, "q_ids", True), _ptr(q_probs, torch.float32, "q_probs", True),
-        _ptr(q_len, torch.int32, "q_len", True), _ld(q_ids, "q_ids") if q_ids is not None else 1,
-        q_ws, _ptr(drafts, torch.int32, "drafts"), _ptr(parent, torch.int32, "parent", True),
-        _ptr(u, torch.float32, "u", True), _ptr(tokens, torch.int32, "tokens"),
-        _ptr(n_emitted, torch.int32, "n_emitted"), _stream(stream))
+    t_ptr = _vec(tokens, "tokens", B * (k + 1), torch.int32, dev)
+    n_ptr = _vec(n_emitted, "n_emitted", B, torch.int32, dev)
+    st = library().spec_accept_rows(mode, B, k, pi_ptr, pp_ptr, pl_ptr, p_ld, p_ws, q_ptrs[0],
+                                    q_ptrs[1], q_ptrs[2], q_ld, q_ws, d_ptr, par_ptr, u_ptr, t_ptr,
+                                    n_ptr, _stream(stream))
     _check(st, "spec_accept_rows")
     return tokens, n_emitted
 
