@@ -12,9 +12,10 @@
  *   - Array arguments are DEVICE pointers owned by the caller (the host
  *     functions vs_choose_depth and vs_lookup_tree take host arrays).  The
  *     library allocates no device memory and keeps no mutable global state
- *     apart from a per-thread copy of the last HIP error text; scratch
- *     space, where needed, is a caller-provided workspace whose size a
- *     companion *_workspace_bytes() call reports.
+ *     apart from a per-thread copy of the last HIP error text (and, for
+ *     topk_rows_noalloc, the per-GPU address of its fixed scratch area);
+ *     scratch space, where needed, is a caller-provided workspace whose
+ *     size a companion *_workspace_bytes() call reports.
  *   - Every call only enqueues work on `stream` and returns; it never
  *     synchronises the device.  Outputs are valid once the stream has
  *     reached the call.
@@ -48,10 +49,12 @@ enum vs_status {
   VS_ERR_UNSUPPORTED = -4, /* a valid combination the library does not handle */
   VS_ERR_WORKSPACE = -5,   /* workspace missing or too small                 */
   VS_ERR_ALIGN = -6,       /* a pointer or leading dimension is misaligned   */
-  VS_ERR_HIP = -7          /* the HIP runtime reported an error at launch    */
+  VS_ERR_HIP = -7,         /* the HIP runtime reported an error at launch    */
+  VS_ERR_SCRATCH = -8      /* the input needs more scratch than the library's
+                              fixed per-GPU area holds (topk_rows_noalloc)  */
 };
 
-#define VS_ABI_VERSION 2
+#define VS_ABI_VERSION 3
 #define VS_MAX_ROWS 24     /* verify rows R = k + 1 per projection call      */
 #define VS_POOL 64         /* width of the sampler's candidate pool          */
 #define VS_MAX_WINDOW 4096 /* longest penalty window                         */
@@ -167,6 +170,28 @@ size_t topk_rows_workspace_bytes(int rows, int V, int K);
 int topk_rows(const float* X, int64_t ldx, int rows, int V, int K,
               float* out_vals, int32_t* out_idx, int64_t ld_out,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * topk_rows_noalloc: topk_rows without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  It allocates nothing:
+ * rows of several chunks keep their per-chunk candidate lists in a fixed
+ * scratch area of topk_rows_noalloc_max_scratch_bytes() bytes (4 MiB) that
+ * the library holds in device memory, one copy per GPU, until the process
+ * ends.  Its device address is looked up once per GPU, on the first call
+ * made with that GPU current (the library's only other state).
+ *   Same arguments, results and errors as topk_rows, bit for bit, and
+ *   VS_ERR_SCRATCH, with nothing launched, when topk_rows_workspace_bytes(
+ *   rows, V, K) exceeds the scratch size (for example 24 rows of a
+ *   151936-token vocabulary at K = 64 need 1.8 MiB and fit).
+ *   Every call on one GPU shares that GPU's scratch area, and each call
+ *   writes what it later reads (no part of it needs to start at zero):
+ *   calls that may overlap on one GPU (distinct streams without ordering,
+ *   or several threads) race and must be serialised by the caller.
+ */
+size_t topk_rows_noalloc_max_scratch_bytes(void);
+int topk_rows_noalloc(const float* X, int64_t ldx, int rows, int V, int K,
+                      float* out_vals, int32_t* out_idx, int64_t ld_out, hipStream_t stream);
 
 /*
  * sample_policy_rows: the sampler distribution of each row, optionally

@@ -32,9 +32,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = vs.library()
-    assert lib.vs_abi_version() == 2
+    assert lib.vs_abi_version() == 3
     assert lib.vs_status_string(0) == b"ok"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         assert lib.vs_status_string(code) != b"unknown status"
     assert lib.vs_last_error_detail() == b""
 
@@ -90,6 +90,22 @@ def test_topk_rejects_before_launch():
     assert lib.topk_rows_workspace_bytes(4, 1024, 64) == 0
     assert lib.topk_rows_workspace_bytes(4, 4096, 64) == 0
     assert lib.topk_rows(FAKE, 8192, 1, 8192, 8, FAKE, FAKE, 8, None, 0, None) == -5   # workspace
+
+
+def test_topk_noalloc_rejects_before_launch():
+    """The allocation-free top-K checks its arguments like topk_rows and
+    refuses inputs whose per-chunk lists exceed its fixed 4 MiB scratch
+    area, before touching the GPU."""
+    lib = vs.library()
+    assert lib.topk_rows_noalloc_max_scratch_bytes() == 4 << 20
+    assert lib.topk_rows_noalloc(None, 100, 1, 100, 8, FAKE, FAKE, 8, None) == -1
+    assert lib.topk_rows_noalloc(FAKE, 100, 1, 100, 65, FAKE, FAKE, 65, None) == -2   # K > 64
+    assert lib.topk_rows_noalloc(FAKE, 100, 1, 100, 8, FAKE, FAKE, 7, None) == -2     # ld_out < K
+    # 54 rows of 151936 at K = 64 need 54 * 38 chunks * 64 * 8 bytes = 1.0 MiB: fits;
+    # 256 rows need 4.75 MiB: refused
+    assert lib.topk_rows_workspace_bytes(54, 151936, 64) < 4 << 20
+    assert lib.topk_rows_workspace_bytes(256, 151936, 64) > 4 << 20
+    assert lib.topk_rows_noalloc(FAKE, 151936, 256, 151936, 64, FAKE, FAKE, 64, None) == -8
 
 
 def test_policy_and_penalty_and_accept_reject_before_launch():

@@ -27,6 +27,7 @@ __all__ = [
     "penalize_tree_rows",
     "topk_rows",
     "topk_rows_workspace_bytes",
+    "topk_rows_noalloc",
     "sample_policy_rows",
     "spec_accept_rows",
     "choose_depth",
@@ -57,6 +58,8 @@ EXPORTED_SYMBOLS = (
     "penalize_tree_rows",
     "topk_rows_workspace_bytes",
     "topk_rows",
+    "topk_rows_noalloc_max_scratch_bytes",
+    "topk_rows_noalloc",
     "sample_policy_rows",
     "spec_accept_rows",
     "vs_choose_depth",
@@ -85,6 +88,8 @@ _SIGNATURES = {
     "penalize_tree_rows": ([P, P, I64, I32, I32, P, I32, P, P, I32, I32, F32, F32, F32, P], I32),
     "topk_rows_workspace_bytes": ([I32, I32, I32], SZ),
     "topk_rows": ([P, I64, I32, I32, I32, P, P, I64, P, SZ, P], I32),
+    "topk_rows_noalloc_max_scratch_bytes": ([], SZ),
+    "topk_rows_noalloc": ([P, I64, I32, I32, I32, P, P, I64, P], I32),
     "sample_policy_rows": ([P, P, I64, I32, I32, F32, I32, F32, F32, P, P, P, I64, P, P, P], I32),
     "spec_accept_rows": ([I32, I32, I32, P, P, P, I32, I64, P, P, P, I32, I64, P, P, P, P, P, P],
                          I32),
@@ -351,6 +356,32 @@ def topk_rows(X, K, out_vals=None, out_idx=None, workspace=None, stream=None):
     st = library().topk_rows(x_ptr, ldx, rows, V, K, v_ptr, o_ptr, ld_out, ws_ptr, ws_bytes,
                              _stream(stream))
     _check(st, "topk_rows")
+    return out_vals, out_idx
+
+
+def topk_rows_noalloc(X, K, out_vals=None, out_idx=None, stream=None):
+    """topk_rows without a workspace: the library's fixed per-GPU scratch
+    area holds the per-chunk candidates (no allocation in the library; pass
+    out_vals and out_idx to allocate nothing here either).  Calls that may
+    overlap on one GPU share that area and must be serialised."""
+    import torch
+
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise VerifySamplingError("X must be a 2-D torch tensor")
+    rows, V = X.shape
+    K = int(K)
+    dev = X.device
+    x_ptr, ldx = _mat(X, "X", rows, V, torch.float32, dev)
+    if out_vals is None:
+        out_vals = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((rows, K), dtype=torch.int32, device=dev)
+    v_ptr, ld_out = _mat(out_vals, "out_vals", rows, K, torch.float32, dev)
+    o_ptr, _ = _mat(out_idx, "out_idx", rows, K, torch.int32, dev)
+    if out_vals.stride() != out_idx.stride() or out_vals.shape != out_idx.shape:
+        raise VerifySamplingError("out_vals and out_idx must share shape and strides")
+    st = library().topk_rows_noalloc(x_ptr, ldx, rows, V, K, v_ptr, o_ptr, ld_out, _stream(stream))
+    _check(st, "topk_rows_noalloc")
     return out_vals, out_idx
 
 

@@ -31,6 +31,7 @@ extern "C" const char* vs_status_string(int status) {
     case VS_ERR_WORKSPACE: return "workspace missing or too small";
     case VS_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
     case VS_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case VS_ERR_SCRATCH: return "the input needs more scratch than the fixed per-GPU area holds";
     default: return "unknown status";
   }
 }

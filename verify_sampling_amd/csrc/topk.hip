@@ -24,6 +24,9 @@
 // survivors.  The selection is exact integer work, so the result does not
 // depend on scheduling or on the chunking.
 
+#include <atomic>
+#include <mutex>
+
 #include "wave_ops.h"
 
 namespace {
@@ -734,20 +737,15 @@ extern "C" size_t topk_rows_workspace_bytes(int rows, int V, int K) {
   return static_cast<size_t>(rows) * p.chunks * K * sizeof(uint64_t);
 }
 
-extern "C" int topk_rows(const float* X, int64_t ldx, int rows, int V, int K, float* out_vals,
-                         int32_t* out_idx, int64_t ld_out, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
-  if (!X || !out_vals || !out_idx) return VS_ERR_NULL;
-  if (rows < 1 || rows > (1 << 24) || K < 1 || K > VS_POOL || V < K || V > VS_MAX_VOCAB)
-    return VS_ERR_SHAPE;
-  if (ldx < V || ld_out < K) return VS_ERR_SHAPE;
+namespace {
+
+// Both launches of a top-K call; ws holds topk_rows_workspace_bytes(rows, V,
+// K) bytes (checked by the callers).
+int launch_topk(const float* X, int64_t ldx, int rows, int V, int K, float* out_vals,
+                int32_t* out_idx, int64_t ld_out, uint64_t* ws, hipStream_t stream) {
   const Plan p = plan_for(rows, V);
   static_assert(MAX_CHUNKS <= 256, "the merge's threshold entries fit four per lane");
   static_assert(MAX_CHUNKS * 4 <= 64 * MERGE_LOADS, "the merge reads at least four entries per chunk");
-  const size_t need = topk_rows_workspace_bytes(rows, V, K);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return VS_ERR_WORKSPACE;
-  if (need > 0 && !vs::aligned16(workspace)) return VS_ERR_ALIGN;
-  uint64_t* ws = static_cast<uint64_t*>(workspace);
   const int64_t units = static_cast<int64_t>(rows) * p.chunks;
   const dim3 grid(static_cast<unsigned>((units + WAVES - 1) / WAVES)), block(64 * WAVES);
   if (p.small)
@@ -766,4 +764,71 @@ extern "C" int topk_rows(const float* X, int64_t ldx, int rows, int V, int K, fl
   topk_merge_kernel<<<dim3(static_cast<unsigned>((rows + WAVES - 1) / WAVES)), block, 0, stream>>>(
       X, ldx, rows, V, K, p.chunks, lg_jp, lg_j2, ws, out_vals, out_idx, ld_out);
   return vs::check_launch();
+}
+
+int check_topk_args(const float* X, int64_t ldx, int rows, int V, int K, const float* out_vals,
+                    const int32_t* out_idx, int64_t ld_out) {
+  if (!X || !out_vals || !out_idx) return VS_ERR_NULL;
+  if (rows < 1 || rows > (1 << 24) || K < 1 || K > VS_POOL || V < K || V > VS_MAX_VOCAB)
+    return VS_ERR_SHAPE;
+  if (ldx < V || ld_out < K) return VS_ERR_SHAPE;
+  return VS_OK;
+}
+
+// The fixed scratch area of topk_rows_noalloc: one copy per GPU, in device
+// memory for the life of the process.  Host code never uses this name as an
+// address; it uses the per-device address that hipGetSymbolAddress returns.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t{4} << 20;
+__device__ __align__(256) uint64_t scratch[NOALLOC_SCRATCH_BYTES / sizeof(uint64_t)];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_addr[MAX_DEVICES];
+std::mutex g_scratch_mutex;
+
+// The address of `scratch` on the current device, looked up once per device.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return vs::hip_status(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return VS_ERR_UNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return vs::hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return VS_OK;
+}
+
+}  // namespace
+
+extern "C" int topk_rows(const float* X, int64_t ldx, int rows, int V, int K, float* out_vals,
+                         int32_t* out_idx, int64_t ld_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  int st = check_topk_args(X, ldx, rows, V, K, out_vals, out_idx, ld_out);
+  if (st != VS_OK) return st;
+  const size_t need = topk_rows_workspace_bytes(rows, V, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return VS_ERR_WORKSPACE;
+  if (need > 0 && !vs::aligned16(workspace)) return VS_ERR_ALIGN;
+  return launch_topk(X, ldx, rows, V, K, out_vals, out_idx, ld_out, static_cast<uint64_t*>(workspace),
+                     stream);
+}
+
+extern "C" size_t topk_rows_noalloc_max_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int topk_rows_noalloc(const float* X, int64_t ldx, int rows, int V, int K,
+                                 float* out_vals, int32_t* out_idx, int64_t ld_out,
+                                 hipStream_t stream) {
+  int st = check_topk_args(X, ldx, rows, V, K, out_vals, out_idx, ld_out);
+  if (st != VS_OK) return st;
+  if (topk_rows_workspace_bytes(rows, V, K) > NOALLOC_SCRATCH_BYTES) return VS_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != VS_OK) return st;
+  return launch_topk(X, ldx, rows, V, K, out_vals, out_idx, ld_out, static_cast<uint64_t*>(ws), stream);
 }
