@@ -21,6 +21,9 @@ Stages and the passage each follows:
   policy.draw           [SD] §03 (one request-seeded random stream)
   accept.*              [SD] §01 figure and text, §02, §03 steps 1-4, §06;
                         [TREE] "Spend the budget on a tree"
+  tree_attention.*      [TREE] "Spend the budget on a tree" (tree attention
+                        mask), "Where the tree earns its keep" (KV scratch
+                        slots, only the accepted branch kept)
 
 Every function's pin (what checks it against something other than itself)
 is in tests/test_oracle_*.py.  Parity unpinned: none of the functions here;
@@ -28,4 +31,4 @@ the sampler policy's stage semantics are pinned only by constructed closed
 forms, since the pages print no numbers for it.
 """
 
-from . import accept, gemv, penalty, pipeline, policy, topk  # noqa: F401
+from . import accept, gemv, penalty, pipeline, policy, topk, tree_attention  # noqa: F401
