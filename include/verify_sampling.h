@@ -299,6 +299,60 @@ int spec_accept_rows(int mode, int B, int k,
                      int32_t* out_tokens, int32_t* out_n, hipStream_t stream);
 
 /*
+ * tree_attention_rows: attention of a token tree's verify rows under the tree
+ * mask.
+ *   [TREE] "Spend the budget on a tree, not a longer guess": one verify pass
+ *   carries several branches that share a prefix, with a tree-shaped
+ *   attention mask under which each branch attends only to its ancestors;
+ *   "Where the tree earns its keep": the candidates' keys and values sit in
+ *   scratch slots; "What I am building toward": the mask folded into the
+ *   decode attention.
+ *
+ * Row 0 is the root (the current position; its key and value in scratch
+ * slot 0), row 1 + j is node j (slot 1 + j).  Row r attends to the context
+ * positions [0, ctx_len) of the cache and to the slots of its ancestors and
+ * itself; node j's path follows parent[] up to the root and stops at a
+ * parent outside [-1, child).  For query head h (KV head h / (Hq / Hkv)):
+ *   out[r][h] = sum_j softmax_j(scale * q[r][h] . k_j) * v_j
+ * over those keys, in fp32 arithmetic: exact products (queries and
+ * probabilities split into three bf16 pieces), fp32 sums in a fixed order,
+ * online softmax over 64-key blocks merged in a fixed order.
+ *   q        fp32 [R][Hq][D] contiguous, 16-byte aligned
+ *   k_cache, v_cache  bf16 bits [Hkv][cache_len][D] (may be NULL when ctx_len == 0)
+ *   k_scr, v_scr      bf16 bits [Hkv][scr_len][D], scr_len >= R
+ *   parent   int32 [R - 1] device array (node j's parent; -1 = the root)
+ *   out      fp32 [R][Hq][D] contiguous
+ *   D == 128, 1 <= R <= 64, Hq % Hkv == 0, (Hq / Hkv) * R <= 256,
+ *   0 <= ctx_len <= cache_len, scale finite.
+ *   workspace  device memory of at least tree_attention_rows_workspace_bytes(
+ *   R, Hq, Hkv, ctx_len) bytes, 16-byte aligned: per-split partial results
+ *   (written before they are read; no initialisation needed).
+ */
+size_t tree_attention_rows_workspace_bytes(int R, int Hq, int Hkv, int ctx_len);
+int tree_attention_rows(const float* q, int R, int Hq, int D, const uint16_t* k_cache,
+                        const uint16_t* v_cache, int64_t cache_len, int ctx_len,
+                        const uint16_t* k_scr, const uint16_t* v_scr, int scr_len,
+                        const int32_t* parent, int Hkv, float scale, float* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tree_commit_kv: keep the accepted branch.
+ *   [TREE] "Where the tree earns its keep": only the accepted branch's keys
+ *   and values are kept.
+ * For every KV head, scratch slot path[i] is copied to cache position
+ * ctx_len + i (0 <= i < n_path), bits unchanged; nothing else changes.
+ * path is a device array of slot indices, root first (slot 0, then the
+ * slots 1 + j of the accepted nodes in order); an index outside [0,
+ * scr_len) leaves its position unchanged.
+ *   caches bf16 bits [Hkv][cache_len][D], scratch [Hkv][scr_len][D], all
+ *   16-byte aligned; D % 8 == 0; ctx_len + n_path <= cache_len;
+ *   0 <= n_path <= 64.
+ */
+int tree_commit_kv(uint16_t* k_cache, uint16_t* v_cache, int64_t cache_len, int ctx_len,
+                   const uint16_t* k_scr, const uint16_t* v_scr, int scr_len,
+                   const int32_t* path, int n_path, int Hkv, int D, hipStream_t stream);
+
+/*
  * vs_choose_depth: the draft depth of the next window.
  *   [SD] §05 "What a verify row costs on RDNA": pick the depth k that
  *   maximises the expected emitted tokens (1 plus the running products of

@@ -154,3 +154,26 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(vs, "_lib", None)
     with pytest.raises(vs.VerifySamplingError):
         vs.library(str(tmp_path / "missing.so"))
+
+
+def test_tree_attention_rejects_before_launch():
+    lib = vs.library()
+    ws = lib.tree_attention_rows_workspace_bytes(25, 32, 8, 2080)
+    assert ws > 0
+    args = lambda **k: dict(dict(q=FAKE, R=25, Hq=32, D=128, kc=FAKE, vc=FAKE, L=4096, ctx=2080, ks=FAKE,
+                                 vs=FAKE, S=25, par=FAKE, Hkv=8, scale=0.088, out=FAKE, ws=FAKE, nws=ws), **k)
+    call = lambda a: lib.tree_attention_rows(a["q"], a["R"], a["Hq"], a["D"], a["kc"], a["vc"], a["L"], a["ctx"],
+                                            a["ks"], a["vs"], a["S"], a["par"], a["Hkv"], a["scale"], a["out"],
+                                            a["ws"], a["nws"], None)
+    assert call(args(q=None)) == -1
+    assert call(args(D=64)) == -4                       # head dimension 128 only
+    assert call(args(R=65, S=65)) == -2                 # at most 64 tree rows
+    assert call(args(Hq=30)) == -2                      # Hq % Hkv
+    assert call(args(ctx=4097)) == -2                   # ctx_len > cache_len
+    assert call(args(S=24)) == -2                       # scr_len < R
+    assert call(args(scale=float("inf"))) == -3
+    assert call(args(nws=ws - 1)) == -5
+    assert call(args(R=64, S=64, Hq=16, Hkv=2)) == -2   # 8 heads x 64 rows > 256 queries per KV head
+    assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, FAKE, 11, 8, 128, None) == -2  # past the cache
+    assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, FAKE, 3, 8, 12, None) == -2    # D % 8
+    assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, None, 0, 8, 128, None) == 0    # nothing to copy

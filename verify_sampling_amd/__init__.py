@@ -32,6 +32,9 @@ __all__ = [
     "spec_accept_rows",
     "choose_depth",
     "lookup_tree",
+    "tree_attention_rows",
+    "tree_attention_rows_workspace_bytes",
+    "tree_commit_kv",
     "ACCEPT_SAMPLED",
     "ACCEPT_GREEDY",
     "ACCEPT_GREEDY_TREE",
@@ -62,6 +65,9 @@ EXPORTED_SYMBOLS = (
     "topk_rows_noalloc",
     "sample_policy_rows",
     "spec_accept_rows",
+    "tree_attention_rows_workspace_bytes",
+    "tree_attention_rows",
+    "tree_commit_kv",
     "vs_choose_depth",
     "vs_lookup_tree",
 )
@@ -93,6 +99,9 @@ _SIGNATURES = {
     "sample_policy_rows": ([P, P, I64, I32, I32, F32, I32, F32, F32, P, P, P, I64, P, P, P], I32),
     "spec_accept_rows": ([I32, I32, I32, P, P, P, I32, I64, P, P, P, I32, I64, P, P, P, P, P, P],
                          I32),
+    "tree_attention_rows_workspace_bytes": ([I32, I32, I32, I32], SZ),
+    "tree_attention_rows": ([P, I32, I32, I32, P, P, I64, I32, P, P, I32, P, I32, F32, P, P, SZ, P], I32),
+    "tree_commit_kv": ([P, P, I64, I32, P, P, I32, P, I32, I32, I32, P], I32),
     "vs_choose_depth": ([P, I32, P, P], I32),
     "vs_lookup_tree": ([P, I32, I32, I32, I32, I32, P, P], I32),
 }
@@ -507,6 +516,80 @@ def spec_accept_rows(mode, drafts, p, q=None, *, u=None, parent=None, p_win_stri
                                     n_ptr, _stream(stream))
     _check(st, "spec_accept_rows")
     return tokens, n_emitted
+
+
+def _bf16_bits(t, name, dev):
+    """A bf16 (or int16/uint16 bit-pattern) 3-D contiguous tensor as its bits."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise VerifySamplingError(f"{name} must be a torch tensor")
+    if t.dtype in (torch.int16, torch.uint16):
+        t = t.view(torch.bfloat16)
+    if t.dim() != 3:
+        raise VerifySamplingError(f"{name} must be 3-D [heads][positions][D]")
+    return _vec(t, name, t.numel(), torch.bfloat16, dev), t
+
+
+def tree_attention_rows_workspace_bytes(R: int, Hq: int, Hkv: int, ctx_len: int) -> int:
+    return int(library().tree_attention_rows_workspace_bytes(R, Hq, Hkv, ctx_len))
+
+
+def tree_attention_rows(q, k_cache, v_cache, ctx_len, k_scr, v_scr, parent, *, scale, out=None,
+                        workspace=None, stream=None):
+    """Attention of the R rows of a token tree (root + R - 1 nodes) under the
+    tree mask.  q float32 [R][Hq][D]; caches and scratch bf16 [Hkv][len][D];
+    parent int32 [R - 1] (device).  Returns out float32 [R][Hq][D]."""
+    import torch
+
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise VerifySamplingError("q must be a 3-D torch tensor [R][Hq][D]")
+    R, Hq, D = q.shape
+    dev = q.device
+    q_ptr = _vec(q, "q", q.numel(), torch.float32, dev)
+    ks_ptr, k_scr = _bf16_bits(k_scr, "k_scr", dev)
+    vs_ptr, v_scr = _bf16_bits(v_scr, "v_scr", dev)
+    Hkv, scr_len, Ds = k_scr.shape
+    if tuple(v_scr.shape) != (Hkv, scr_len, Ds) or Ds != D:
+        raise VerifySamplingError("k_scr and v_scr must be [Hkv][scr_len][D] alike")
+    kc_ptr, k_cache = _bf16_bits(k_cache, "k_cache", dev)
+    vc_ptr, v_cache = _bf16_bits(v_cache, "v_cache", dev)
+    if k_cache.shape[0] != Hkv or k_cache.shape[2] != D or v_cache.shape != k_cache.shape:
+        raise VerifySamplingError("k_cache and v_cache must be [Hkv][cache_len][D] alike")
+    cache_len = int(k_cache.shape[1])
+    p_ptr = _vec(parent, "parent", R - 1, torch.int32, dev, allow_none=R == 1)
+    if out is None:
+        out = torch.empty((R, Hq, D), dtype=torch.float32, device=dev)
+    o_ptr = _vec(out, "out", R * Hq * D, torch.float32, dev)
+    need = tree_attention_rows_workspace_bytes(R, Hq, Hkv, int(ctx_len))
+    if workspace is None:
+        workspace = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _workspace(workspace, "workspace", dev)
+    st = library().tree_attention_rows(q_ptr, R, Hq, D, kc_ptr, vc_ptr, cache_len, int(ctx_len),
+                                       ks_ptr, vs_ptr, scr_len, p_ptr, Hkv, float(scale), o_ptr,
+                                       ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "tree_attention_rows")
+    return out
+
+
+def tree_commit_kv(k_cache, v_cache, ctx_len, k_scr, v_scr, path, stream=None):
+    """Copies scratch slots path[i] into cache positions ctx_len + i, every KV head."""
+    import torch
+
+    dev = k_cache.device
+    kc_ptr, k_cache = _bf16_bits(k_cache, "k_cache", dev)
+    vc_ptr, v_cache = _bf16_bits(v_cache, "v_cache", dev)
+    ks_ptr, k_scr = _bf16_bits(k_scr, "k_scr", dev)
+    vs_ptr, v_scr = _bf16_bits(v_scr, "v_scr", dev)
+    Hkv, cache_len, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_scr.shape[0] != Hkv or k_scr.shape[2] != D or \
+            v_scr.shape != k_scr.shape:
+        raise VerifySamplingError("caches [Hkv][cache_len][D] and scratch [Hkv][scr_len][D] must agree")
+    n = int(path.numel()) if path is not None else 0
+    pa_ptr = _vec(path, "path", n, torch.int32, dev) if n else None
+    st = library().tree_commit_kv(kc_ptr, vc_ptr, cache_len, int(ctx_len), ks_ptr, vs_ptr,
+                                  int(k_scr.shape[1]), pa_ptr, n, Hkv, D, _stream(stream))
+    _check(st, "tree_commit_kv")
 
 
 def choose_depth(alpha, cost):
