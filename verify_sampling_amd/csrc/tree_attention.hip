@@ -86,6 +86,13 @@ __device__ __forceinline__ void split3_one(float x, uint16_t& hi, uint16_t& mid,
   lo = static_cast<uint16_t>(fbits(s) >> 16);
 }
 
+// e^x through the hardware base-2 exponential: x * log2(e) rounds once
+// (relative error |x| * 2^-24, |x| < ~100 here) and v_exp_f32 adds about
+// one ulp; far inside the tolerance the attention is held to
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 // max / sum over the 16 lanes of a row group (lanes l with equal l / 16),
 // always in the same butterfly order
 __device__ __forceinline__ float group16_max(float v) {
@@ -100,7 +107,7 @@ __device__ __forceinline__ float group16_sum(float v) {
 }
 
 // The scratch slots row `row` attends to, as a bit mask (bit s = slot s).
-__device__ __forceinline__ uint64_t ancestor_mask(const int32_t* __restrict__ parent, int row) {
+__device__ __forceinline__ uint64_t ancestor_mask(const int32_t* parent, int row) {
   uint64_t m = 1ull;  // the root's slot
   if (row > 0) {
     int child = row - 1;
@@ -133,12 +140,27 @@ struct Args {
   float* part_ml;          // [splits][Hkv][M][2]
 };
 
-// MTW: 16-query tiles per wave (M = G * R <= 64 * WAVES * MTW)
-template <int MTW>
+// Workgroup (g, split, z): KV head g, one split of its keys, query tiles
+// WAVES * MTW * z ..; MTW: 16-query tiles per wave.  QREG:
+// the queries' bf16 planes stay in registers for the whole split (else they
+// are reloaded and split for every sub-block).
+//
+// Both products are taken transposed, so that a lane owns one query of a
+// tile throughout: S^T = K Q^T (A = keys, B = query planes; lane (g, c)
+// holds query c and keys 16 t + 4 g + e) and O^T = V^T P^T (A = V^T from
+// LDS, B = the probability planes; lane (g, c) holds query c and dimensions
+// 16 t + 4 g + e).  A row's maximum and sum are then 16 register values and
+// two shuffles across the lane groups, and its probabilities are written to
+// LDS four keys at a time.
+template <int MTW, bool QREG>
 __global__ void __launch_bounds__(64 * WAVES)
 tree_attention_split_kernel(Args a) {
-  __shared__ __align__(16) uint16_t pl[WAVES][MTW][3][16 * PSTR];  // probability planes, per wave
-  __shared__ __align__(16) uint16_t vt[HD * VSTR];                 // V of the sub-block, transposed
+  constexpr int KSTR = HD + 8;  // LDS row stride (bf16) of the key block
+  __shared__ __align__(16) uint16_t pl[WAVES][MTW][3][16 * PSTR];  // probability planes [query][key]
+  __shared__ __align__(16) uint16_t vt[HD * VSTR];                 // values of the sub-block, [dim][key]
+  __shared__ __align__(16) uint16_t kt[BKEYS * KSTR];              // keys of the sub-block, [key][dim]
+  __shared__ int32_t par[MAX_ROWS];
+  __shared__ uint64_t anc_row[MAX_ROWS];
   const int lane = threadIdx.x & 63;
   const int w = vs::wave_index();
   const int g = blockIdx.x;                 // KV head
@@ -146,58 +168,110 @@ tree_attention_split_kernel(Args a) {
   const bool scratch = split == a.ctx_splits;
   const int M = a.G * a.R;
   const int col = lane & 15, grp = lane >> 4;
+  const int mt0 = blockIdx.z * WAVES * MTW;  // this workgroup's first query tile
 
-  // this wave's query tiles: mt = w + WAVES * i; per lane, the scratch
-  // slots visible to the query row of each of its C elements (4 per tile;
-  // padding rows past M see slot 0 only, and their results are dropped)
-  uint64_t anc[MTW][4];
+  // the tree mask (scratch split only): parents to LDS, one row per thread
+  if (scratch) {  // uniform over the workgroup
+    for (int t = threadIdx.x; t < a.R - 1; t += 64 * WAVES) par[t] = a.parent[t];
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.R; r += 64 * WAVES) anc_row[r] = ancestor_mask(par, r);
+    __syncthreads();
+  }
+  // this wave's query tiles: mt = mt0 + w + WAVES * i; lane (g, c) owns
+  // query 16 mt + c of each; padding queries past M see slot 0 only and are
+  // dropped
+  uint64_t anc[MTW];
 #pragma unroll
-  for (int i = 0; i < MTW; ++i)
+  for (int i = 0; i < MTW; ++i) {
+    const int m = (mt0 + w + WAVES * i) * 16 + col;
+    anc[i] = (scratch && m < M) ? anc_row[m % a.R] : 1ull;
+  }
+
+  // queries as B operands (query c of the tile, dimensions 32 ks + 8 g ..),
+  // split into bf16 planes
+  auto q_planes = [&](int i, int ks, u32x4& hi, u32x4& mid, u32x4& lo) {
+    const int m = (mt0 + w + WAVES * i) * 16 + col;
+    float x[8];
+    if (m < M) {
+      const int r = m % a.R, hq = g * a.G + m / a.R;
+      const float* src = a.q + (static_cast<int64_t>(r) * a.Hq + hq) * HD + ks * 32 + grp * 8;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = (w + WAVES * i) * 16 + 4 * grp + e;
-      anc[i][e] = (scratch && m < M) ? ancestor_mask(a.parent, m % a.R) : 1ull;
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
     }
+    split3(x, hi, mid, lo);
+  };
+  u32x4 qp[QREG ? MTW : 1][KSTEPS][3];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) q_planes(i, ks, qp[i][ks][0], qp[i][ks][1], qp[i][ks][2]);
+  }
 
-  f32x4 o[MTW][NT_O];
-  float rm[MTW][4], rl[MTW][4];
+  f32x4 o[MTW][NT_O];  // O^T tiles: lane (g, c), element e = dimension 16 t + 4 g + e of query c
+  float rm[MTW], rl[MTW];
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
 #pragma unroll
     for (int t = 0; t < NT_O; ++t) o[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      rm[i][e] = -__builtin_inff();
-      rl[i][e] = 0.f;
-    }
+    rm[i] = -__builtin_inff();
+    rl[i] = 0.f;
   }
 
   const uint16_t* kbase = scratch ? a.ks + static_cast<int64_t>(g) * a.scr_len * HD
                                   : a.kc + static_cast<int64_t>(g) * a.cache_len * HD;
   const uint16_t* vbase = scratch ? a.vs + static_cast<int64_t>(g) * a.scr_len * HD
                                   : a.vc + static_cast<int64_t>(g) * a.cache_len * HD;
-  const int nsub = scratch ? 1 : a.NB;
-  for (int sb = 0; sb < nsub; ++sb) {
-    // keys of this sub-block: positions p0 .. p0 + 63 below nkeys
-    const int p0 = scratch ? 0 : (split * a.NB + sb) * BKEYS;
-    const int nkeys = scratch ? a.R : a.ctx_len;
-    if (!scratch && p0 >= nkeys) break;  // uniform over the workgroup
+  const int nkeys = scratch ? a.R : a.ctx_len;
+  const int first = scratch ? 0 : split * a.NB * BKEYS;
+  int nsub = scratch ? 1 : (nkeys - first + BKEYS - 1) / BKEYS;  // sub-blocks of this split
+  if (nsub > (scratch ? 1 : a.NB)) nsub = scratch ? 1 : a.NB;
 
-    // V of the sub-block into LDS, transposed ([dim][key]); keys past the
-    // end are zero (their probabilities are zero, and 0 * garbage could be NaN)
-    __syncthreads();  // the previous sub-block's vt has been read
-    for (int c = threadIdx.x; c < BKEYS * HD / 8; c += 64 * WAVES) {
-      const int key = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (p0 + key < nkeys) v = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(p0 + key) * HD + d0);
+  // this thread's share of a sub-block's keys and values: 16-byte pieces
+  // t + 64 WAVES j, piece p = (key p % 64, dimensions 8 (p / 64) ..); keys
+  // past the end are zero (their probabilities are zero, and 0 * garbage
+  // could be NaN)
+  constexpr int PIECES = BKEYS * HD / 8 / (64 * WAVES);
+  u32x4 kr[PIECES], vr[PIECES];
+  auto load_kv = [&](int p0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vt[(d0 + 2 * j) * VSTR + key] = static_cast<uint16_t>(v[j] & 0xffffu);
-        vt[(d0 + 2 * j + 1) * VSTR + key] = static_cast<uint16_t>(v[j] >> 16);
+    for (int j = 0; j < PIECES; ++j) {
+      const int piece = threadIdx.x + 64 * WAVES * j;
+      const int key = piece & (BKEYS - 1), d0 = (piece / BKEYS) * 8;
+      const bool ok = p0 + key < nkeys;
+      const int64_t off = static_cast<int64_t>(p0 + key) * HD + d0;
+      kr[j] = ok ? *reinterpret_cast<const u32x4*>(kbase + off) : u32x4{0u, 0u, 0u, 0u};
+      vr[j] = ok ? *reinterpret_cast<const u32x4*>(vbase + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_kv = [&]() {
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+      const int piece = threadIdx.x + 64 * WAVES * j;
+      const int key = piece & (BKEYS - 1), d0 = (piece / BKEYS) * 8;
+      *reinterpret_cast<u32x4*>(&kt[key * KSTR + d0]) = kr[j];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        vt[(d0 + 2 * jj) * VSTR + key] = static_cast<uint16_t>(vr[j][jj] & 0xffffu);
+        vt[(d0 + 2 * jj + 1) * VSTR + key] = static_cast<uint16_t>(vr[j][jj] >> 16);
       }
     }
+  };
 
-    // scores: S[query][key] for this wave's tiles
+  if (nsub > 0) load_kv(first);
+  for (int sb = 0; sb < nsub; ++sb) {  // uniform over the workgroup
+    const int p0 = first + sb * BKEYS;
+    __syncthreads();  // the previous sub-block's kt, vt and planes have been read
+    store_kv();
+    __syncthreads();
+    if (sb + 1 < nsub) load_kv(p0 + BKEYS);  // the next sub-block, in flight meanwhile
+
+    // S^T tiles: A = keys 16 t .. (key c of the tile, dimensions 32 ks + 8 g ..)
     f32x4 s[MTW][NT_S];
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
@@ -205,88 +279,84 @@ tree_attention_split_kernel(Args a) {
       for (int t = 0; t < NT_S; ++t) s[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int d = ks * 32 + grp * 8;
-      u32x4 kb[NT_S];
+      u32x4 ka[NT_S];
 #pragma unroll
-      for (int t = 0; t < NT_S; ++t) {
-        const int key = p0 + t * 16 + col;
-        kb[t] = key < nkeys ? *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * HD + d)
-                            : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int t = 0; t < NT_S; ++t)
+        ka[t] = *reinterpret_cast<const u32x4*>(&kt[(t * 16 + col) * KSTR + ks * 32 + grp * 8]);
 #pragma unroll
       for (int i = 0; i < MTW; ++i) {
-        const int m = (w + WAVES * i) * 16 + col;  // A operand: query row col of the tile
-        float x[8];
-        if (m < M) {
-          const int r = m % a.R, hq = g * a.G + m / a.R;
-          const float* src = a.q + (static_cast<int64_t>(r) * a.Hq + hq) * HD + d;
-          const float4 x0 = *reinterpret_cast<const float4*>(src);
-          const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-          x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = 0.f;
-        }
         u32x4 hi, mid, lo;
-        split3(x, hi, mid, lo);
+        if constexpr (QREG) {
+          hi = qp[i][ks][0];
+          mid = qp[i][ks][1];
+          lo = qp[i][ks][2];
+        } else {
+          q_planes(i, ks, hi, mid, lo);
+        }
 #pragma unroll
         for (int t = 0; t < NT_S; ++t) {
-          s[i][t] = mfma(hi, kb[t], s[i][t]);
-          s[i][t] = mfma(mid, kb[t], s[i][t]);
-          s[i][t] = mfma(lo, kb[t], s[i][t]);
+          s[i][t] = mfma(ka[t], hi, s[i][t]);
+          s[i][t] = mfma(ka[t], mid, s[i][t]);
+          s[i][t] = mfma(ka[t], lo, s[i][t]);
         }
       }
     }
 
-    // online softmax over the sub-block; probabilities into this wave's planes
+    // online softmax over the sub-block for the lane's query of each tile;
+    // the probabilities go to this wave's planes, four keys per store
+    const bool all_keys = !scratch && p0 + BKEYS <= nkeys;
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
-      float alpha[4];
+      float bm = -__builtin_inff();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float bm = -__builtin_inff();
+      for (int t = 0; t < NT_S; ++t)
 #pragma unroll
-        for (int t = 0; t < NT_S; ++t) {
-          const int key = t * 16 + col;  // within the sub-block
-          const bool ok = scratch ? (key < a.R && ((anc[i][e] >> key) & 1ull)) : (p0 + key < nkeys);
+        for (int e = 0; e < 4; ++e) {
+          const int key = t * 16 + 4 * grp + e;  // within the sub-block
+          const bool ok = all_keys || (scratch ? (key < a.R && ((anc[i] >> key) & 1ull)) : (p0 + key < nkeys));
           s[i][t][e] = ok ? s[i][t][e] * a.scale : -__builtin_inff();
           bm = fmaxf(bm, s[i][t][e]);
         }
-        bm = group16_max(bm);  // every row sees at least one key of every sub-block
-        const float mn = fmaxf(rm[i][e], bm);
-        alpha[e] = expf(rm[i][e] - mn);  // 0 on the first sub-block
-        rm[i][e] = mn;
-        float ps = 0.f;
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));  // every query sees a key of every sub-block
+      const float mn = fmaxf(rm[i], bm);
+      const float alpha = fast_exp(rm[i] - mn);  // 0 on the first sub-block
+      rm[i] = mn;
+      float ps = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT_S; ++t) {
-          const float p = expf(s[i][t][e] - mn);  // 0 for masked keys
+      for (int t = 0; t < NT_S; ++t) {
+        uint16_t h[4], md[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = fast_exp(s[i][t][e] - mn);  // 0 for masked keys
           ps += p;
-          uint16_t h, md, l;
-          split3_one(p, h, md, l);
-          const int off = (4 * grp + e) * PSTR + t * 16 + col;
-          pl[w][i][0][off] = h;
-          pl[w][i][1][off] = md;
-          pl[w][i][2][off] = l;
+          split3_one(p, h[e], md[e], l[e]);
         }
-        rl[i][e] = rl[i][e] * alpha[e] + group16_sum(ps);
+        const int off = col * PSTR + t * 16 + 4 * grp;
+        *reinterpret_cast<uint2*>(&pl[w][i][0][off]) = uint2{h[0] | (uint32_t{h[1]} << 16), h[2] | (uint32_t{h[3]} << 16)};
+        *reinterpret_cast<uint2*>(&pl[w][i][1][off]) = uint2{md[0] | (uint32_t{md[1]} << 16), md[2] | (uint32_t{md[3]} << 16)};
+        *reinterpret_cast<uint2*>(&pl[w][i][2][off]) = uint2{l[0] | (uint32_t{l[1]} << 16), l[2] | (uint32_t{l[3]} << 16)};
       }
-      // rescale the running output rows (C layout: element e is row 4 grp + e)
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      rl[i] = rl[i] * alpha + ps;
 #pragma unroll
-      for (int t = 0; t < NT_O; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[i][t][e] *= alpha[e];
+      for (int t = 0; t < NT_O; ++t) o[i][t] *= alpha;
     }
-    __syncthreads();  // vt written by all waves; this wave's planes written
+    // the planes are this wave's own: its LDS writes complete before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // output += P V: A = probability planes (query col, keys 8 grp ..), B = V^T
+    // O^T += V^T P^T: A = V^T (dimension c of the tile, keys 32 kk + 8 g ..),
+    // B = the probability planes (query c, keys 32 kk + 8 g ..)
 #pragma unroll
     for (int kk = 0; kk < BKEYS / 32; ++kk) {
       const int k0 = kk * 32 + grp * 8;
-      u32x4 vb[NT_O];
+      u32x4 va[NT_O];
 #pragma unroll
       for (int t = 0; t < NT_O; ++t)
-        vb[t] = *reinterpret_cast<const u32x4*>(&vt[(t * 16 + col) * VSTR + k0]);
+        va[t] = *reinterpret_cast<const u32x4*>(&vt[(t * 16 + col) * VSTR + k0]);
 #pragma unroll
       for (int i = 0; i < MTW; ++i) {
         const u32x4 ph = *reinterpret_cast<const u32x4*>(&pl[w][i][0][col * PSTR + k0]);
@@ -294,50 +364,75 @@ tree_attention_split_kernel(Args a) {
         const u32x4 pq = *reinterpret_cast<const u32x4*>(&pl[w][i][2][col * PSTR + k0]);
 #pragma unroll
         for (int t = 0; t < NT_O; ++t) {
-          o[i][t] = mfma(ph, vb[t], o[i][t]);
-          o[i][t] = mfma(pm, vb[t], o[i][t]);
-          o[i][t] = mfma(pq, vb[t], o[i][t]);
+          o[i][t] = mfma(va[t], ph, o[i][t]);
+          o[i][t] = mfma(va[t], pm, o[i][t]);
+          o[i][t] = mfma(va[t], pq, o[i][t]);
         }
       }
     }
   }
 
-  // partial results of this split: rows of real queries only
+  // partial results of this split: real queries only
   const int64_t base = (static_cast<int64_t>(split) * a.Hkv + g) * M;
 #pragma unroll
-  for (int i = 0; i < MTW; ++i)
+  for (int i = 0; i < MTW; ++i) {
+    const int m = (mt0 + w + WAVES * i) * 16 + col;
+    if (m >= M) continue;
+    float* dst = a.part_o + (base + m) * HD + 4 * grp;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = (w + WAVES * i) * 16 + 4 * grp + e;
-      if (m >= M) continue;
-      float* dst = a.part_o + (base + m) * HD;
-#pragma unroll
-      for (int t = 0; t < NT_O; ++t) dst[t * 16 + col] = o[i][t][e];
-      if (col == 0) {
-        a.part_ml[(base + m) * 2] = rm[i][e];
-        a.part_ml[(base + m) * 2 + 1] = rl[i][e];
-      }
+    for (int t = 0; t < NT_O; ++t) *reinterpret_cast<f32x4*>(dst + t * 16) = o[i][t];
+    if (grp == 0) {
+      a.part_ml[(base + m) * 2] = rm[i];
+      a.part_ml[(base + m) * 2 + 1] = rl[i];
     }
+  }
 }
 
 // out[r][hq][d] from the splits' partial results, merged in split order.
+// One workgroup per query vector, one thread per dimension.  The splits'
+// statistics are loaded one split per thread and their weights e^(m_s - M)
+// kept in LDS; each thread then adds its dimension over the splits in split
+// order, loading the partial outputs 16 splits at a time.
+constexpr int MAX_SPLITS = 260;  // plan_for keeps the context splits of a KV head <= 256
+
 __global__ void __launch_bounds__(HD)
 tree_attention_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                               int splits, int Hkv, int G, int R, int Hq, float* __restrict__ out) {
+  __shared__ float f[MAX_SPLITS];   // e^(m_s - M), 0 for a split without keys
+  __shared__ float lf[MAX_SPLITS];  // l_s * e^(m_s - M)
+  __shared__ float wmax[HD / 64];
   const int M = G * R;
   const int gm = blockIdx.x;  // g * M + m
   const int g = gm / M, m = gm % M;
   const int d = threadIdx.x;
+  auto stat = [&](int s) { return (static_cast<int64_t>(s) * Hkv + g) * M + m; };
   float mx = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_ml[((static_cast<int64_t>(s) * Hkv + g) * M + m) * 2]);
+  for (int s = d; s < splits; s += HD) mx = fmaxf(mx, part_ml[stat(s) * 2]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((d & 63) == 0) wmax[d >> 6] = mx;
+  __syncthreads();
+  mx = wmax[0];
+#pragma unroll
+  for (int i = 1; i < HD / 64; ++i) mx = fmaxf(mx, wmax[i]);
+  for (int s = d; s < splits; s += HD) {
+    const float ms = part_ml[stat(s) * 2];
+    const float e = ms == -__builtin_inff() ? 0.f : expf(ms - mx);
+    f[s] = e;
+    lf[s] = part_ml[stat(s) * 2 + 1] * e;
+  }
+  __syncthreads();
   float l = 0.f, acc = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const int64_t idx = (static_cast<int64_t>(s) * Hkv + g) * M + m;
-    const float ms = part_ml[idx * 2];
-    if (ms == -__builtin_inff()) continue;  // a split with no key for this row
-    const float f = expf(ms - mx);
-    l += part_ml[idx * 2 + 1] * f;
-    acc += part_o[idx * HD + d] * f;
+  for (int s0 = 0; s0 < splits; s0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = s0 + j < splits ? part_o[stat(s0 + j) * HD + d] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (s0 + j < splits && f[s0 + j] != 0.f) {
+        l += lf[s0 + j];
+        acc += v[j] * f[s0 + j];
+      }
   }
   const int r = m % R, hq = g * G + m / R;
   out[(static_cast<int64_t>(r) * Hq + hq) * HD + d] = acc / l;
@@ -362,7 +457,7 @@ tree_commit_kernel(uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t
 // workgroups per CU, at least one sub-block each
 int blocks_per_split(int ctx_len, int Hkv) {
   const int nblk = (ctx_len + BKEYS - 1) / BKEYS;
-  const int target = (512 + Hkv - 1) / Hkv;  // splits per KV head
+  const int target = (256 + Hkv - 1) / Hkv;  // splits per KV head (<= 256)
   int nb = (nblk + target - 1) / target;
   return nb < 1 ? 1 : nb;
 }
@@ -409,6 +504,7 @@ extern "C" int tree_attention_rows(const float* q, int R, int Hq, int D, const u
   if (!workspace || workspace_bytes < need) return VS_ERR_WORKSPACE;
   if (!vs::aligned16(workspace)) return VS_ERR_ALIGN;
   const Plan p = plan_for(R, Hq, Hkv, ctx_len);
+  if (p.splits > MAX_SPLITS) return VS_ERR_SHAPE;  // not reached: plan_for keeps splits <= 257
   Args a;
   a.q = q;
   a.kc = k_cache;
@@ -428,11 +524,10 @@ extern "C" int tree_attention_rows(const float* q, int R, int Hq, int D, const u
   a.ctx_splits = p.ctx_splits;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + static_cast<size_t>(p.splits) * Hkv * p.M * HD;
-  const dim3 grid(Hkv, p.splits), block(64 * WAVES);
-  const int mt = (p.M + 15) / 16;
-  if (mt <= WAVES) tree_attention_split_kernel<1><<<grid, block, 0, stream>>>(a);
-  else if (mt <= 2 * WAVES) tree_attention_split_kernel<2><<<grid, block, 0, stream>>>(a);
-  else tree_attention_split_kernel<4><<<grid, block, 0, stream>>>(a);
+  // one 16-query tile per wave, the query tiles spread over grid.z
+  const int mt = (p.M + 15) / 16;  // <= 16 (M <= 256)
+  const dim3 grid(Hkv, p.splits, (mt + WAVES - 1) / WAVES), block(64 * WAVES);
+  tree_attention_split_kernel<1, true><<<grid, block, 0, stream>>>(a);
   int st = vs::check_launch();
   if (st != VS_OK) return st;
   tree_attention_combine_kernel<<<dim3(Hkv * p.M), dim3(HD), 0, stream>>>(
