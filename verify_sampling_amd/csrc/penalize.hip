@@ -24,7 +24,7 @@
 // operation, in the documented order (the library is built without
 // floating-point contraction and with a correctly rounded divide).
 
-#include "vs_internal.h"
+#include "penalty_dev.h"
 
 namespace {
 
@@ -34,13 +34,6 @@ constexpr int TABLE_BITS = 13;
 constexpr int TABLE = 1 << TABLE_BITS;  // hash slots: at least twice the longest history
 static_assert(TABLE >= 2 * VS_MAX_WINDOW, "the table never fills");
 constexpr size_t TABLE_BYTES = 2 * TABLE * sizeof(int32_t);  // keys, then counts
-
-__device__ __forceinline__ float penalize_one(float l, int c, float rep, float pres, float freq) {
-  const float l1 = (l > 0.f) ? (l / rep) : (l * rep);
-  const float cf = static_cast<float>(c) * freq;
-  const float l2 = l1 - cf;
-  return l2 - pres;
-}
 
 __global__ void __launch_bounds__(THREADS)
 penalize_kernel(float* __restrict__ logits, const int32_t* __restrict__ ids, int64_t ld, int width,

@@ -93,19 +93,6 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
-// max / sum over the 16 lanes of a row group (lanes l with equal l / 16),
-// always in the same butterfly order
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // The scratch slots row `row` attends to, as a bit mask (bit s = slot s).
 __device__ __forceinline__ uint64_t ancestor_mask(const int32_t* parent, int row) {
   uint64_t m = 1ull;  // the root's slot
