@@ -54,7 +54,7 @@ enum vs_status {
                               fixed per-GPU area holds (topk_rows_noalloc)  */
 };
 
-#define VS_ABI_VERSION 3
+#define VS_ABI_VERSION 4
 #define VS_MAX_ROWS 24     /* verify rows R = k + 1 per projection call      */
 #define VS_POOL 64         /* width of the sampler's candidate pool          */
 #define VS_MAX_WINDOW 4096 /* longest penalty window                         */
@@ -297,6 +297,58 @@ int spec_accept_rows(int mode, int B, int k,
                      int q_ld, int64_t q_win_stride,
                      const int32_t* drafts, const int32_t* parent, const float* u,
                      int32_t* out_tokens, int32_t* out_n, hipStream_t stream);
+
+/*
+ * verify_window: the whole acceptance stage of one chain window in two
+ * launches.
+ *   [SD] §04: every verify row, and the draft's candidates for it, are
+ *   penalised against H_i before sampling and only the penalised row is
+ *   used; §03 "how hipfire does it": the 64-wide pool and the policy, the
+ *   same for p and q; §03 steps 1-4 and §02: rejection sampling or greedy
+ *   acceptance.
+ *
+ * The same results, bit for bit, as the sequence
+ *   penalize_rows(logits, NULL, ld, R, V, V, ctx, ctx_len, drafts, R - 1, ...)
+ *   topk_rows(logits, ld, R, V, 64, pool_vals, pool_ids, 64, ...)
+ *   sample_policy_rows(pool_vals, pool_ids, 64, R, 64, policy..., p_ids,
+ *                      p_probs, p_len, 64, NULL, NULL)
+ *   and, when temperature > 0 (sampled):
+ *     penalize_rows(q_vals', q_ids, q_ld, R - 1, q_m, V, ctx, ctx_len,
+ *                   drafts, R - 1, ...) on a copy q_vals' written to q_pen
+ *     sample_policy_rows(q_vals', q_ids, q_ld, R - 1, q_m, policy...,
+ *                        q_dist_ids, q_dist_probs, q_dist_len, q_ld, NULL, NULL)
+ *     spec_accept_rows(VS_ACCEPT_SAMPLED, 1, R - 1, p..., 64, R, q..., q_ld,
+ *                      R - 1, drafts, NULL, u, out_tokens, out_n)
+ *   else (greedy; the draft's candidates, q_* and u are not used and may be NULL):
+ *     spec_accept_rows(VS_ACCEPT_GREEDY, 1, R - 1, p..., ...)
+ *   logits   fp32 [R][ld], penalised in place (row i against H_i, the last
+ *            `window` tokens of ctx || drafts[0, min(i, R - 1)))
+ *   ctx      int32 [ctx_len], drafts int32 [R - 1] (device)
+ *   q_ids, q_vals  [R - 1][q_ld], q_m candidates per draft row; the inputs
+ *            are not changed; q_pen (nullable) receives the penalised values
+ *   u        fp32 [R][2] in [0, 1)
+ *   pool_vals, pool_ids [R][64]; p_ids, p_probs [R][64], p_len [R];
+ *   q_dist_ids, q_dist_probs [R - 1][q_ld], q_dist_len [R - 1];
+ *   out_tokens [R] (entries past the count are -1), out_n [1].
+ *   1 <= R <= VS_MAX_DRAFTS + 1, 64 <= V <= VS_MAX_VOCAB, ld >= V,
+ *   sampled: 1 <= q_m <= VS_POOL, q_m <= q_ld <= 2^24; penalty and policy
+ *   parameters as for penalize_rows and sample_policy_rows.
+ *   workspace: device memory of at least verify_window_workspace_bytes(R, V)
+ *   bytes (the chunk lists of topk_rows at K = 64), 16-byte aligned; no
+ *   initialisation needed, scratch after the call.
+ *   A VS_ERR_HIP from the second launch leaves the first one's writes in
+ *   place: the penalised logits, q_pen, the q distributions and, for
+ *   V <= 1024, the pools.
+ */
+size_t verify_window_workspace_bytes(int R, int V);
+int verify_window(float* logits, int64_t ld, int R, int V, const int32_t* ctx, int ctx_len,
+                  const int32_t* drafts, int window, float repeat, float presence, float frequency,
+                  const int32_t* q_ids, const float* q_vals, int64_t q_ld, int q_m, float* q_pen,
+                  float temperature, int top_k, float top_p, float min_p, const float* u,
+                  float* pool_vals, int32_t* pool_ids, int32_t* p_ids, float* p_probs,
+                  int32_t* p_len, int32_t* q_dist_ids, float* q_dist_probs, int32_t* q_dist_len,
+                  int32_t* out_tokens, int32_t* out_n, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /*
  * tree_attention_rows: attention of a token tree's verify rows under the tree

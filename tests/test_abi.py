@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = vs.library()
-    assert lib.vs_abi_version() == 3
+    assert lib.vs_abi_version() == 4
     assert lib.vs_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.vs_status_string(code) != b"unknown status"
@@ -177,3 +177,37 @@ def test_tree_attention_rejects_before_launch():
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, FAKE, 11, 8, 128, None) == -2  # past the cache
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, FAKE, 3, 8, 12, None) == -2    # D % 8
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, None, 0, 8, 128, None) == 0    # nothing to copy
+
+
+def test_verify_window_rejects_before_launch():
+    """The fused acceptance stage checks shapes, parameters and the workspace
+    on the host (its workspace is topk_rows' at K = 64)."""
+    lib = vs.library()
+    V = 151936
+    assert lib.verify_window_workspace_bytes(4, V) == lib.topk_rows_workspace_bytes(4, V, 64)
+    assert lib.verify_window_workspace_bytes(4, 1024) == 0
+    ws = lib.verify_window_workspace_bytes(4, V)
+    base = dict(logits=FAKE, ld=V, R=4, V=V, ctx=FAKE, n_ctx=100, drafts=FAKE, window=64, rep=1.1,
+                pres=1.5, freq=0.2, qi=FAKE, qv=FAKE, q_ld=8, q_m=8, q_pen=None, T=0.7, top_k=20,
+                top_p=0.95, min_p=0.05, u=FAKE, pv=FAKE, pi=FAKE, di=FAKE, dp=FAKE, dl=FAKE, qdi=FAKE,
+                qdp=FAKE, qdl=FAKE, tok=FAKE, n=FAKE, ws=FAKE, nws=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.verify_window(*a.values(), None)
+
+    assert call(logits=None) == -1
+    assert call(R=0) == -2
+    assert call(R=65) == -2                      # at most 64 rows
+    assert call(V=63, ld=63) == -2               # the pool needs 64 entries
+    assert call(ld=V - 1) == -2
+    assert call(drafts=None) == -1
+    assert call(window=5000) == -3
+    assert call(rep=0.0) == -3
+    assert call(T=float("nan")) == -3
+    assert call(u=None) == -1                    # sampled needs uniforms
+    assert call(qi=None) == -1                   # and the draft's candidates
+    assert call(q_m=65, q_ld=65) == -2
+    assert call(q_ld=7) == -2                    # q_ld < q_m
+    assert call(nws=ws - 1) == -5
+    assert call(ws=ctypes.c_void_p(0x100008)) == -6

@@ -30,6 +30,8 @@ __all__ = [
     "topk_rows_noalloc",
     "sample_policy_rows",
     "spec_accept_rows",
+    "verify_window",
+    "verify_window_workspace_bytes",
     "choose_depth",
     "lookup_tree",
     "tree_attention_rows",
@@ -65,6 +67,8 @@ EXPORTED_SYMBOLS = (
     "topk_rows_noalloc",
     "sample_policy_rows",
     "spec_accept_rows",
+    "verify_window_workspace_bytes",
+    "verify_window",
     "tree_attention_rows_workspace_bytes",
     "tree_attention_rows",
     "tree_commit_kv",
@@ -99,6 +103,9 @@ _SIGNATURES = {
     "sample_policy_rows": ([P, P, I64, I32, I32, F32, I32, F32, F32, P, P, P, I64, P, P, P], I32),
     "spec_accept_rows": ([I32, I32, I32, P, P, P, I32, I64, P, P, P, I32, I64, P, P, P, P, P, P],
                          I32),
+    "verify_window_workspace_bytes": ([I32, I32], SZ),
+    "verify_window": ([P, I64, I32, I32, P, I32, P, I32, F32, F32, F32, P, P, I64, I32, P, F32, I32, F32,
+                       F32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
     "tree_attention_rows_workspace_bytes": ([I32, I32, I32, I32], SZ),
     "tree_attention_rows": ([P, I32, I32, I32, P, P, I64, I32, P, P, I32, P, I32, F32, P, P, SZ, P], I32),
     "tree_commit_kv": ([P, P, I64, I32, P, P, I32, P, I32, I32, I32, P], I32),
@@ -516,6 +523,101 @@ def spec_accept_rows(mode, drafts, p, q=None, *, u=None, parent=None, p_win_stri
                                     n_ptr, _stream(stream))
     _check(st, "spec_accept_rows")
     return tokens, n_emitted
+
+
+def verify_window_workspace_bytes(R: int, V: int) -> int:
+    return int(library().verify_window_workspace_bytes(R, V))
+
+
+def verify_window(logits, ctx, drafts, *, window, repeat, presence, frequency, temperature, top_k,
+                  top_p, min_p, q_ids=None, q_vals=None, u=None, out=None, workspace=None,
+                  stream=None):
+    """The acceptance stage of one chain window in two launches.
+
+    logits float32 [R][V] (penalised in place); ctx int32 [n] and drafts
+    int32 [R - 1] 1-D device tensors.  Sampled (temperature > 0) also needs
+    q_ids int32 / q_vals float32 [R - 1][M] (equal strides; not changed) and
+    u float32 [R][2].  Returns a dict: tokens int32 [R] (-1 past the count),
+    n int32 [1], pool_vals / pool_ids [R][64], p = (ids, probs, len) of the
+    target rows, q = (ids, probs, len) and q_pen (the penalised candidates)
+    in sampled mode, else None.  out: an optional dict of the same outputs,
+    preallocated (q entries [R - 1][ld of q_vals]).
+    """
+    import torch
+
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise VerifySamplingError("logits must be a 2-D torch tensor [R][V]")
+    R, V = logits.shape
+    k = R - 1
+    dev = logits.device
+    l_ptr, ld = _mat(logits, "logits", R, V, torch.float32, dev)
+    c_ptr, n_ctx = _ids1d(ctx, "ctx", torch.int32, dev)
+    d_ptr, n_d = _ids1d(drafts, "drafts", torch.int32, dev)
+    if n_d != k:
+        raise VerifySamplingError(f"{R} rows verify {k} drafts, got {n_d}")
+    sampled = float(temperature) > 0
+    qi_ptr = qv_ptr = u_ptr = None
+    q_ld, q_m = 1, 1
+    if sampled:
+        u_ptr = _vec(u, "u", R * 2, torch.float32, dev)
+        if k > 0:
+            qv_ptr, q_ld = _mat(q_vals, "q_vals", k, 1, torch.float32, dev)
+            q_m = q_vals.shape[1]
+            qi_ptr, _ = _mat(q_ids, "q_ids", k, q_m, torch.int32, dev)
+            if tuple(q_ids.shape) != tuple(q_vals.shape) or q_ids.stride() != q_vals.stride():
+                raise VerifySamplingError("q_ids must match q_vals in shape and strides")
+            if q_m > POOL:
+                raise VerifySamplingError(f"q rows hold at most {POOL} candidates, got {q_m}")
+    if out is None:
+        out = dict(tokens=torch.empty((R,), dtype=torch.int32, device=dev),
+                   n=torch.empty((1,), dtype=torch.int32, device=dev),
+                   pool_vals=torch.empty((R, POOL), dtype=torch.float32, device=dev),
+                   pool_ids=torch.empty((R, POOL), dtype=torch.int32, device=dev),
+                   p=(torch.empty((R, POOL), dtype=torch.int32, device=dev),
+                      torch.empty((R, POOL), dtype=torch.float32, device=dev),
+                      torch.empty((R,), dtype=torch.int32, device=dev)),
+                   q=None, q_pen=None)
+        if sampled and k > 0:
+            out["q"] = (torch.empty((k, q_ld), dtype=torch.int32, device=dev),
+                        torch.empty((k, q_ld), dtype=torch.float32, device=dev),
+                        torch.empty((k,), dtype=torch.int32, device=dev))
+            out["q_pen"] = torch.empty((k, q_ld), dtype=torch.float32, device=dev)
+
+    def dense(t, name, rows, cols, dtype):
+        ptr = _vec(t, name, rows * cols, dtype, dev)
+        if tuple(t.shape) != (rows, cols):
+            raise VerifySamplingError(f"{name} must be [{rows}][{cols}], got {list(t.shape)}")
+        return ptr
+
+    t_ptr = _vec(out["tokens"], "tokens", R, torch.int32, dev)
+    n_ptr = _vec(out["n"], "n", 1, torch.int32, dev)
+    pv_ptr = dense(out["pool_vals"], "pool_vals", R, POOL, torch.float32)
+    pi_ptr = dense(out["pool_ids"], "pool_ids", R, POOL, torch.int32)
+    p_ids, p_probs, p_len = out["p"]
+    di_ptr = dense(p_ids, "p_ids", R, POOL, torch.int32)
+    dp_ptr = dense(p_probs, "p_probs", R, POOL, torch.float32)
+    dl_ptr = _vec(p_len, "p_len", R, torch.int32, dev)
+    qdi_ptr = qdp_ptr = qdl_ptr = qp_ptr = None
+    if sampled and k > 0:
+        if out.get("q") is None:
+            raise VerifySamplingError("out['q'] is required in sampled mode")
+        q_d_ids, q_d_probs, q_d_len = out["q"]
+        qdi_ptr = dense(q_d_ids, "q_dist_ids", k, q_ld, torch.int32)
+        qdp_ptr = dense(q_d_probs, "q_dist_probs", k, q_ld, torch.float32)
+        qdl_ptr = _vec(q_d_len, "q_dist_len", k, torch.int32, dev)
+        if out.get("q_pen") is not None:
+            qp_ptr = dense(out["q_pen"], "q_pen", k, q_ld, torch.float32)
+    need = verify_window_workspace_bytes(R, V)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _workspace(workspace, "workspace", dev)
+    st = library().verify_window(l_ptr, ld, R, V, c_ptr, n_ctx, d_ptr, int(window), float(repeat),
+                                 float(presence), float(frequency), qi_ptr, qv_ptr, q_ld, q_m, qp_ptr,
+                                 float(temperature), int(top_k), float(top_p), float(min_p), u_ptr,
+                                 pv_ptr, pi_ptr, di_ptr, dp_ptr, dl_ptr, qdi_ptr, qdp_ptr, qdl_ptr,
+                                 t_ptr, n_ptr, ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "verify_window")
+    return out
 
 
 def _bf16_bits(t, name, dev):

@@ -1,0 +1,326 @@
+// verify_window: the acceptance stage of one verify window in two launches.
+//
+// "Speculative decoding on RDNA": §04 (every verify row, and the draft's
+// candidates for it, penalised against H_i, the last W tokens of prompt ||
+// emitted || drafts[0, i); only the penalised row leaves the GPU), §03 "how
+// hipfire does it" (the 64-wide pool, then temperature, top-k, min-p and
+// top-p; the same policy for the draft's re-scored candidates), §03 steps
+// 1-4 and §02 (rejection sampling, greedy acceptance).
+//
+// The same work as penalize_rows (target rows and candidates), topk_rows
+// (K = 64), sample_policy_rows (p and q) and spec_accept_rows (sampled or
+// greedy), with the same device code for every stage, so the same bits, in
+// two launches instead of seven:
+//  * select: one wave per (row, 1024- or 4096-element chunk) of the target
+//    rows.  The chunk's values are loaded, the row's penalties are applied to
+//    those of its history tokens that fall in the chunk (in the registers,
+//    and written back to the row, which is penalised in place), then the
+//    chunk's top 64 are selected as topk_rows does.  Extra waves, one per
+//    draft row, penalise its candidates against the same history and compute
+//    the draft's policy distribution.
+//  * finish: one workgroup merges each row's chunk lists into its pool, runs
+//    the target's policy on it, and then one wave accepts the drafts.  Pools
+//    and distributions pass through LDS and are also written out.
+
+#include "accept_dev.h"
+#include "penalty_dev.h"
+#include "policy_dev.h"
+#include "topk_dev.h"
+
+namespace {
+
+constexpr int WIN_K = VS_POOL;     // pool width
+constexpr int FIN_WAVES = 4;       // waves of the finish workgroup
+constexpr int MAX_WIN_ROWS = VS_MAX_DRAFTS + 1;
+
+// H_row for every row: the last `window` tokens of ctx || drafts[0, min(row, k)).
+struct History {
+  const int32_t* ctx;
+  const int32_t* drafts;
+  int ctx_len, k, V, window;
+
+  // H_row's length; start: the position of its first token in ctx || drafts
+  __device__ __forceinline__ int span(int row, int64_t& start) const {
+    const int nd = row < k ? row : k;
+    const int64_t total = static_cast<int64_t>(ctx_len) + nd;
+    const int hlen = static_cast<int>(total < window ? total : window);
+    start = total - hlen;
+    return hlen;
+  }
+  // token j of a history starting at `start` (-1 for ids outside the
+  // vocabulary, which never match)
+  __device__ __forceinline__ int32_t token(int64_t start, int j) const {
+    const int64_t pos = start + j;
+    const int32_t t = pos < ctx_len ? ctx[pos] : drafts[pos - ctx_len];
+    return (t >= 0 && t < V) ? t : -1;
+  }
+};
+
+struct Penalty {
+  float rep, pres, freq;
+};
+
+struct WinArgs {
+  float* logits;  // [R][ld] target rows, penalised in place
+  int64_t ld;
+  int R;
+  History h;      // h.k = R - 1 drafts
+  Penalty pen;
+  bool sampled;
+  const int32_t* q_ids;  // [k][q_ld], q_m candidates per row
+  const float* q_vals;
+  int64_t q_ld;
+  int q_m;
+  float* q_pen;          // nullable: penalised candidate logits [k][q_ld]
+  float temperature;
+  int k_eff;
+  float top_p, min_p;
+  const float* u;        // [R][2]
+  float* pool_vals;      // [R][64]
+  int32_t* pool_ids;
+  int32_t* p_ids;        // [R][64]
+  float* p_probs;
+  int32_t* p_len;        // [R]
+  int32_t* q_dist_ids;   // [k][q_ld]
+  float* q_dist_probs;
+  int32_t* q_dist_len;   // [k]
+  int32_t* out_tokens;   // [R]
+  int32_t* out_n;
+  uint64_t* ws;
+  int chunks, lg_jp, lg_j2;
+};
+
+// The select stage's hook: the penalties of target row `row` on its history
+// tokens in [base, base + n).  Each distinct token is handled once, at its
+// first history position, with its count over the whole history, by the
+// lane that holds it (element j of lane l is chunk index 256 (j / 4) + 4 l +
+// j % 4), which also writes it back to the row with a device-coherent store.
+struct ChunkPenalty {
+  History h;
+  Penalty pen;
+  int row;
+  template <int NPL>
+  __device__ __forceinline__ void operator()(float (&x)[NPL], float* xrow, int base, int n) const {
+    if (h.window == 0) return;
+    const int lane = threadIdx.x & 63;
+    int64_t start;
+    const int hlen = h.span(row, start);
+    for (int h0 = 0; h0 < hlen; h0 += 64) {  // uniform
+      const int32_t t = h0 + lane < hlen ? h.token(start, h0 + lane) : -1;
+      uint64_t inr = __ballot(t >= base && t < base + n);
+      while (inr) {  // uniform
+        const int src = __ffsll(static_cast<long long>(inr)) - 1;
+        inr &= inr - 1;
+        const int32_t tk = vs::bcast(t, src);
+        const int pos = h0 + src;
+        bool first = true;
+        int c = 0;
+        for (int g0 = 0; g0 < hlen; g0 += 64) {  // uniform
+          const int32_t tt = g0 == h0 ? t : (g0 + lane < hlen ? h.token(start, g0 + lane) : -1);
+          const uint64_t eq = __ballot(tt == tk);
+          c += __popcll(eq);
+          const int before = pos - g0;  // positions of this batch before pos
+          if (before > 0 && (before >= 64 ? eq : (eq & ((1ull << before) - 1ull))) != 0ull) first = false;
+        }
+        if (!first) continue;
+        const int li = tk - base;
+        const int owner = (li & 255) >> 2;
+        const int jreg = ((li >> 8) << 2) | (li & 3);
+        if (lane == owner) {
+          float nv = 0.f;
+#pragma unroll
+          for (int q = 0; q < NPL; ++q) {
+            if (q == jreg) {  // uniform: no dynamic register index
+              x[q] = penalize_one(x[q], c, pen.rep, pen.pres, pen.freq);
+              nv = x[q];
+            }
+          }
+          __hip_atomic_store(xrow + tk, nv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before any reload of the chunk
+  }
+};
+
+// Draft row i: its candidates penalised against H_i, then its policy.
+__device__ __forceinline__ void draft_row(const WinArgs& a, int i, float* vrow, int32_t* irow, double* run) {
+  const int lane = threadIdx.x & 63;
+  const bool real = lane < a.q_m;
+  const int64_t off = static_cast<int64_t>(i) * a.q_ld + lane;
+  const int32_t id = real ? a.q_ids[off] : -1;
+  float v = real ? a.q_vals[off] : 0.f;
+  if (a.h.window > 0) {
+    int64_t start;
+    const int hlen = a.h.span(i, start);
+    const bool in_vocab = id >= 0 && id < a.h.V;  // other ids (empty slots) are never penalised
+    int c = 0;
+    for (int h0 = 0; h0 < hlen; h0 += 64) {  // uniform
+      const int32_t t = h0 + lane < hlen ? a.h.token(start, h0 + lane) : -1;
+      const int nb = hlen - h0 < 64 ? hlen - h0 : 64;
+      for (int j = 0; j < nb; ++j) c += vs::bcast(t, j) == id;
+    }
+    if (real && in_vocab && c > 0) v = penalize_one(v, c, a.pen.rep, a.pen.pres, a.pen.freq);
+  }
+  if (real) {
+    vrow[lane] = v;
+    irow[lane] = id;
+    if (a.q_pen) a.q_pen[off] = v;
+  }
+  vs::wave_lds_sync();
+  const int64_t drow = static_cast<int64_t>(i) * a.q_ld;
+  policy_row(vrow, irow, a.q_m, a.temperature, a.k_eff, a.top_p, a.min_p, a.q_dist_ids + drow,
+             a.q_dist_probs + drow, a.q_dist_len + i, nullptr, nullptr, run);
+}
+
+struct DraftShared {
+  float v[64];
+  int32_t id[64];
+  double run[64];
+};
+
+template <int NPL>
+__global__ void __launch_bounds__(64 * WAVES)
+window_select_kernel(WinArgs a) {
+  __shared__ union {
+    WaveShared chunk;
+    DraftShared draft;
+  } shared[WAVES];
+  const int w = vs::wave_index();
+  const int unit = blockIdx.x * WAVES + w;
+  const int cunits = a.R * a.chunks;
+  if (unit < cunits) {
+    const int row = unit / a.chunks, chunk = unit - row * a.chunks;
+    chunk_unit<NPL, 4, true>(shared[w].chunk, a.logits, a.ld, row, chunk, a.h.V, WIN_K, a.chunks, a.ws,
+                             a.pool_vals, a.pool_ids, WIN_K, ChunkPenalty{a.h, a.pen, row});
+  } else if (a.sampled && unit < cunits + a.h.k) {
+    DraftShared& d = shared[w].draft;
+    draft_row(a, unit - cunits, d.v, d.id, d.run);
+  }
+}
+
+__global__ void __launch_bounds__(64 * FIN_WAVES)
+window_finish_kernel(WinArgs a) {
+  __shared__ MergeShared msh[FIN_WAVES];
+  __shared__ float pv[FIN_WAVES][WIN_K];  // each wave's current pool
+  __shared__ int32_t pi[FIN_WAVES][WIN_K];
+  __shared__ int32_t dids[MAX_WIN_ROWS][WIN_K];
+  __shared__ float dprobs[MAX_WIN_ROWS][WIN_K];
+  __shared__ int32_t dlen[MAX_WIN_ROWS];
+  __shared__ double run[FIN_WAVES][64];
+  const int lane = threadIdx.x & 63;
+  const int w = vs::wave_index();
+  for (int row = w; row < a.R; row += FIN_WAVES) {  // uniform per wave
+    if (a.chunks > 1) {
+      merge_row(msh[w], a.logits, a.ld, row, a.h.V, WIN_K, a.chunks, a.lg_jp, a.lg_j2, a.ws, pv[w], pi[w]);
+      vs::wave_lds_sync();
+      a.pool_vals[row * WIN_K + lane] = pv[w][lane];
+      a.pool_ids[row * WIN_K + lane] = pi[w][lane];
+    } else {  // the select stage wrote the pool
+      vs::wave_lds_sync();  // the previous row's pool has been read
+      pv[w][lane] = a.pool_vals[row * WIN_K + lane];
+      pi[w][lane] = a.pool_ids[row * WIN_K + lane];
+      vs::wave_lds_sync();
+    }
+    policy_row(pv[w], pi[w], WIN_K, a.temperature, a.k_eff, a.top_p, a.min_p, dids[row], dprobs[row],
+               &dlen[row], nullptr, nullptr, run[w]);
+    vs::wave_lds_sync();
+    a.p_ids[row * WIN_K + lane] = dids[row][lane];
+    a.p_probs[row * WIN_K + lane] = dprobs[row][lane];
+    if (lane == 0) a.p_len[row] = dlen[row];
+  }
+  __syncthreads();
+  if (w == 0) {
+    const Dists d{&dids[0][0], &dprobs[0][0], dlen, WIN_K, a.h.k + 1,
+                  a.q_dist_ids, a.q_dist_probs, a.q_dist_len, static_cast<int>(a.q_ld), a.h.k};
+    accept_window(a.sampled ? VS_ACCEPT_SAMPLED : VS_ACCEPT_GREEDY, 0, a.h.k, d, a.h.drafts, nullptr, a.u,
+                  a.out_tokens, a.out_n, run[0]);
+  }
+}
+
+}  // namespace
+
+extern "C" size_t verify_window_workspace_bytes(int R, int V) {
+  if (R < 1 || V < WIN_K) return 0;
+  const Plan p = plan_for(R, V);
+  return p.chunks <= 1 ? 0 : static_cast<size_t>(R) * p.chunks * WIN_K * sizeof(uint64_t);
+}
+
+extern "C" int verify_window(float* logits, int64_t ld, int R, int V, const int32_t* ctx, int ctx_len,
+                             const int32_t* drafts, int window, float repeat, float presence,
+                             float frequency, const int32_t* q_ids, const float* q_vals, int64_t q_ld,
+                             int q_m, float* q_pen, float temperature, int top_k, float top_p,
+                             float min_p, const float* u, float* pool_vals, int32_t* pool_ids,
+                             int32_t* p_ids, float* p_probs, int32_t* p_len, int32_t* q_dist_ids,
+                             float* q_dist_probs, int32_t* q_dist_len, int32_t* out_tokens,
+                             int32_t* out_n, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!logits || !pool_vals || !pool_ids || !p_ids || !p_probs || !p_len || !out_tokens || !out_n)
+    return VS_ERR_NULL;
+  if (R < 1 || R > MAX_WIN_ROWS || V < WIN_K || V > VS_MAX_VOCAB || ld < V) return VS_ERR_SHAPE;
+  const int k = R - 1;
+  if (ctx_len < 0) return VS_ERR_SHAPE;
+  if ((ctx_len > 0 && !ctx) || (k > 0 && !drafts)) return VS_ERR_NULL;
+  if (window < 0 || window > VS_MAX_WINDOW) return VS_ERR_PARAM;
+  if (!(repeat > 0.f) || !__builtin_isfinite(repeat) || !__builtin_isfinite(presence) ||
+      !__builtin_isfinite(frequency))
+    return VS_ERR_PARAM;
+  if (__builtin_isnan(temperature) || __builtin_isinf(temperature) || __builtin_isnan(top_p) ||
+      __builtin_isnan(min_p))
+    return VS_ERR_PARAM;
+  const bool sampled = temperature > 0.f;
+  if (sampled) {
+    if (!u) return VS_ERR_NULL;
+    if (k > 0) {
+      if (!q_ids || !q_vals || !q_dist_ids || !q_dist_probs || !q_dist_len) return VS_ERR_NULL;
+      if (q_m < 1 || q_m > VS_POOL || q_ld < q_m || q_ld > (1 << 24)) return VS_ERR_SHAPE;
+    }
+  }
+  const size_t need = verify_window_workspace_bytes(R, V);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return VS_ERR_WORKSPACE;
+  if (need > 0 && !vs::aligned16(workspace)) return VS_ERR_ALIGN;
+
+  const Plan p = plan_for(R, V);
+  WinArgs a;
+  a.logits = logits;
+  a.ld = ld;
+  a.R = R;
+  // nothing to penalise without a window or a history (as penalize_rows)
+  a.h = History{ctx, drafts, ctx_len, k, V, (ctx_len == 0 && k == 0) ? 0 : window};
+  a.pen = Penalty{repeat, presence, frequency};
+  a.sampled = sampled;
+  a.q_ids = q_ids;
+  a.q_vals = q_vals;
+  a.q_ld = q_ld;
+  a.q_m = q_m;
+  a.q_pen = q_pen;
+  a.temperature = temperature;
+  a.k_eff = policy_k_eff(top_k);
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.u = u;
+  a.pool_vals = pool_vals;
+  a.pool_ids = pool_ids;
+  a.p_ids = p_ids;
+  a.p_probs = p_probs;
+  a.p_len = p_len;
+  a.q_dist_ids = q_dist_ids;
+  a.q_dist_probs = q_dist_probs;
+  a.q_dist_len = q_dist_len;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n;
+  a.ws = static_cast<uint64_t*>(workspace);
+  a.chunks = p.chunks;
+  merge_reads(p.chunks, WIN_K, a.lg_jp, a.lg_j2);
+
+  const int units = R * p.chunks + (sampled ? k : 0);
+  const dim3 grid(static_cast<unsigned>((units + WAVES - 1) / WAVES)), block(64 * WAVES);
+  if (p.small)
+    window_select_kernel<16><<<grid, block, 0, stream>>>(a);
+  else
+    window_select_kernel<64><<<grid, block, 0, stream>>>(a);
+  int st = vs::check_launch();
+  if (st != VS_OK) return st;
+  window_finish_kernel<<<dim3(1), dim3(64 * FIN_WAVES), 0, stream>>>(a);
+  return vs::check_launch();
+}
