@@ -501,6 +501,69 @@ __device__ __forceinline__ void merge_rank_write(MergeShared& sh, int c, int K, 
   }
 }
 
+// Merge of a row whose chunk maxima are the threshold's entries and fit three
+// to a lane (K <= chunks <= 192, K even), lane-major: lane l holds the first
+// WIDE_READ entries of chunks l, l + 64 and l + 128.  With v the K-th
+// largest chunk maximum (as in merge_row, step 1), each chunk's survivors
+// (keys >= v) are a prefix of its sorted list, so their positions in the
+// survivor list follow from one prefix sum of the per-lane counts over the
+// lanes (five ballots of the counts' bits), with no compaction rounds.
+// Returns false, having written only LDS, when a chunk may hold more
+// survivors than its entries read (all WIDE_READ survive, K > WIDE_READ) or
+// more than CAND survive; merge_row then takes its general path.
+constexpr int WIDE_SLOTS = 3;
+constexpr int WIDE_READ = 8;
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bool merge_row_wide(MergeShared& sh, const uint64_t* __restrict__ src, int chunks, int K,
+                                               int& count) {
+  const int lane = threadIdx.x & 63;
+  uint64_t e[WIDE_SLOTS][WIDE_READ];
+#pragma unroll
+  for (int s = 0; s < WIDE_SLOTS; ++s) {
+    const int c = lane + 64 * s;
+#pragma unroll
+    for (int j = 0; j < WIDE_READ; j += 2) {
+      u64x2 pr = {0ull, 0ull};
+      if (c < chunks) pr = *reinterpret_cast<const u64x2*>(src + c * K + j);  // K even: 16-byte aligned
+      e[s][j] = pr.x;
+      e[s][j + 1] = pr.y;
+    }
+  }
+  uint64_t m[WIDE_SLOTS];
+#pragma unroll
+  for (int s = 0; s < WIDE_SLOTS; ++s) m[s] = e[s][0];  // 0 for chunks past the row's
+  const uint64_t v = wave_kth_largest<WIDE_SLOTS>(m, K);
+  int n[WIDE_SLOTS];
+  int total = 0;
+  bool full = false;
+#pragma unroll
+  for (int s = 0; s < WIDE_SLOTS; ++s) {
+    n[s] = 0;
+#pragma unroll
+    for (int j = 0; j < WIDE_READ; ++j) n[s] += e[s][j] != 0ull && e[s][j] >= v;
+    total += n[s];
+    full = full || n[s] == WIDE_READ;
+  }
+  if (K > WIDE_READ && __ballot(full) != 0ull) return false;  // uniform
+  // exclusive prefix of total over the lanes (total <= 24: five bits)
+  int pos = 0;
+  count = 0;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {
+    const uint64_t bb = __ballot((total >> b) & 1);
+    pos += static_cast<int>(lanes_below(bb)) << b;
+    count += __popcll(bb) << b;
+  }
+  if (count > CAND) return false;  // uniform
+#pragma unroll
+  for (int s = 0; s < WIDE_SLOTS; ++s)
+#pragma unroll
+    for (int j = 0; j < WIDE_READ; ++j)
+      if (j < n[s]) sh.key[pos++] = e[s][j];
+  return true;
+}
+
 // Merge stage: one wavefront per row over the chunks' candidate lists (K
 // keys per chunk, sorted descending, zero-padded).
 //   1. v = the K-th largest key among the first jp entries of every chunk
@@ -514,7 +577,8 @@ __device__ __forceinline__ void merge_rank_write(MergeShared& sh, int c, int K, 
 //   3. ranks among the survivors, as in the chunk stage.
 // More than CAND survivors (ties resolved by index crowd the top K into the
 // first chunks, as in the all-equal row with K = 64) take a second,
-// narrower round whose survivors are bounded by CAND.
+// narrower round whose survivors are bounded by CAND.  Rows of K to 192
+// chunks first try merge_row_wide, steps 1-2 in fewer instructions.
 // ovals, oidx: the row's K outputs (global or LDS).
 __device__ __forceinline__ void merge_row(MergeShared& sh, const float* __restrict__ X, int64_t ldx, int row,
                                           int V, int K, int chunks, int lg_jp, int lg_j2,
@@ -523,141 +587,146 @@ __device__ __forceinline__ void merge_row(MergeShared& sh, const float* __restri
   const int n = chunks * K;
   const uint64_t* src = ws + static_cast<int64_t>(row) * n;
   const int jp = 1 << lg_jp, j2 = 1 << lg_j2;
-
-  // both reads in one round: the threshold's entries (chunks * jp <= 256)
-  // and the first j2 entries of every chunk
-  uint64_t m[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = lane + 64 * i;
-    const int c = t >> lg_jp, j = t & (jp - 1);
-    m[i] = (c < chunks && j < K) ? src[c * K + j] : 0ull;
-  }
-  uint64_t e[MERGE_LOADS];
-  const int n2 = chunks << lg_j2;
-#pragma unroll
-  for (int i = 0; i < MERGE_LOADS; ++i) {
-    e[i] = 0ull;
-    if (64 * i < n2) {  // uniform
-      const int s = lane + 64 * i;
-      const int c = s >> lg_j2, j = s & (j2 - 1);
-      if (c < chunks && j < K) e[i] = src[c * K + j];
-    }
-  }
-
-  // 1: the K-th largest key of the threshold's entries (0 if fewer than K)
-  const uint64_t v = wave_kth_largest<4>(m, K);
-
-  // 2: survivors of the first round, and the chunks to read on
-  int count = 0, n_cont = 0;
-#pragma unroll
-  for (int i = 0; i < MERGE_LOADS; ++i) {
-    if (64 * i < n2) {
-      const bool live = e[i] != 0ull && e[i] >= v;
-      compact_key(sh, count, live, e[i]);
-      if (j2 < K) {
-        const int s = lane + 64 * i;
-        const bool more = live && (s & (j2 - 1)) == j2 - 1;  // its chunk's last entry read
-        const uint64_t mm = __ballot(more);
-        if (more) sh.cont[lanes_below(mm, static_cast<uint32_t>(n_cont))] = static_cast<uint32_t>(s >> lg_j2);
-        n_cont += __popcll(mm);
-      }
-    }
-  }
-  vs::wave_lds_sync();
-  if (n_cont > 0 && count <= CAND) {
-    // entries j2 .. K-1 of those chunks, P (a power of two >= K - j2) lanes per chunk
-    const int tail = K - j2;
-    const int lg_p = tail <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(tail - 1));
-    const int total = n_cont << lg_p;
-    for (int s0 = 0; s0 < total && count <= CAND; s0 += 64 * 8) {
-      uint64_t f[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = s0 + 64 * u + lane;
-        const int j = j2 + (s & ((1 << lg_p) - 1));
-        f[u] = 0ull;
-        if (s < total && j < K) f[u] = src[static_cast<int>(sh.cont[s >> lg_p]) * K + j];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) compact_key(sh, count, f[u] != 0ull && f[u] >= v, f[u]);
-    }
-  }
-
-  if (count > CAND) {
-    // Second round.  Only the chunks whose first entry is >= v can hold a
-    // top-K key: exactly K of them when jp = 1, else at most chunks < K.
-    // Their first jb entries (nrel * jb <= 64 * MERGE_LOADS, so jb >= 16
-    // when jb < K) give the exact K-th largest key v2 of that set; exactly
-    // K read entries are >= v2, so at most K / jb chunks have all jb read
-    // entries >= v2, and only those are read on.  That bounds the
-    // survivors by K * K / jb <= CAND.
-    vs::wave_lds_sync();  // the first round's survivors are dropped
-    int nrel = 0;
+  int count = 0;
+  const bool wide = lg_jp == 0 && chunks <= 64 * WIDE_SLOTS && (K & 1) == 0 && K >= WIDE_READ &&
+                    merge_row_wide(sh, src, chunks, K, count);
+  if (!wide) {
+    // both reads in one round: the threshold's entries (chunks * jp <= 256)
+    // and the first j2 entries of every chunk
+    uint64_t m[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = lane + 64 * i;
-      const bool rel = m[i] != 0ull && m[i] >= v && (t & (jp - 1)) == 0;
-      const uint64_t mm = __ballot(rel);
-      if (rel) sh.cont[lanes_below(mm, static_cast<uint32_t>(nrel))] = static_cast<uint32_t>(t >> lg_jp);
-      nrel += __popcll(mm);
+      const int c = t >> lg_jp, j = t & (jp - 1);
+      m[i] = (c < chunks && j < K) ? src[c * K + j] : 0ull;
     }
-    vs::wave_lds_sync();
-    int lg_jb = 31 - __builtin_clz(static_cast<unsigned>((64 * MERGE_LOADS) / (nrel > 0 ? nrel : 1)));
-    const int lg_k = K <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(K - 1));
-    lg_jb = lg_jb < lg_k ? lg_jb : lg_k;
-    const int jb = 1 << lg_jb;
-    const int nb = nrel << lg_jb;
+    uint64_t e[MERGE_LOADS];
+    const int n2 = chunks << lg_j2;
 #pragma unroll
     for (int i = 0; i < MERGE_LOADS; ++i) {
       e[i] = 0ull;
-      if (64 * i < nb) {  // uniform
+      if (64 * i < n2) {  // uniform
         const int s = lane + 64 * i;
-        const int r = s >> lg_jb, j = s & (jb - 1);
-        if (r < nrel && j < K) e[i] = src[static_cast<int>(sh.cont[r]) * K + j];
+        const int c = s >> lg_j2, j = s & (j2 - 1);
+        if (c < chunks && j < K) e[i] = src[c * K + j];
       }
     }
-    // (one bit per step: this rare path keeps its scalar registers few)
-    uint64_t v2 = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t cand = v2 | (1ull << bit);
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < MERGE_LOADS; ++i)
-        if (64 * i < nb) c += __popcll(__ballot(e[i] >= cand));
-      if (c >= K) v2 = cand;
-    }
+
+    // 1: the K-th largest key of the threshold's entries (0 if fewer than K)
+    const uint64_t v = wave_kth_largest<4>(m, K);
+
+    // 2: survivors of the first round, and the chunks to read on
     count = 0;
-    int nlong = 0;
+    int n_cont = 0;
 #pragma unroll
     for (int i = 0; i < MERGE_LOADS; ++i) {
-      if (64 * i < nb) {
-        const int s = lane + 64 * i;
-        const bool live = e[i] != 0ull && e[i] >= v2;
+      if (64 * i < n2) {
+        const bool live = e[i] != 0ull && e[i] >= v;
         compact_key(sh, count, live, e[i]);
-        if (jb < K) {
-          const bool more = live && (s & (jb - 1)) == jb - 1;
+        if (j2 < K) {
+          const int s = lane + 64 * i;
+          const bool more = live && (s & (j2 - 1)) == j2 - 1;  // its chunk's last entry read
           const uint64_t mm = __ballot(more);
-          // after the relevant list (<= 64 entries)
-          if (more) sh.cont[64 + lanes_below(mm, static_cast<uint32_t>(nlong))] = sh.cont[s >> lg_jb];
-          nlong += __popcll(mm);
+          if (more) sh.cont[lanes_below(mm, static_cast<uint32_t>(n_cont))] = static_cast<uint32_t>(s >> lg_j2);
+          n_cont += __popcll(mm);
         }
       }
     }
     vs::wave_lds_sync();
-    // entries jb .. K-1 of at most K / jb <= 4 chunks, 64 lanes per chunk
-    for (int u0 = 0; u0 < nlong; u0 += 4) {
-      uint64_t f[4];
+    if (n_cont > 0 && count <= CAND) {
+      // entries j2 .. K-1 of those chunks, P (a power of two >= K - j2) lanes per chunk
+      const int tail = K - j2;
+      const int lg_p = tail <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(tail - 1));
+      const int total = n_cont << lg_p;
+      for (int s0 = 0; s0 < total && count <= CAND; s0 += 64 * 8) {
+        uint64_t f[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = jb + lane;
-        f[u] = 0ull;
-        if (u0 + u < nlong && j < K) f[u] = src[static_cast<int>(sh.cont[64 + u0 + u]) * K + j];
+        for (int u = 0; u < 8; ++u) {
+          const int s = s0 + 64 * u + lane;
+          const int j = j2 + (s & ((1 << lg_p) - 1));
+          f[u] = 0ull;
+          if (s < total && j < K) f[u] = src[static_cast<int>(sh.cont[s >> lg_p]) * K + j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) compact_key(sh, count, f[u] != 0ull && f[u] >= v, f[u]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) compact_key(sh, count, f[u] != 0ull && f[u] >= v2, f[u]);
     }
-  }
+
+    if (count > CAND) {
+      // Second round.  Only the chunks whose first entry is >= v can hold a
+      // top-K key: exactly K of them when jp = 1, else at most chunks < K.
+      // Their first jb entries (nrel * jb <= 64 * MERGE_LOADS, so jb >= 16
+      // when jb < K) give the exact K-th largest key v2 of that set; exactly
+      // K read entries are >= v2, so at most K / jb chunks have all jb read
+      // entries >= v2, and only those are read on.  That bounds the
+      // survivors by K * K / jb <= CAND.
+      vs::wave_lds_sync();  // the first round's survivors are dropped
+      int nrel = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = lane + 64 * i;
+        const bool rel = m[i] != 0ull && m[i] >= v && (t & (jp - 1)) == 0;
+        const uint64_t mm = __ballot(rel);
+        if (rel) sh.cont[lanes_below(mm, static_cast<uint32_t>(nrel))] = static_cast<uint32_t>(t >> lg_jp);
+        nrel += __popcll(mm);
+      }
+      vs::wave_lds_sync();
+      int lg_jb = 31 - __builtin_clz(static_cast<unsigned>((64 * MERGE_LOADS) / (nrel > 0 ? nrel : 1)));
+      const int lg_k = K <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(K - 1));
+      lg_jb = lg_jb < lg_k ? lg_jb : lg_k;
+      const int jb = 1 << lg_jb;
+      const int nb = nrel << lg_jb;
+#pragma unroll
+      for (int i = 0; i < MERGE_LOADS; ++i) {
+        e[i] = 0ull;
+        if (64 * i < nb) {  // uniform
+          const int s = lane + 64 * i;
+          const int r = s >> lg_jb, j = s & (jb - 1);
+          if (r < nrel && j < K) e[i] = src[static_cast<int>(sh.cont[r]) * K + j];
+        }
+      }
+      // (one bit per step: this rare path keeps its scalar registers few)
+      uint64_t v2 = 0;
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = v2 | (1ull << bit);
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < MERGE_LOADS; ++i)
+          if (64 * i < nb) c += __popcll(__ballot(e[i] >= cand));
+        if (c >= K) v2 = cand;
+      }
+      count = 0;
+      int nlong = 0;
+#pragma unroll
+      for (int i = 0; i < MERGE_LOADS; ++i) {
+        if (64 * i < nb) {
+          const int s = lane + 64 * i;
+          const bool live = e[i] != 0ull && e[i] >= v2;
+          compact_key(sh, count, live, e[i]);
+          if (jb < K) {
+            const bool more = live && (s & (jb - 1)) == jb - 1;
+            const uint64_t mm = __ballot(more);
+            // after the relevant list (<= 64 entries)
+            if (more) sh.cont[64 + lanes_below(mm, static_cast<uint32_t>(nlong))] = sh.cont[s >> lg_jb];
+            nlong += __popcll(mm);
+          }
+        }
+      }
+      vs::wave_lds_sync();
+      // entries jb .. K-1 of at most K / jb <= 4 chunks, 64 lanes per chunk
+      for (int u0 = 0; u0 < nlong; u0 += 4) {
+        uint64_t f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = jb + lane;
+          f[u] = 0ull;
+          if (u0 + u < nlong && j < K) f[u] = src[static_cast<int>(sh.cont[64 + u0 + u]) * K + j];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) compact_key(sh, count, f[u] != 0ull && f[u] >= v2, f[u]);
+      }
+    }
+  }  // general path
 
   if (count > CAND) count = CAND;  // not reached: the rounds above bound the survivors
   vs::wave_lds_sync();

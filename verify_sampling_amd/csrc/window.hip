@@ -30,7 +30,7 @@
 namespace {
 
 constexpr int WIN_K = VS_POOL;     // pool width
-constexpr int FIN_WAVES = 4;       // waves of the finish workgroup
+constexpr int FIN_WAVES = 8;       // waves of the finish workgroup
 constexpr int MAX_WIN_ROWS = VS_MAX_DRAFTS + 1;
 
 // H_row for every row: the last `window` tokens of ctx || drafts[0, min(row, k)).
@@ -207,9 +207,39 @@ window_finish_kernel(WinArgs a) {
   __shared__ int32_t dids[MAX_WIN_ROWS][WIN_K];
   __shared__ float dprobs[MAX_WIN_ROWS][WIN_K];
   __shared__ int32_t dlen[MAX_WIN_ROWS];
+  __shared__ int32_t qids[MAX_WIN_ROWS - 1][WIN_K];
+  __shared__ float qprobs[MAX_WIN_ROWS - 1][WIN_K];
+  __shared__ int32_t qlen[MAX_WIN_ROWS - 1];
+  __shared__ float us[MAX_WIN_ROWS * 2];
+  __shared__ int32_t dr[MAX_WIN_ROWS - 1];
   __shared__ double run[FIN_WAVES][64];
   const int lane = threadIdx.x & 63;
   const int w = vs::wave_index();
+  const int k = a.h.k;
+
+  // the acceptance's other inputs (draft distributions, uniforms, drafts),
+  // loaded now and parked in LDS after the merges, so that their latency
+  // overlaps the merges instead of following them (draft rows past the
+  // first QPRE of each wave, windows of more than 16 drafts, are loaded
+  // when they are parked)
+  constexpr int QSLOTS = (MAX_WIN_ROWS - 1 + FIN_WAVES - 1) / FIN_WAVES;
+  constexpr int QPRE = 2;
+  int32_t qi_r[QPRE], ql_r[QPRE];
+  float qp_r[QPRE];
+  const bool qm = a.sampled && lane < a.q_m;
+#pragma unroll
+  for (int t = 0; t < QPRE; ++t) {
+    const int i = w + FIN_WAVES * t;
+    const bool live = a.sampled && i < k;
+    const int64_t off = static_cast<int64_t>(i) * a.q_ld + lane;
+    qi_r[t] = live && qm ? a.q_dist_ids[off] : -1;
+    qp_r[t] = live && qm ? a.q_dist_probs[off] : 0.f;
+    ql_r[t] = live && lane == 0 ? a.q_dist_len[i] : 0;
+  }
+  const int tid = static_cast<int>(threadIdx.x);
+  const float u_r = a.sampled && tid < 2 * a.R ? a.u[tid] : 0.f;
+  const int32_t d_r = tid < k ? a.h.drafts[tid] : 0;
+
   for (int row = w; row < a.R; row += FIN_WAVES) {  // uniform per wave
     if (a.chunks > 1) {
       merge_row(msh[w], a.logits, a.ld, row, a.h.V, WIN_K, a.chunks, a.lg_jp, a.lg_j2, a.ws, pv[w], pi[w]);
@@ -229,12 +259,21 @@ window_finish_kernel(WinArgs a) {
     a.p_probs[row * WIN_K + lane] = dprobs[row][lane];
     if (lane == 0) a.p_len[row] = dlen[row];
   }
+  for (int t = 0; t < QSLOTS; ++t) {
+    const int i = w + FIN_WAVES * t;
+    if (!(a.sampled && i < k)) break;  // uniform
+    const int64_t off = static_cast<int64_t>(i) * a.q_ld + lane;
+    qids[i][lane] = t < QPRE ? qi_r[t < QPRE ? t : 0] : (qm ? a.q_dist_ids[off] : -1);
+    qprobs[i][lane] = t < QPRE ? qp_r[t < QPRE ? t : 0] : (qm ? a.q_dist_probs[off] : 0.f);
+    if (lane == 0) qlen[i] = t < QPRE ? ql_r[t < QPRE ? t : 0] : a.q_dist_len[i];
+  }
+  if (tid < 2 * a.R) us[tid] = u_r;
+  if (tid < k) dr[tid] = d_r;
   __syncthreads();
   if (w == 0) {
-    const Dists d{&dids[0][0], &dprobs[0][0], dlen, WIN_K, a.h.k + 1,
-                  a.q_dist_ids, a.q_dist_probs, a.q_dist_len, static_cast<int>(a.q_ld), a.h.k};
-    accept_window(a.sampled ? VS_ACCEPT_SAMPLED : VS_ACCEPT_GREEDY, 0, a.h.k, d, a.h.drafts, nullptr, a.u,
-                  a.out_tokens, a.out_n, run[0]);
+    const Dists d{&dids[0][0], &dprobs[0][0], dlen, WIN_K, k + 1, &qids[0][0], &qprobs[0][0], qlen, WIN_K, k};
+    accept_window(a.sampled ? VS_ACCEPT_SAMPLED : VS_ACCEPT_GREEDY, 0, k, d, dr, nullptr, us, a.out_tokens,
+                  a.out_n, run[0]);
   }
 }
 
