@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (for scaling HBM traffic counters)")
+    ap.add_argument("--family-sweep", action="store_true",
+                    help="only time verify_gemv_rows per matrix on three model sizes "
+                         "(hidden 2560, 4096, 5120) for R = 1..24 and print that as the JSON line")
     return ap.parse_args()
 
 
@@ -558,6 +561,45 @@ def cpu_baseline(synth, R, budget_s=8.0):
             "accept_rows_per_s": R / acc_s}
 
 
+def family_sweep(torch, vs, synth, dev, reps=12, warmup=3):
+    """verify_gemv_rows alone on every fused projection and LM head of three
+    model sizes, each R = 1..24: median of `reps` HIP-event-timed calls after
+    `warmup`, with the matrix's algorithmic bytes over that time as a
+    fraction of the 8 TB/s peak.  Weights N(0, 0.02) bf16, activations
+    N(0, 1); the workspace is passed where the dispatch uses one."""
+    lib = vs.library()
+    X = torch.randn(24, max(K for f in synth.FAMILY_SHAPES.values() for _, K in f.values()),
+                    device=dev, dtype=torch.float32)
+    out = {}
+    for fam, shapes in synth.FAMILY_SHAPES.items():
+        for name, (N, K) in shapes.items():
+            W = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+            Y = torch.empty(24, N, device=dev, dtype=torch.float32)
+            nws = max(vs.verify_gemv_rows_workspace_bytes(N, K, R) for R in range(1, 25))
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+            per = {}
+            for R in range(1, 25):
+                need = vs.verify_gemv_rows_workspace_bytes(N, K, R)
+                args = (W.data_ptr(), K, N, K, X.data_ptr(), X.stride(0), R, Y.data_ptr(), N,
+                        ws.data_ptr() if need else None, need)
+
+                def call():
+                    st = lib.verify_gemv_rows(*args, torch.cuda.current_stream().cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(f"verify_gemv_rows failed with status {st}")
+
+                us = float(np.median(time_each(torch, call, reps, warmup))) * 1e3
+                nbytes = 2 * N * K + 4 * R * (K + N)
+                per[str(R)] = {"us": round(us, 2), "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                               "kernel": "split-K" if need else "row-block"}
+            out[f"{fam}/{name}"] = {"N": N, "K": K, "vs_R": per}
+            log(f"{fam}/{name} {N}x{K}: R1 {per['1']['frac_of_hbm_peak']}, R4 {per['4']['frac_of_hbm_peak']}, "
+                f"R24 {per['24']['frac_of_hbm_peak']}")
+            del W, Y, ws
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -573,6 +615,13 @@ def main():
     vs.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.family_sweep:
+        fam = family_sweep(torch, vs, synth, dev)
+        print(json.dumps({"metric": "verify_gemv_rows fraction of HBM peak per matrix, three model sizes",
+                          "unit": "fraction of 8 TB/s", "data": "synthetic", "n_gpus": 1,
+                          "timing": "median of 12 HIP-event-timed calls after 3 warm-ups per R",
+                          "family_sweep": fam}), flush=True)
+        return
     if args.copy_calibration:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

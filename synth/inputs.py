@@ -47,6 +47,7 @@ __all__ = [
     "LAYER_SHAPES",
     "LAYER_SHAPES_FUSED",
     "LM_HEAD_SHAPE",
+    "FAMILY_SHAPES",
     "N_LAYERS",
     "VOCAB",
 ]
@@ -73,6 +74,18 @@ LAYER_SHAPES_FUSED = {
 N_LAYERS = 36
 VOCAB = 151936
 LM_HEAD_SHAPE = (VOCAB, 4096)
+
+# The fused projections and the LM head of two other sizes of the same model
+# family (hidden 2560 with MLP width 9728, hidden 5120 with 17408; 32 and 40
+# query heads of 128, 8 KV heads), for the dispatch's parity and timing
+# beyond the 8B-class shapes.
+FAMILY_SHAPES = {
+    "hidden2560": {"qkv": (6144, 2560), "o": (2560, 4096), "gate_up": (19456, 2560),
+                   "down": (2560, 9728), "lm_head": (VOCAB, 2560)},
+    "hidden4096": {**LAYER_SHAPES_FUSED, "lm_head": LM_HEAD_SHAPE},
+    "hidden5120": {"qkv": (7168, 5120), "o": (5120, 5120), "gate_up": (34816, 5120),
+                   "down": (5120, 17408), "lm_head": (VOCAB, 5120)},
+}
 
 
 def rng(seed: int) -> np.random.Generator:

@@ -211,3 +211,27 @@ def test_verify_window_rejects_before_launch():
     assert call(q_ld=7) == -2                    # q_ld < q_m
     assert call(nws=ws - 1) == -5
     assert call(ws=ctypes.c_void_p(0x100008)) == -6
+
+
+def test_gemv_dispatch_rule():
+    """Which (N, K, R) run the split-K kernel (exactly the calls that report a
+    workspace).  The 8B-class shapes keep the choices their sweeps made; on
+    the hidden-5120 shapes, whose 16-row tiles give 320 row-block
+    workgroups (1.25 rounds of the 256 CUs), the fill model moves down to
+    split-K at every R, o from 7 rows and gate|up from 5."""
+    lib = vs.library()
+
+    def split_k_rows(N, K):
+        return [R for R in range(1, 25) if lib.verify_gemv_rows_workspace_bytes(N, K, R) > 0]
+
+    above16 = list(range(17, 25))
+    assert split_k_rows(6144, 4096) == above16          # q|k|v
+    assert split_k_rows(24576, 4096) == above16         # gate|up
+    assert split_k_rows(4096, 12288) == list(range(9, 25))   # down: long rows
+    assert split_k_rows(4096, 4096) == []               # o: under 48 MB
+    assert split_k_rows(151936, 4096) == []             # LM head
+    assert split_k_rows(5120, 17408) == list(range(1, 25))
+    assert split_k_rows(5120, 5120) == list(range(7, 25))
+    assert split_k_rows(34816, 5120) == list(range(5, 25))
+    assert split_k_rows(2560, 9728) == list(range(9, 25))
+    assert split_k_rows(6144, 2560) == [] and split_k_rows(151936, 2560) == []

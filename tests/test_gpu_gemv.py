@@ -13,7 +13,8 @@ import torch
 import verify_sampling_amd as vs
 from gpu_common import dev, host
 from oracle.gemv import gemv_rows
-from synth import LAYER_SHAPES, LAYER_SHAPES_FUSED, LM_HEAD_SHAPE, gemv_case, torch_bf16_weights
+from synth import (FAMILY_SHAPES, LAYER_SHAPES, LAYER_SHAPES_FUSED, LM_HEAD_SHAPE, gemv_case,
+                   torch_bf16_weights)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -204,3 +205,28 @@ def test_workspace_fallbacks_and_stale_contents():
     for ws in (small, big[4:4 + need], stale, None):
         y = host(vs.verify_gemv_rows(W, X, workspace=ws))
         assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+FAMILY_CASES = [(fam, name) for fam, shapes in FAMILY_SHAPES.items() if fam != "hidden4096"
+                for name in shapes]
+
+
+@pytest.mark.parametrize("fam,name", FAMILY_CASES)
+def test_other_model_sizes_sampled_rows(fam, name):
+    """The fused projections and LM heads of the hidden-2560 and hidden-5120
+    models at every kernel and tile configuration the dispatch picks for
+    them (row-block and split-K, one and two column tiles), on sampled
+    output rows against the oracle, with the last row equal to its 1-row call."""
+    N, K = FAMILY_SHAPES[fam][name]
+    W = torch_bf16_weights((N, K), 1600 + N % 997 + K % 89, "cuda:0")
+    rows = sampled_rows(N, 1200, 1601 + N % 991)
+    w_rows = host(W[torch.from_numpy(rows).to("cuda:0")].contiguous())
+    for R in (1, 4, 8, 9, 16, 17, 24):
+        x = np.random.default_rng(1602 + R + K).standard_normal((R, K)).astype(np.float32)
+        X = dev(x)
+        y = host(vs.verify_gemv_rows(W, X))
+        ref, s = gemv_rows(w_rows, x)
+        err = np.abs(y[:, rows].astype(np.float64) - ref)
+        assert (err <= TOL * s).all(), (fam, name, R)
+        y1 = host(vs.verify_gemv_rows(W, X[R - 1:R]))
+        assert np.array_equal(y1[0].view(np.uint32), y[R - 1].view(np.uint32)), (fam, name, R)

@@ -49,6 +49,7 @@
 //    layout and may instead walk all of K per wave, adding its partition sums
 //    in registers (very wide matrices).
 
+#include <cmath>
 #include <type_traits>
 
 #include "vs_internal.h"
@@ -915,18 +916,28 @@ reduce_partials_kernel(const float* __restrict__ parts, int64_t ldp, int splits,
 }
 
 // K partitions (the k-split): a function of N and K alone, so that the
-// summation order of a row does not change with R.  Wide matrices (many row
-// tiles) do best with few, long partitions; narrower ones split K further
-// for parallelism: 8 partitions, or 16 for long rows (the staged row-block
-// kernel then walks two partitions per wave and keeps its wave count, the
-// split-K kernel gets 16 workgroups per row block, which is what matters
-// above 16 rows).  Chosen by sweeps of the verify pass on MI355X.
+// summation order of a row does not change with R.
+//  * Wide matrices (N >= 16384: enough row tiles to fill the chip) take few,
+//    long partitions: the fewest with at most 32 k-blocks each whose length
+//    is a whole number of the staged kernel's 4-k-block pipeline
+//    iterations (a ragged partition costs a partial iteration in every wave;
+//    on 151936 x 2560, 3 ragged partitions ran at 0.61 of peak, 4 or 5 whole
+//    ones at 0.78-0.80);
+//  * narrower ones split K further for parallelism: 8 partitions, or 16 for
+//    long rows (the staged row-block kernel then walks two partitions per
+//    wave and keeps its wave count, the split-K kernel gets 16 workgroups
+//    per row block).
+// Chosen by sweeps of 15 matrices of three model sizes on MI355X.
 int splits_for(int N, int K) {
   const int nkb = (K + KBLK - 1) / KBLK;
-  int s;
-  if (N >= 16384) s = (nkb + 31) / 32 < 16 ? (nkb + 31) / 32 : 16;
-  else if (nkb >= 256) s = 16;  // long rows (4096 x 12288): more, shorter partitions
-  else s = (nkb + 15) / 16 < 8 ? (nkb + 15) / 16 : 8;
+  if (N >= 16384) {
+    const int lo = (nkb + 31) / 32 < 1 ? 1 : (nkb + 31) / 32;
+    for (int s = lo; s <= MAX_SPLITS; ++s)
+      if (nkb % s == 0 && (nkb / s) % 4 == 0 && (s <= 8 || s % 2 == 0)) return s;
+    return lo < MAX_SPLITS ? lo : MAX_SPLITS;
+  }
+  if (nkb >= 256) return 16;  // long rows (4096 x 12288): more, shorter partitions
+  const int s = (nkb + 15) / 16 < 8 ? (nkb + 15) / 16 : 8;
   return s < 1 ? 1 : s;  // <= MAX_SPLITS
 }
 
@@ -938,29 +949,61 @@ bool staged_fits(int N, int K) {
   return K % KBLK == 0 && nkb / splits >= 2 && (splits <= 8 || splits % 2 == 0);
 }
 
-// Which kernel runs for (N, K, R).  Chosen by per-shape sweeps on MI355X.
-// The row-block kernels re-read the activations once per row tile, so their
-// time grows with R; the split-K kernels share each activation tile among a
-// workgroup's waves and stay nearly flat in R, from a higher base (a
-// dependent partition-sum launch).  The staged row-block kernel wins up to 8
-// rows everywhere, up to 16 below 65536 rows, at every R on matrices under
-// 48 MB and on the LM head (whose partial sums would cost more than the
-// shared activations save); long rows of >= 48 MB (down) take the staged
-// split-K kernel from 9 rows, the other matrices of >= 48 MB below 65536
-// rows (q|k|v, gate|up) above 16.  Where the staged
-// kernels cannot run (K % 32 != 0), matrices of >= 48 MB take the older
-// shared kernels from 9 rows (long rows) or above 16 rows (all-K for very
-// wide ones).
+// The share of the chip's workgroup slots that G workgroups use when each
+// CU runs one at a time: G over the slots of all the rounds they take.
+constexpr double CUS = 256.0;
+double fill(double G) { return G / (CUS * std::ceil(G / CUS)); }
+
+// Whether the staged split-K kernel (and its partition-sum launch) is
+// modelled faster than the staged row-block kernel at R <= 16 rows.  Each
+// kernel's time is the bytes it moves over an effective bandwidth scaled by
+// how well its grid fills the CUs:
+//   row-block: weights + the activations that each row tile re-reads,
+//   split-K:   weights + each workgroup's activation slice + the partial
+//              sums written and read back, plus the dependent launch.
+// Activation re-reads are mostly L2 hits and count 0.3 of an HBM byte.  The
+// constants (7 TB/s, 5 us, 0.3) are fitted to row-block and split-K timings
+// of 13 matrices of three model sizes at R = 1..16 on MI355X; the tile
+// heights are the ones the dispatch below launches.
+bool split_k_pays(int N, int K, int R) {
+  constexpr double BW = 7.0e12, LAUNCH_S = 5e-6, ACT = 0.3;
+  const int nkb = (K + KBLK - 1) / KBLK;
+  const int s = splits_for(N, K);
+  const int t_rb = N < 6144 ? 1 : 2;                       // row tiles per row-block wave
+  const int t_sk = (nkb >= 256 || N >= 16384) ? 2 : 1;     // per split-K wave (4 waves)
+  const double g_rb = std::ceil(N / (16.0 * t_rb));
+  const double g_sk = std::ceil(N / (64.0 * t_sk)) * s;
+  const double w = 2.0 * N * K;
+  const double t_row = (w + ACT * g_rb * R * K * 4.0) / (BW * fill(g_rb));
+  const double t_split = (w + ACT * g_sk * R * (static_cast<double>(K) / s) * 4.0 + 8.0 * R * N * s) /
+                             (BW * fill(g_sk)) + LAUNCH_S;
+  return t_split < t_row;
+}
+
+// Which kernel runs for (N, K, R).  The row-block kernels re-read the
+// activations once per row tile, so their time grows with R; the split-K
+// kernels share each activation tile among a workgroup's waves and stay
+// nearly flat in R, from a higher base (a dependent partition-sum launch),
+// and their grid (row blocks x partitions) fills the chip where the
+// row-block grid leaves a part of a round idle.  Matrices under 48 MB and
+// the LM head (whose partial sums would cost more than the shared
+// activations save) always take the row-block kernel.  Otherwise the
+// split-K kernel runs above 16 rows (where the row-block kernel needs a
+// second activation column tile), from 9 rows for long rows, and wherever
+// split_k_pays models it faster.  Where the staged kernels cannot run
+// (K % 32 != 0), matrices of >= 48 MB take the older shared kernels from 9
+// rows (long rows) or above 16 rows (all-K for very wide ones).
 enum class Kind { kRowBlock, kSharedAllK, kSharedSplitK, kStagedSplitK };
 
 Kind kind_for(int N, int K, int R) {
-  if (R <= 8) return Kind::kRowBlock;
   const bool big = 2.0 * N * K >= 48e6;
   const bool long_rows = (K + KBLK - 1) / KBLK >= 256;
   if (staged_fits(N, K)) {
-    if (big && N < 65536 && (long_rows || R > 16)) return Kind::kStagedSplitK;
+    if (!big || N >= 65536) return Kind::kRowBlock;
+    if (R > 16 || (long_rows && R >= 9) || split_k_pays(N, K, R)) return Kind::kStagedSplitK;
     return Kind::kRowBlock;
   }
+  if (R <= 8) return Kind::kRowBlock;
   if (N < 65536 && big && long_rows) return Kind::kSharedSplitK;
   if (R <= 16 || !big) return Kind::kRowBlock;
   return N >= 65536 ? Kind::kSharedAllK : Kind::kSharedSplitK;
