@@ -81,9 +81,16 @@ const char* vs_last_error_detail(void);
  * result is bit-identical to the result of the same call with R = 1 and
  * X = row r: the summation order depends only on N and K.  It also does
  * not depend on the workspace: with or without one the bits are the same.
+ * Accuracy: every product is exact and the sum is fp32, within
+ * 1e-4 * sum_k |W x| of the exact sum in practice (the tested bound), plus
+ * 2^-133 * sum_k |W[n][k]| for subnormal activations, whose bits below
+ * 2^-133 (the smallest bf16 subnormal) the exact three-plane split cannot
+ * hold.  Non-finite activations follow the sum term by term: an output is
+ * NaN if a term is NaN (a NaN activation, or +-inf times a zero weight) or
+ * +inf and -inf terms meet, else +-inf if a term is infinite.
  *
  *   W    bf16 bit patterns, row-major [N][ldw] (nn.Linear layout, out x in);
- *        16-byte aligned, ldw % 8 == 0, K <= ldw < 2^24.
+ *        finite values; 16-byte aligned, ldw % 8 == 0, K <= ldw < 2^24.
  *   X    fp32 [R][ldx]; 16-byte aligned, ldx % 4 == 0, K <= ldx < 2^24.
  *   Y    fp32 [R][ldy]; ldy >= N.  Must not overlap W, X or the workspace.
  *   1 <= N <= 2^31 - 1024, 1 <= K with K % 8 == 0, 1 <= R <= VS_MAX_ROWS.

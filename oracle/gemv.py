@@ -9,6 +9,13 @@ Weights are bf16 bit patterns (uint16), activations fp32.  The oracle
 widens both exactly to fp64 and multiplies in fp64 (numpy matmul as the
 primitive), which is exact to about 1e-16 relative for these sizes, and
 also returns sum_k |w*x| per output, the scale of the parity tolerance.
+
+Non-finite activations (the pages are silent; the plainest reading of the
+sum): a row holding +-inf or NaN is evaluated term by term in IEEE fp64,
+so an output is NaN if any term is NaN (a NaN activation, or an infinite
+one times a zero weight) or if +inf and -inf terms meet, otherwise +-inf if
+any term is infinite.  Subnormal activations are ordinary finite values.
+Weights are model parameters and are taken to be finite.
 """
 
 from __future__ import annotations
@@ -37,9 +44,15 @@ def gemv_rows(w_bits: np.ndarray, x: np.ndarray, rows: np.ndarray | None = None,
     y = np.empty((R, len(idx)), dtype=np.float64)
     s = np.empty((R, len(idx)), dtype=np.float64)
     ax = np.abs(x64)
+    special = ~np.isfinite(x64).all(axis=1)  # rows evaluated term by term
     for b0 in range(0, len(idx), block):
         sel = idx[b0:b0 + block]
         w = bf16_bits_to_f64(w_bits[sel])
-        y[:, b0:b0 + len(sel)] = x64 @ w.T
-        s[:, b0:b0 + len(sel)] = ax @ np.abs(w).T
+        with np.errstate(invalid="ignore"):
+            y[:, b0:b0 + len(sel)] = x64 @ w.T
+            s[:, b0:b0 + len(sel)] = ax @ np.abs(w).T
+            for r in np.nonzero(special)[0]:
+                terms = w * x64[r][None, :]              # [n][k], IEEE products
+                y[r, b0:b0 + len(sel)] = terms.sum(axis=1)
+                s[r, b0:b0 + len(sel)] = np.abs(terms).sum(axis=1)
     return y, s

@@ -230,3 +230,38 @@ def test_other_model_sizes_sampled_rows(fam, name):
         assert (err <= TOL * s).all(), (fam, name, R)
         y1 = host(vs.verify_gemv_rows(W, X[R - 1:R]))
         assert np.array_equal(y1[0].view(np.uint32), y[R - 1].view(np.uint32)), (fam, name, R)
+
+
+@pytest.mark.parametrize("N,K,R", [(64, 256, 4), (1000, 1000, 5), (4096, 4096, 9), (6144, 4096, 17)])
+def test_non_finite_and_subnormal_activations(N, K, R):
+    """Activations with +-inf, opposite infinities, NaN, and rows scaled into
+    the subnormal range, against the oracle's term-by-term IEEE reading:
+    NaN exactly where it is NaN, the same infinities, and finite outputs
+    within the tolerance plus the library's absolute term 2^-133 * sum|w|
+    (a subnormal activation keeps its bits down to 2^-133, the smallest bf16
+    subnormal; its three-plane split cannot hold the rest) and K * 2^-149
+    (the resolution of fp32 sums in that range).  Row identity holds for
+    every row."""
+    w, x = gemv_case(1700 + N + R, N, K, R)
+    x[0, 3] = np.inf                     # +inf: +-inf outputs, NaN where w = 0
+    x[1, 5], x[1, 9] = -np.inf, np.inf   # opposite infinities: NaN or +-inf by the weights' signs
+    x[2, 7] = np.nan
+    x[3] *= np.float32(2.0 ** -130)      # subnormal activations
+    if R > 4:
+        x[4] *= np.float32(2.0 ** -120)  # small normal activations, subnormal products
+    W, X = dev(w), dev(x)
+    y = host(vs.verify_gemv_rows(W, X))
+    ref, s = gemv_rows(w, x)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    inf = np.isinf(ref)
+    assert np.array_equal(y[inf], ref[inf])
+    fin = ~(nan | inf)
+    _, sw = gemv_rows(w, np.ones((1, K), dtype=np.float32))   # sum_k |w[n][k]|
+    bound = TOL * s + np.broadcast_to(sw, s.shape) * 2.0 ** -133 + K * 2.0 ** -149
+    err = np.abs(y[fin].astype(np.float64) - ref[fin])
+    assert (err <= bound[fin]).all(), float((err / bound[fin]).max())
+    assert np.abs(ref[3]).max() > 0 and np.abs(y[3]).max() > 0   # not flushed to zero
+    for r in range(R):
+        y1 = host(vs.verify_gemv_rows(W, X[r:r + 1]))
+        assert np.array_equal(y1[0].view(np.uint32), y[r].view(np.uint32)), r

@@ -67,3 +67,34 @@ def test_bf16_decode_and_encode():
     # 1 + 3*2^-8 is a tie -> 1 + 2^-6 (even), 1 + 2^-8 + 2^-20 rounds up
     x = np.array([1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-20], dtype=np.float32)
     assert list(f32_to_bf16_bits(x)) == [0x3F80, 0x3F82, 0x3F81]
+
+
+
+def test_non_finite_activations_hand_worked():
+    """IEEE term-by-term reading of y = sum_k w x for rows holding +-inf or
+    NaN, against values worked by hand: an infinite term decides the sign,
+    opposite infinities or an infinity times a zero weight give NaN, a NaN
+    activation gives NaN everywhere; finite rows are unchanged."""
+    inf, nan = np.inf, np.nan
+    w = f32_to_bf16_bits(np.array([[1.0, 2.0, 0.5],
+                                   [0.0, 1.0, 1.0],
+                                   [-1.0, 3.0, 0.0],
+                                   [2.0, -2.0, 1.0]], dtype=np.float32))
+    x = np.array([[inf, 1.0, 2.0],
+                  [inf, -inf, 1.0],
+                  [nan, 1.0, 1.0],
+                  [1.0, 2.0, 3.0]], dtype=np.float32)
+    y, s = gemv_rows(w, x)
+    want = np.array([[inf, nan, -inf, inf],     # inf+2+1, 0*inf, -inf+3, 2inf-2+2
+                     [nan, nan, -inf, inf],     # inf-2inf, 0*inf, -inf-3inf, 2inf+2inf+1
+                     [nan, nan, nan, nan],
+                     [6.5, 5.0, 5.0, 1.0]])
+    np.testing.assert_array_equal(y, want)
+    assert np.isinf(s[0, 0]) and np.isnan(s[0, 1]) and s[3, 3] == 2 + 4 + 3
+
+
+def test_subnormal_activations_are_ordinary_values():
+    w = f32_to_bf16_bits(np.array([[1.0, 2.0, 1.0]], dtype=np.float32))
+    x = np.array([[2.0 ** -130, 2.0 ** -140, 0.0]], dtype=np.float32)
+    y, _ = gemv_rows(w, x)
+    assert y[0, 0] == 2.0 ** -130 + 2.0 ** -139

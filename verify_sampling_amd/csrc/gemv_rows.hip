@@ -66,12 +66,23 @@ constexpr int TILE = 16;   // weight rows per tile
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bitsf(uint32_t b) { return __builtin_bit_cast(float, b); }
 
-// Splits 8 fp32 values into three bf16x8 planes with x == hi + mid + lo exactly.
+// x minus its top plane, the part the lower planes hold: exact for finite
+// x; 0 for x = +-inf (whose difference with itself would be NaN), so that an
+// infinite activation contributes hi * w = +-inf (NaN for w = 0) as its term
+// of the sum does.  A NaN activation stays NaN through its top plane or its
+// residual.
+__device__ __forceinline__ float residual(float x, uint32_t h) {
+  const float r = x - bitsf(h);
+  return __builtin_isinf(x) ? 0.f : r;
+}
+
+// Splits 8 fp32 values into three bf16x8 planes with x == hi + mid + lo
+// exactly (finite x; an infinite one is hi alone, see residual).
 __device__ __forceinline__ void split3(const float (&x)[8], u32x4& hi, u32x4& mid, u32x4& lo) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     uint32_t h0 = fbits(x[2 * p]) & 0xffff0000u, h1 = fbits(x[2 * p + 1]) & 0xffff0000u;
-    float r0 = x[2 * p] - bitsf(h0), r1 = x[2 * p + 1] - bitsf(h1);
+    float r0 = residual(x[2 * p], h0), r1 = residual(x[2 * p + 1], h1);
     uint32_t m0 = fbits(r0) & 0xffff0000u, m1 = fbits(r1) & 0xffff0000u;
     float s0 = r0 - bitsf(m0), s1 = r1 - bitsf(m1);
     hi[p] = (h0 >> 16) | h1;
@@ -95,7 +106,7 @@ __device__ __forceinline__ void split3x4(float4 x, uint2& hi, uint2& mid, uint2&
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     uint32_t h0 = fbits(v[2 * p]) & 0xffff0000u, h1 = fbits(v[2 * p + 1]) & 0xffff0000u;
-    float r0 = v[2 * p] - bitsf(h0), r1 = v[2 * p + 1] - bitsf(h1);
+    float r0 = residual(v[2 * p], h0), r1 = residual(v[2 * p + 1], h1);
     uint32_t m0 = fbits(r0) & 0xffff0000u, m1 = fbits(r1) & 0xffff0000u;
     float s0 = r0 - bitsf(m0), s1 = r1 - bitsf(m1);
     h[p] = (h0 >> 16) | h1;
