@@ -41,7 +41,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 CALIB_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_rows_traffic_r4.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_rows_traffic_r{R}.md")
 KERNEL_SOURCE = os.path.join(ROOT, "verify_sampling_amd", "csrc", "gemv_rows.hip")
 
 
@@ -55,7 +55,7 @@ def measured_traffic(R):
     import re
 
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILE.format(R=R)).read()
         src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
@@ -718,6 +718,8 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "frac_of_measured_copy": achieved / copy["gbs_read_plus_write"],
             "traffic": measured_traffic(R),
+            "traffic_unit": "HBM bytes per projection call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_vs_R": {str(r): measured_traffic(r) for r in (4, 9, 16, 17, 24)},
             "launches_per_pass": vp.n_launches(),
             "avg_launch_us": per_launch_ms * 1e3,
         },
