@@ -561,6 +561,45 @@ def cpu_baseline(synth, R, budget_s=8.0):
             "accept_rows_per_s": R / acc_s}
 
 
+def tree_attention_leg(torch, vs, synth, dev, reps=20, warmup=3):
+    """Attention of a 3-branch x 8-deep token tree (25 rows) under the tree
+    mask: 32 query heads over 8 KV heads of 128, a 2080-position context
+    (prompt 2048 + 32 emitted) in a 4096-position cache, keys and values
+    N(0, 1) bf16, queries N(0, 1) fp32.  Median of `reps` HIP-event-timed
+    C-ABI calls with cached arguments.  Algorithmic bytes: the context's keys
+    and values once, the scratch slots, queries and outputs once."""
+    R, Hq, Hkv, D, ctx, L = 25, 32, 8, 128, 2080, 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(7100)
+    q = torch.randn((R, Hq, D), generator=g, device=dev, dtype=torch.float32)
+    kc = torch.randn((Hkv, L, D), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((Hkv, L, D), generator=g, device=dev).to(torch.bfloat16)
+    ks = torch.randn((Hkv, R, D), generator=g, device=dev).to(torch.bfloat16)
+    vs_ = torch.randn((Hkv, R, D), generator=g, device=dev).to(torch.bfloat16)
+    parent = torch.tensor([-1 if j % 8 == 0 else j - 1 for j in range(R - 1)], dtype=torch.int32, device=dev)
+    out = torch.empty((R, Hq, D), dtype=torch.float32, device=dev)
+    nws = vs.tree_attention_rows_workspace_bytes(R, Hq, Hkv, ctx)
+    ws = torch.empty(max(16, nws), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(D))
+    vs.tree_attention_rows(q, kc, vc, ctx, ks, vs_, parent, scale=scale, out=out, workspace=ws)  # checks the arguments
+    lib = vs.library()
+    args = (q.data_ptr(), R, Hq, D, kc.data_ptr(), vc.data_ptr(), L, ctx, ks.data_ptr(), vs_.data_ptr(), R,
+            parent.data_ptr(), Hkv, scale, out.data_ptr(), ws.data_ptr(), int(ws.numel()))
+
+    def call():
+        st = lib.tree_attention_rows(*args, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"tree_attention_rows failed with status {st}")
+
+    us = float(np.median(time_each(torch, call, reps, warmup))) * 1e3
+    nbytes = 2 * Hkv * ctx * D * 2 + 2 * Hkv * R * D * 2 + 2 * R * Hq * D * 4
+    return {"config": f"3 x 8 tree ({R} rows), {Hq}/{Hkv} heads of {D}, context {ctx}",
+            "us": round(us, 2), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "hbm_floor_us": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
+
+
 def family_sweep(torch, vs, synth, dev, reps=12, warmup=3):
     """verify_gemv_rows alone on every fused projection and LM head of three
     model sizes, each R = 1..24: median of `reps` HIP-event-timed calls after
@@ -679,6 +718,8 @@ def main():
     if sampling:
         log(f"sampling: {sampling['rows_per_s']:.3e} rows/s")
     draft = None if args.no_sampling else draft_side(torch, vs, synth, dev)
+    tree_attn = tree_attention_leg(torch, vs, synth, dev)
+    log(f"tree attention: {tree_attn['us']} us ({tree_attn['frac_of_hbm_peak']} of peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -754,6 +795,7 @@ def main():
         "prompt_lookup_drafter": lookup_report(vs, synth),
         "sampling": sampling,
         "draft_side": draft,
+        "tree_attention": tree_attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
