@@ -43,7 +43,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int HD = 128;       // head dimension
 constexpr int BKEYS = 64;     // keys per sub-block
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
 constexpr int KSTEPS = HD / 32;     // MFMA k-steps over the head dimension
 constexpr int NT_S = BKEYS / 16;    // key tiles of a sub-block
 constexpr int NT_O = HD / 16;       // dimension tiles of the output
@@ -192,13 +192,6 @@ tree_attention_split_kernel(Args a) {
     }
     split3(x, hi, mid, lo);
   };
-  u32x4 qp[QREG ? MTW : 1][KSTEPS][3];
-  if constexpr (QREG) {
-#pragma unroll
-    for (int i = 0; i < MTW; ++i)
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) q_planes(i, ks, qp[i][ks][0], qp[i][ks][1], qp[i][ks][2]);
-  }
 
   f32x4 o[MTW][NT_O];  // O^T tiles: lane (g, c), element e = dimension 16 t + 4 g + e of query c
   float rm[MTW], rl[MTW];
@@ -250,7 +243,16 @@ tree_attention_split_kernel(Args a) {
     }
   };
 
+  // the first sub-block's keys and values are in flight while the queries
+  // are loaded and split
   if (nsub > 0) load_kv(first);
+  u32x4 qp[QREG ? MTW : 1][KSTEPS][3];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) q_planes(i, ks, qp[i][ks][0], qp[i][ks][1], qp[i][ks][2]);
+  }
   for (int sb = 0; sb < nsub; ++sb) {  // uniform over the workgroup
     const int p0 = first + sb * BKEYS;
     __syncthreads();  // the previous sub-block's kt, vt and planes have been read
@@ -376,11 +378,13 @@ tree_attention_split_kernel(Args a) {
 }
 
 // out[r][hq][d] from the splits' partial results, merged in split order.
-// One workgroup per query vector, one thread per dimension.  The splits'
-// statistics are loaded one split per thread and their weights e^(m_s - M)
-// kept in LDS; each thread then adds its dimension over the splits in split
-// order, loading the partial outputs 16 splits at a time.
+// One workgroup per query vector, one thread per dimension.  The first
+// PRE splits' partial outputs are loaded together with the statistics (one
+// memory round for both); the splits' weights e^(m_s - M) are kept in LDS;
+// each thread then adds its dimension over the splits in split order,
+// loading any further partial outputs 16 splits at a time.
 constexpr int MAX_SPLITS = 260;  // plan_for keeps the context splits of a KV head <= 256
+constexpr int PRE = 32;
 
 __global__ void __launch_bounds__(HD)
 tree_attention_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -393,6 +397,9 @@ tree_attention_combine_kernel(const float* __restrict__ part_o, const float* __r
   const int g = gm / M, m = gm % M;
   const int d = threadIdx.x;
   auto stat = [&](int s) { return (static_cast<int64_t>(s) * Hkv + g) * M + m; };
+  float pre[PRE];
+#pragma unroll
+  for (int j = 0; j < PRE; ++j) pre[j] = j < splits ? part_o[stat(j) * HD + d] : 0.f;
   float mx = -__builtin_inff();
   for (int s = d; s < splits; s += HD) mx = fmaxf(mx, part_ml[stat(s) * 2]);
 #pragma unroll
@@ -410,7 +417,13 @@ tree_attention_combine_kernel(const float* __restrict__ part_o, const float* __r
   }
   __syncthreads();
   float l = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += 16) {
+#pragma unroll
+  for (int j = 0; j < PRE; ++j)
+    if (j < splits && f[j] != 0.f) {
+      l += lf[j];
+      acc += pre[j] * f[j];
+    }
+  for (int s0 = PRE; s0 < splits; s0 += 16) {
     float v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = s0 + j < splits ? part_o[stat(s0 + j) * HD + d] : 0.f;
@@ -441,7 +454,8 @@ tree_commit_kernel(uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t
 }
 
 // context sub-blocks per split: enough splits to give the device about two
-// workgroups per CU, at least one sub-block each
+// workgroups per CU, at least one sub-block each (more splits than the
+// resident slots, two 64 KB workgroups per CU, add a second round)
 int blocks_per_split(int ctx_len, int Hkv) {
   const int nblk = (ctx_len + BKEYS - 1) / BKEYS;
   const int target = (256 + Hkv - 1) / Hkv;  // splits per KV head (<= 256)
