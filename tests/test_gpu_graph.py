@@ -100,3 +100,64 @@ def test_window_replays_equal_eager(window_state):
         assert 1 <= int(eager["n"][0]) <= K_DRAFT + 1
         seen.append(got["Y1"].tobytes() + got["pi"].tobytes())
     assert len(set(seen)) == len(seen)  # each replay computed on its own inputs
+
+
+def fused_window(W2, b, t):
+    """The LM-head projection, verify_window and tree attention with the
+    commit of a branch, on the current stream."""
+    L = vs.verify_gemv_rows(W2, b["x2"])
+    raw = L.clone()
+    out = vs.verify_window(L, b["ctx"], b["drafts"], q_ids=b["q_ids"], q_vals=b["q_vals"],
+                           u=b["u"][0], **PEN, **CFG)
+    att = vs.tree_attention_rows(t["q"], t["kc"], t["vc"], 200, t["ks"], t["vs"], t["parent"],
+                                 scale=0.0883883)
+    kc, vc = t["kc"].clone(), t["vc"].clone()
+    vs.tree_commit_kv(kc, vc, 200, t["ks"], t["vs"], t["path"])
+    res = dict(raw=raw, L=L, att=att, kc=kc, vc=vc, tokens=out["tokens"], n=out["n"],
+               pool_vals=out["pool_vals"], pool_ids=out["pool_ids"], q_pen=out["q_pen"])
+    for name, tup in (("p", out["p"]), ("q", out["q"])):
+        for j, tt in enumerate(tup):
+            res[f"{name}{j}"] = tt
+    return res
+
+
+def tree_inputs(seed):
+    g = np.random.default_rng(seed)
+    R, Hq, Hkv, D, L = 9, 8, 2, 128, 256
+    f = lambda shape: torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(DEV)
+    return dict(q=f((R, Hq, D)), kc=f((Hkv, L, D)).to(torch.bfloat16), vc=f((Hkv, L, D)).to(torch.bfloat16),
+                ks=f((Hkv, R, D)).to(torch.bfloat16), vs=f((Hkv, R, D)).to(torch.bfloat16))
+
+
+def test_fused_window_and_tree_attention_replay_equal_eager(window_state):
+    """verify_window (its multi-chunk select and one-workgroup finish) and
+    tree attention (split and merge kernels) with the commit, captured once
+    and replayed on fresh inputs: every replay equals the eager run bit for
+    bit."""
+    _, W2, bufs = window_state
+    t = tree_inputs(2800)
+    t["parent"] = torch.tensor([-1, 0, 1, -1, 3, 4, 0, 6], dtype=torch.int32, device=DEV)
+    t["path"] = torch.tensor([0, 4, 5, 6], dtype=torch.int32, device=DEV)
+    assert vs.verify_window_workspace_bytes(K_DRAFT + 1, VOCAB) > 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fused_window(W2, bufs, t)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = fused_window(W2, bufs, t)
+
+    for rep, seed in enumerate([2810, 2820, 2830]):
+        for k, v in new_inputs(seed).items():
+            bufs[k].copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        for k, v in tree_inputs(seed + 1).items():
+            t[k].copy_(v)
+        eager = {k: host(v) for k, v in fused_window(W2, bufs, t).items()}
+        graph.replay()
+        got = {k: host(v) for k, v in captured.items()}
+        for k in eager:
+            assert np.array_equal(eager[k].view(np.uint8), got[k].view(np.uint8)), (rep, k)
+        assert 1 <= int(eager["n"][0]) <= K_DRAFT + 1
