@@ -18,9 +18,14 @@
 //    chunk's top 64 are selected as topk_rows does.  Extra waves, one per
 //    draft row, penalise its candidates against the same history and compute
 //    the draft's policy distribution.
-//  * finish: one workgroup merges each row's chunk lists into its pool, runs
-//    the target's policy on it, and then one wave accepts the drafts.  Pools
-//    and distributions pass through LDS and are also written out.
+//  * finish: one workgroup of eight waves; wave w merges rows w, w + 8, ...
+//    into their pools and runs the target's policy on each, while the
+//    draft distributions, uniforms and drafts it loaded at the start wait in
+//    registers; after one barrier one wave accepts the drafts.  Pools and
+//    distributions pass through LDS and are also written out.
+// Both stages are latency-bound (one window is a few MB): the select stage's
+// cost is its waves' load latency and selection, the finish stage's a
+// single wave's dependent merge, policy and acceptance per row.
 
 #include "accept_dev.h"
 #include "penalty_dev.h"
