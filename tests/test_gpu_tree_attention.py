@@ -121,3 +121,26 @@ def test_commit_keeps_the_accepted_branch():
     k2 = host(K2)
     assert np.array_equal(k2[:, ctx], ks[:, 0]) and np.array_equal(k2[:, ctx + 1], kc[:, ctx + 1])
     assert np.array_equal(k2[:, ctx + 2], ks[:, 3])
+
+
+@pytest.mark.parametrize("seed", range(2300, 2312))
+def test_random_trees_heads_and_contexts(seed):
+    """Seeded random shapes: rows 1..64, query heads per KV head 1..8 (at most
+    256 queries per KV head), 1..8 KV heads, contexts 0..3000 (ragged last
+    blocks), random parents (some malformed), scales, and scratch longer than
+    the tree; every output within the tolerance of the oracle."""
+    g = np.random.default_rng(seed)
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    G = int(g.choice([1, 2, 4, 8]))
+    R = int(g.integers(1, min(64, 256 // G) + 1))
+    ctx = int(g.choice([0, 1, 31, 64, 129, 777, 2080, 3000]))
+    parent = np.array([int(g.integers(-1, j)) if j > 0 else -1 for j in range(R - 1)], dtype=np.int32)
+    if R > 3 and g.integers(0, 3) == 0:
+        parent[int(g.integers(1, R - 1))] = int(g.choice([-7, R + 3]))   # a malformed parent
+    scale = float(g.uniform(0.02, 0.2))
+    print(f"seed {seed}: R={R} G={G} Hkv={Hkv} ctx={ctx}", flush=True)
+    q, kc, vc, ks, vs_ = case(seed + 100, R, G * Hkv, Hkv, ctx, L=ctx + 1 + int(g.integers(0, 40)))
+    ks_long = np.concatenate([ks, ks[:, :2]], axis=1)   # scratch of R + 2 slots
+    vs_long = np.concatenate([vs_, vs_[:, :2]], axis=1)
+    got = run(q, kc, vc, ctx, ks_long, vs_long, parent, scale)
+    check(got, q, kc, vc, ctx, ks_long, vs_long, parent, scale)

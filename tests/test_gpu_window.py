@@ -202,3 +202,32 @@ def test_q_policy_matches_oracle_policy_rows():
         oi, op = policy_row(want["q_penalized"][i], q_ids[i, :q_m], **CFG)
         assert ln[i] == len(oi) and np.array_equal(ids[i, :ln[i]], oi)
         assert (ulp_diff_f32(probs[i, :ln[i]], op) <= 1).all()
+
+
+def random_config(seed):
+    g = np.random.default_rng(seed)
+    V = int(g.choice([64, 100, 1024, 1500, 4096, 32000, 50257, 151936]))
+    R = int(g.integers(1, 65))
+    q_m = int(g.integers(1, 17))
+    mk = dict(q_m=q_m, q_ld=q_m + int(g.integers(0, 4)), ld=V + int(g.choice([0, 0, 1, 3, 8])),
+              ctx_len=int(g.choice([0, 1, 5, 64, 300, 5000])), bad_ids=bool(g.integers(0, 2)),
+              planted=bool(V >= 1024 and g.integers(0, 4) == 0))
+    pen = dict(window=int(g.choice([0, 1, 7, 64, 200, 4096])), repeat=float(g.choice([0.5, 1.0, 1.3])),
+               presence=float(g.uniform(-1, 2)), frequency=float(g.uniform(-0.5, 0.5)))
+    cfg = dict(temperature=float(g.choice([0.0, 0.3, 0.7, 1.0, 2.5])), top_k=int(g.choice([-1, 0, 1, 5, 20, 64])),
+               top_p=float(g.choice([0.1, 0.9, 1.0])), min_p=float(g.choice([0.0, 0.05, 0.5])))
+    return V, R, mk, pen, cfg
+
+
+@pytest.mark.parametrize("seed", range(3500, 3524))
+def test_fused_window_random_configurations(seed):
+    """Seeded random windows (vocabulary, rows up to 64, row and candidate
+    strides, context and window lengths, penalty signs, every policy
+    setting, greedy and sampled): the fused call equals the separate calls
+    byte for byte."""
+    V, R, mk, pen, cfg = random_config(seed)
+    print(f"seed {seed}: V={V} R={R} {mk} {pen} {cfg}", flush=True)
+    lg, ctx, drafts, q_ids, q_vals, u = make_case(seed, V, R, **mk)
+    a = fused(lg, ctx, drafts, q_ids, q_vals, u, V, mk["q_m"], pen, cfg)
+    b = separate(lg, ctx, drafts, q_ids, q_vals, u, V, mk["q_m"], pen, cfg)
+    assert_same(a, b, mk["q_m"])
