@@ -341,8 +341,10 @@ int spec_accept_rows(int mode, int B, int k,
  *   sampled: 1 <= q_m <= VS_POOL, q_m <= q_ld <= 2^24; penalty and policy
  *   parameters as for penalize_rows and sample_policy_rows.
  *   workspace: device memory of at least verify_window_workspace_bytes(R, V)
- *   bytes (the chunk lists of topk_rows at K = 64), 16-byte aligned; no
- *   initialisation needed, scratch after the call.
+ *   bytes (the chunk lists of topk_rows at K = 64, and for R > 8 a 16-byte
+ *   arrival counter of the finishing workgroups), 16-byte aligned; no
+ *   initialisation needed (the call sets what it reads), scratch after the
+ *   call.
  *   A VS_ERR_HIP from the second launch leaves the first one's writes in
  *   place: the penalised logits, q_pen, the q distributions and, for
  *   V <= 1024, the pools.

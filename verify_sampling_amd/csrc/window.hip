@@ -18,11 +18,12 @@
 //    chunk's top 64 are selected as topk_rows does.  Extra waves, one per
 //    draft row, penalise its candidates against the same history and compute
 //    the draft's policy distribution.
-//  * finish: one workgroup of eight waves; wave w merges rows w, w + 8, ...
-//    into their pools and runs the target's policy on each, while the
-//    draft distributions, uniforms and drafts it loaded at the start wait in
-//    registers; after one barrier one wave accepts the drafts.  Pools and
-//    distributions pass through LDS and are also written out.
+//  * finish: one wave per row, in workgroups of eight; each wave merges its
+//    row's chunk lists into the pool and runs the target's policy on it,
+//    while the draft distributions, uniforms and drafts loaded at the start
+//    wait in registers; then one wave accepts the drafts (in the last
+//    workgroup to finish, when there are several).  Pools and distributions
+//    pass through LDS and are also written out.
 // Both stages are latency-bound (one window is a few MB): the select stage's
 // cost is its waves' load latency and selection, the finish stage's a
 // single wave's dependent merge, policy and acceptance per row.
@@ -92,6 +93,7 @@ struct WinArgs {
   int32_t* out_tokens;   // [R]
   int32_t* out_n;
   uint64_t* ws;
+  uint32_t* counter;     // finish workgroups that have published their rows (several workgroups)
   int chunks, lg_jp, lg_j2;
 };
 
@@ -192,6 +194,7 @@ window_select_kernel(WinArgs a) {
     DraftShared draft;
   } shared[WAVES];
   const int w = vs::wave_index();
+  if (a.counter != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.counter = 0u;  // read by the next launch
   const int unit = blockIdx.x * WAVES + w;
   const int cunits = a.R * a.chunks;
   if (unit < cunits) {
@@ -245,7 +248,10 @@ window_finish_kernel(WinArgs a) {
   const float u_r = a.sampled && tid < 2 * a.R ? a.u[tid] : 0.f;
   const int32_t d_r = tid < k ? a.h.drafts[tid] : 0;
 
-  for (int row = w; row < a.R; row += FIN_WAVES) {  // uniform per wave
+  __shared__ int last;
+  // one row per wave: the grid holds ceil(R / FIN_WAVES) workgroups
+  const int row = blockIdx.x * FIN_WAVES + w;
+  if (row < a.R) {  // uniform per wave
     if (a.chunks > 1) {
       merge_row(msh[w], a.logits, a.ld, row, a.h.V, WIN_K, a.chunks, a.lg_jp, a.lg_j2, a.ws, pv[w], pi[w]);
       vs::wave_lds_sync();
@@ -274,6 +280,29 @@ window_finish_kernel(WinArgs a) {
   }
   if (tid < 2 * a.R) us[tid] = u_r;
   if (tid < k) dr[tid] = d_r;
+  if (gridDim.x > 1) {  // uniform
+    // More than one workgroup: each publishes its rows to the device and is
+    // counted; the last to arrive reads the others' rows and accepts.  Each
+    // wave's stores have reached the L2 before the barrier; one agent-scope
+    // release then writes the L2 back, and the last workgroup's acquire
+    // drops stale lines before it reads.  Nothing waits on another
+    // workgroup.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t arrived = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = arrived == gridDim.x - 1u;
+    }
+    __syncthreads();
+    if (!last) return;  // uniform over the workgroup
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int r = w; r < a.R; r += FIN_WAVES) {  // the other workgroups' rows
+      if (r / FIN_WAVES == static_cast<int>(blockIdx.x)) continue;  // uniform per wave
+      dids[r][lane] = a.p_ids[r * WIN_K + lane];
+      dprobs[r][lane] = a.p_probs[r * WIN_K + lane];
+      if (lane == 0) dlen[r] = a.p_len[r];
+    }
+  }
   __syncthreads();
   if (w == 0) {
     const Dists d{&dids[0][0], &dprobs[0][0], dlen, WIN_K, k + 1, &qids[0][0], &qprobs[0][0], qlen, WIN_K, k};
@@ -282,12 +311,19 @@ window_finish_kernel(WinArgs a) {
   }
 }
 
+// The workspace: the chunk lists of rows of several chunks (topk_rows' at
+// K = 64), then, for more rows than one finish workgroup takes, a 16-byte
+// slot for the arrival counter.
+size_t lists_bytes(int R, int V) {
+  const Plan p = plan_for(R, V);
+  return p.chunks <= 1 ? 0 : static_cast<size_t>(R) * p.chunks * WIN_K * sizeof(uint64_t);
+}
+
 }  // namespace
 
 extern "C" size_t verify_window_workspace_bytes(int R, int V) {
   if (R < 1 || V < WIN_K) return 0;
-  const Plan p = plan_for(R, V);
-  return p.chunks <= 1 ? 0 : static_cast<size_t>(R) * p.chunks * WIN_K * sizeof(uint64_t);
+  return lists_bytes(R, V) + (R > FIN_WAVES ? 16 : 0);
 }
 
 extern "C" int verify_window(float* logits, int64_t ld, int R, int V, const int32_t* ctx, int ctx_len,
@@ -354,6 +390,9 @@ extern "C" int verify_window(float* logits, int64_t ld, int R, int V, const int3
   a.out_tokens = out_tokens;
   a.out_n = out_n;
   a.ws = static_cast<uint64_t*>(workspace);
+  a.counter = R > FIN_WAVES
+                  ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + lists_bytes(R, V))
+                  : nullptr;
   a.chunks = p.chunks;
   merge_reads(p.chunks, WIN_K, a.lg_jp, a.lg_j2);
 
@@ -365,6 +404,7 @@ extern "C" int verify_window(float* logits, int64_t ld, int R, int V, const int3
     window_select_kernel<64><<<grid, block, 0, stream>>>(a);
   int st = vs::check_launch();
   if (st != VS_OK) return st;
-  window_finish_kernel<<<dim3(1), dim3(64 * FIN_WAVES), 0, stream>>>(a);
+  window_finish_kernel<<<dim3(static_cast<unsigned>((R + FIN_WAVES - 1) / FIN_WAVES)), dim3(64 * FIN_WAVES), 0,
+                         stream>>>(a);
   return vs::check_launch();
 }
