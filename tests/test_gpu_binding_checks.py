@@ -125,3 +125,60 @@ def test_accept_rejects(T):
     raises(lambda: vs.spec_accept_rows(S, d, p, q, u=u, out=(i(B, k), i(B))))  # tokens short
     raises(lambda: vs.spec_accept_rows(S, d, p, q, u=u, out=(i(B, k + 1), i(1))))
     raises(lambda: vs.spec_accept_rows(S, d, p, q, u=u, p_win_stride=-1))
+
+
+def test_window_rejects(T):
+    torch, vs, z, i = T
+    R, V = 4, 1000
+    L = z(R, V)
+    ctx, dr = i(16), i(R - 1)
+    qi, qv, u = i(R - 1, 8), z(R - 1, 8), z(R, 2)
+    kw = dict(window=8, repeat=1.1, presence=0.5, frequency=0.1, temperature=0.7, top_k=20,
+              top_p=0.9, min_p=0.05)
+    ok = dict(q_ids=qi, q_vals=qv, u=u)
+    raises(lambda: vs.verify_window(z(V), ctx, dr, **ok, **kw))                 # 1-D logits
+    raises(lambda: vs.verify_window(L.double(), ctx, dr, **ok, **kw))           # dtype
+    raises(lambda: vs.verify_window(L[:, ::2], ctx, dr, **ok, **kw))            # strided columns
+    raises(lambda: vs.verify_window(L, ctx, i(R), **ok, **kw))                  # R - 1 drafts
+    raises(lambda: vs.verify_window(L, i(4, 4), dr, **ok, **kw))                # 2-D history
+    raises(lambda: vs.verify_window(L, ctx, z(R - 1), **ok, **kw))              # float drafts
+    raises(lambda: vs.verify_window(L, ctx, dr, q_ids=qi, q_vals=qv, **kw))     # u missing
+    raises(lambda: vs.verify_window(L, ctx, dr, q_ids=qi, q_vals=qv, u=z(2 * R - 1), **kw))
+    raises(lambda: vs.verify_window(L, ctx, dr, q_ids=i(R - 1, 6), q_vals=qv, u=u, **kw))
+    raises(lambda: vs.verify_window(L, ctx, dr, q_ids=i(R - 1, 65), q_vals=z(R - 1, 65), u=u, **kw))
+    raises(lambda: vs.verify_window(L, ctx, dr, q_ids=qi, q_vals=z(R - 2, 8), u=u, **kw))
+    raises(lambda: vs.verify_window(L, ctx, dr, **ok, workspace=z(64), **kw))  # float workspace
+    good = dict(tokens=i(R), n=i(1), pool_vals=z(R, 64), pool_ids=i(R, 64),
+                p=(i(R, 64), z(R, 64), i(R)), q=(i(R - 1, 8), z(R - 1, 8), i(R - 1)), q_pen=z(R - 1, 8))
+    for key, bad in (("tokens", i(R - 1)), ("pool_vals", z(R, 32)), ("pool_ids", z(R, 64)),
+                     ("p", (i(R, 64), z(R - 1, 64), i(R))), ("q", None),
+                     ("q", (i(R - 1, 8), z(R - 1, 8), i(R - 2))), ("q_pen", z(R - 1, 4))):
+        raises(lambda: vs.verify_window(L, ctx, dr, **ok, out=dict(good, **{key: bad}), **kw))
+
+
+def test_tree_attention_rejects(T):
+    torch, vs, z, i = T
+    R, Hq, Hkv, D, n = 5, 4, 2, 128, 40
+    q = z(R, Hq, D)
+    kc = z(Hkv, n, D, dtype=torch.bfloat16)
+    ks = z(Hkv, R, D, dtype=torch.bfloat16)
+    par = i(R - 1)
+    raises(lambda: vs.tree_attention_rows(z(R, Hq * D), kc, kc, n, ks, ks, par, scale=0.1))
+    raises(lambda: vs.tree_attention_rows(q.double(), kc, kc, n, ks, ks, par, scale=0.1))
+    raises(lambda: vs.tree_attention_rows(q, kc, kc, n, ks, z(Hkv, R + 1, D, dtype=torch.bfloat16),
+                                          par, scale=0.1))                      # v_scr shape
+    raises(lambda: vs.tree_attention_rows(q, z(Hkv, n, 64, dtype=torch.bfloat16), kc, n, ks, ks,
+                                          par, scale=0.1))                      # cache head dim
+    raises(lambda: vs.tree_attention_rows(q, kc.float(), kc, n, ks, ks, par, scale=0.1))
+    raises(lambda: vs.tree_attention_rows(q, kc, kc, n, ks, ks, i(R - 2), scale=0.1))  # parent
+    raises(lambda: vs.tree_attention_rows(q, kc, kc, n, ks, ks, None, scale=0.1))
+    raises(lambda: vs.tree_attention_rows(q, kc, kc, n, ks, ks, par, scale=0.1,
+                                          out=z(R, Hq, D - 1)))                 # out too small
+    raises(lambda: vs.tree_attention_rows(q, kc, kc, n, ks, ks, par, scale=0.1,
+                                          out=z(R, Hq, 2 * D)[:, :, :D]))       # strided out
+    raises(lambda: vs.tree_attention_rows(q, kc, kc, n, ks, ks, par, scale=0.1, workspace=z(64)))
+    raises(lambda: vs.tree_commit_kv(kc, kc, n - 3, z(Hkv, R, 64, dtype=torch.bfloat16),
+                                     z(Hkv, R, 64, dtype=torch.bfloat16), i(2)))  # head dim
+    raises(lambda: vs.tree_commit_kv(kc, kc, n - 3, ks, ks, z(2)))              # float path
+    raises(lambda: vs.tree_commit_kv(kc, z(Hkv, n + 1, D, dtype=torch.bfloat16), n - 3, ks, ks,
+                                     i(2)))                                     # cache shapes
