@@ -27,8 +27,9 @@
 //  * softmax: online over the sub-blocks in fp32 (running maximum m, sum l,
 //    rescale by exp(m_old - m_new)); each row's maximum and sum over a
 //    sub-block reduce across the 16 lanes of a row group in a fixed order;
-//  * values: the probabilities, split exactly into three bf16 planes in LDS
-//    (the A operand), times V transposed into LDS (the B operand);
+//  * values: the probabilities, split exactly into three bf16 planes in
+//    registers (the A operand), times V staged transposed in LDS (the B
+//    operand, its keys in the order the probabilities sit in the lanes);
 //  * each split writes its (m, l, unnormalised output) to a workspace; a
 //    second kernel merges the splits in split order: out = sum_s o_s
 //    e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s.
@@ -47,7 +48,6 @@ constexpr int WAVES = 8;
 constexpr int KSTEPS = HD / 32;     // MFMA k-steps over the head dimension
 constexpr int NT_S = BKEYS / 16;    // key tiles of a sub-block
 constexpr int NT_O = HD / 16;       // dimension tiles of the output
-constexpr int PSTR = BKEYS + 8;     // LDS row stride (bf16) of the probability planes
 constexpr int VSTR = BKEYS + 8;     // LDS row stride (bf16) of V transposed
 constexpr int MAX_ROWS = 64;        // tree rows (root + up to 63 nodes)
 constexpr int MAX_QUERIES = 256;    // G * R per KV head
@@ -93,6 +93,17 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Slot of key `key` of a sub-block in the LDS copy of V^T.  Within each
+// 32-key chunk the keys sit in the order in which a lane holds them after the
+// score product (lane group gg has keys 4 gg + e of the chunk's first 16-key
+// tile and 16 + 4 gg + e of its second), so that the probabilities serve as
+// the A operand of the value product straight from registers: key
+// 16 h + 4 gg + e of the chunk goes to slot 8 gg + 4 h + e.
+__device__ __forceinline__ int vslot(int key) {
+  const int c = key & 31;
+  return (key & ~31) + 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3);
+}
+
 // The scratch slots row `row` attends to, as a bit mask (bit s = slot s).
 __device__ __forceinline__ uint64_t ancestor_mask(const int32_t* parent, int row) {
   uint64_t m = 1ull;  // the root's slot
@@ -132,19 +143,19 @@ struct Args {
 // the queries' bf16 planes stay in registers for the whole split (else they
 // are reloaded and split for every sub-block).
 //
-// Both products are taken transposed, so that a lane owns one query of a
-// tile throughout: S^T = K Q^T (A = keys, B = query planes; lane (g, c)
-// holds query c and keys 16 t + 4 g + e) and O^T = V^T P^T (A = V^T from
-// LDS, B = the probability planes; lane (g, c) holds query c and dimensions
-// 16 t + 4 g + e).  A row's maximum and sum are then 16 register values and
-// two shuffles across the lane groups, and its probabilities are written to
-// LDS four keys at a time.
+// Scores are taken transposed, S^T = K Q^T (A = keys, B = query planes), so
+// that lane (g, c) holds query c and keys 16 t + 4 g + e: a query's maximum
+// and sum are 16 register values and two shuffles across the lane groups.
+// Outputs are O = P V (A = the probability planes, straight from the
+// registers that computed them; B = V from LDS, its keys permuted to match,
+// see vslot); lane (g, c) then holds queries 4 g + e and dimension c of each
+// 16-dimension tile, and takes the rescale factors of its four queries from
+// the lanes that own them.
 template <int MTW, bool QREG>
 __global__ void __launch_bounds__(64 * WAVES)
 tree_attention_split_kernel(Args a) {
   constexpr int KSTR = HD + 8;  // LDS row stride (bf16) of the key block
-  __shared__ __align__(16) uint16_t pl[WAVES][MTW][3][16 * PSTR];  // probability planes [query][key]
-  __shared__ __align__(16) uint16_t vt[HD * VSTR];                 // values of the sub-block, [dim][key]
+  __shared__ __align__(16) uint16_t vt[HD * VSTR];                 // values of the sub-block, [dim][slot]
   __shared__ __align__(16) uint16_t kt[BKEYS * KSTR];              // keys of the sub-block, [key][dim]
   __shared__ int32_t par[MAX_ROWS];
   __shared__ uint64_t anc_row[MAX_ROWS];
@@ -193,7 +204,7 @@ tree_attention_split_kernel(Args a) {
     split3(x, hi, mid, lo);
   };
 
-  f32x4 o[MTW][NT_O];  // O^T tiles: lane (g, c), element e = dimension 16 t + 4 g + e of query c
+  f32x4 o[MTW][NT_O];  // O tiles: lane (g, c), element e = query 4 g + e, dimension 16 t + c
   float rm[MTW], rl[MTW];
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
@@ -235,10 +246,11 @@ tree_attention_split_kernel(Args a) {
       const int piece = threadIdx.x + 64 * WAVES * j;
       const int key = piece & (BKEYS - 1), d0 = (piece / BKEYS) * 8;
       *reinterpret_cast<u32x4*>(&kt[key * KSTR + d0]) = kr[j];
+      const int slot = vslot(key);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        vt[(d0 + 2 * jj) * VSTR + key] = static_cast<uint16_t>(vr[j][jj] & 0xffffu);
-        vt[(d0 + 2 * jj + 1) * VSTR + key] = static_cast<uint16_t>(vr[j][jj] >> 16);
+        vt[(d0 + 2 * jj) * VSTR + slot] = static_cast<uint16_t>(vr[j][jj] & 0xffffu);
+        vt[(d0 + 2 * jj + 1) * VSTR + slot] = static_cast<uint16_t>(vr[j][jj] >> 16);
       }
     }
   };
@@ -292,8 +304,10 @@ tree_attention_split_kernel(Args a) {
     }
 
     // online softmax over the sub-block for the lane's query of each tile;
-    // the probabilities go to this wave's planes, four keys per store
+    // the probabilities are split into the A operands of the value product
+    // (chunk kk: keys of tiles 2 kk and 2 kk + 1, in vslot order)
     const bool all_keys = !scratch && p0 + BKEYS <= nkeys;
+    u32x4 pa[MTW][BKEYS / 32][3];
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
       float bm = -__builtin_inff();
@@ -313,51 +327,44 @@ tree_attention_split_kernel(Args a) {
       rm[i] = mn;
       float ps = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT_S; ++t) {
-        uint16_t h[4], md[4], l[4];
+      for (int kk = 0; kk < BKEYS / 32; ++kk) {
+        float pv[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp(s[i][t][e] - mn);  // 0 for masked keys
-          ps += p;
-          split3_one(p, h[e], md[e], l[e]);
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = fast_exp(s[i][2 * kk + j / 4][j % 4] - mn);  // 0 for masked keys
+          ps += pv[j];
         }
-        const int off = col * PSTR + t * 16 + 4 * grp;
-        *reinterpret_cast<uint2*>(&pl[w][i][0][off]) = uint2{h[0] | (uint32_t{h[1]} << 16), h[2] | (uint32_t{h[3]} << 16)};
-        *reinterpret_cast<uint2*>(&pl[w][i][1][off]) = uint2{md[0] | (uint32_t{md[1]} << 16), md[2] | (uint32_t{md[3]} << 16)};
-        *reinterpret_cast<uint2*>(&pl[w][i][2][off]) = uint2{l[0] | (uint32_t{l[1]} << 16), l[2] | (uint32_t{l[3]} << 16)};
+        split3(pv, pa[i][kk][0], pa[i][kk][1], pa[i][kk][2]);
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
       rl[i] = rl[i] * alpha + ps;
+      // the rescale factors of this lane's output queries 4 g + e
+      float ae[4];
 #pragma unroll
-      for (int t = 0; t < NT_O; ++t) o[i][t] *= alpha;
-    }
-    // the planes are this wave's own: its LDS writes complete before its reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // O^T += V^T P^T: A = V^T (dimension c of the tile, keys 32 kk + 8 g ..),
-    // B = the probability planes (query c, keys 32 kk + 8 g ..)
-#pragma unroll
-    for (int kk = 0; kk < BKEYS / 32; ++kk) {
-      const int k0 = kk * 32 + grp * 8;
-      u32x4 va[NT_O];
+      for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * grp + e, 64);
 #pragma unroll
       for (int t = 0; t < NT_O; ++t)
-        va[t] = *reinterpret_cast<const u32x4*>(&vt[(t * 16 + col) * VSTR + k0]);
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) {
-        const u32x4 ph = *reinterpret_cast<const u32x4*>(&pl[w][i][0][col * PSTR + k0]);
-        const u32x4 pm = *reinterpret_cast<const u32x4*>(&pl[w][i][1][col * PSTR + k0]);
-        const u32x4 pq = *reinterpret_cast<const u32x4*>(&pl[w][i][2][col * PSTR + k0]);
+        for (int e = 0; e < 4; ++e) o[i][t][e] *= ae[e];
+    }
+
+    // O += P V: A = the probability planes (query c, slots 32 kk + 8 g ..),
+    // B = V (slots 32 kk + 8 g .., dimension c of the tile)
+#pragma unroll
+    for (int kk = 0; kk < BKEYS / 32; ++kk) {
+      u32x4 vb[NT_O];
+#pragma unroll
+      for (int t = 0; t < NT_O; ++t)
+        vb[t] = *reinterpret_cast<const u32x4*>(&vt[(t * 16 + col) * VSTR + kk * 32 + grp * 8]);
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
 #pragma unroll
         for (int t = 0; t < NT_O; ++t) {
-          o[i][t] = mfma(va[t], ph, o[i][t]);
-          o[i][t] = mfma(va[t], pm, o[i][t]);
-          o[i][t] = mfma(va[t], pq, o[i][t]);
+          o[i][t] = mfma(pa[i][kk][0], vb[t], o[i][t]);
+          o[i][t] = mfma(pa[i][kk][1], vb[t], o[i][t]);
+          o[i][t] = mfma(pa[i][kk][2], vb[t], o[i][t]);
         }
-      }
     }
   }
 
@@ -365,12 +372,17 @@ tree_attention_split_kernel(Args a) {
   const int64_t base = (static_cast<int64_t>(split) * a.Hkv + g) * M;
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
-    const int m = (mt0 + w + WAVES * i) * 16 + col;
-    if (m >= M) continue;
-    float* dst = a.part_o + (base + m) * HD + 4 * grp;
+    const int mb = (mt0 + w + WAVES * i) * 16;
 #pragma unroll
-    for (int t = 0; t < NT_O; ++t) *reinterpret_cast<f32x4*>(dst + t * 16) = o[i][t];
-    if (grp == 0) {
+    for (int e = 0; e < 4; ++e) {
+      const int m = mb + 4 * grp + e;
+      if (m >= M) continue;
+      float* dst = a.part_o + (base + m) * HD + col;
+#pragma unroll
+      for (int t = 0; t < NT_O; ++t) dst[t * 16] = o[i][t][e];
+    }
+    const int m = mb + col;
+    if (m < M && grp == 0) {
       a.part_ml[(base + m) * 2] = rm[i];
       a.part_ml[(base + m) * 2 + 1] = rl[i];
     }
