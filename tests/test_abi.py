@@ -179,6 +179,26 @@ def test_tree_attention_rejects_before_launch():
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, None, 0, 8, 128, None) == 0    # nothing to copy
 
 
+def test_tree_attention_split_plan():
+    """The workspace holds (splits x KV heads x queries) partial results of
+    130 floats, so its size shows the plan: about 256 / KV heads context
+    splits of whole 64-key sub-blocks (one workgroup per CU), plus the
+    scratch slots' split."""
+    lib = vs.library()
+    per = lambda Hkv, M: Hkv * M * 130 * 4
+    # 3 x 8 tree, 32/8 heads (100 queries per KV head), context 2080: 33
+    # sub-blocks in 17 splits of two, plus the slots
+    assert lib.tree_attention_rows_workspace_bytes(25, 32, 8, 2080) == 18 * per(8, 100)
+    # 8000 positions (125 sub-blocks): 32 splits of four
+    assert lib.tree_attention_rows_workspace_bytes(9, 32, 8, 8000) == 33 * per(8, 36)
+    # 16 KV heads, 2000 positions: 16 splits of two
+    assert lib.tree_attention_rows_workspace_bytes(9, 32, 16, 2000) == 17 * per(16, 18)
+    # one KV head, 40000 positions (625 sub-blocks): 209 splits of three
+    assert lib.tree_attention_rows_workspace_bytes(5, 4, 1, 40000) == 210 * per(1, 20)
+    # no context: the slots' split alone
+    assert lib.tree_attention_rows_workspace_bytes(25, 32, 8, 0) == 1 * per(8, 100)
+
+
 def test_verify_window_rejects_before_launch():
     """The fused acceptance stage checks shapes, parameters and the workspace
     on the host (its workspace is topk_rows' at K = 64)."""

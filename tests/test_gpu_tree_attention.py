@@ -144,3 +144,14 @@ def test_random_trees_heads_and_contexts(seed):
     vs_long = np.concatenate([vs_, vs_[:, :2]], axis=1)
     got = run(q, kc, vc, ctx, ks_long, vs_long, parent, scale)
     check(got, q, kc, vc, ctx, ks_long, vs_long, parent, scale)
+
+
+@pytest.mark.parametrize("R,G,Hkv,ctx", [(9, 4, 8, 8000), (5, 4, 1, 40000), (9, 2, 16, 2000)])
+def test_long_contexts_walk_several_sub_blocks_per_split(R, G, Hkv, ctx):
+    """Long contexts: each split walks three or four 64-key sub-blocks (8000
+    positions over 8 KV heads, 40000 over one), the next in flight while the
+    current one is computed, and many splits are merged (210 for 40000)."""
+    g = np.random.default_rng(2400 + ctx)
+    parent = np.array([int(g.integers(-1, j)) if j > 0 else -1 for j in range(R - 1)], dtype=np.int32)
+    q, kc, vc, ks, vs_ = case(2410 + Hkv, R, G * Hkv, Hkv, ctx)
+    check(run(q, kc, vc, ctx, ks, vs_, parent, 0.07), q, kc, vc, ctx, ks, vs_, parent, 0.07)
