@@ -314,6 +314,7 @@ class VerifyPass:
 
 
 ACCEPT_REPS = 200
+GRAPH_SWEEP_R = (1, 4, 8, 9, 16, 17, 24)
 
 
 def time_region(torch, fn, steps, warmup):
@@ -682,22 +683,36 @@ def main():
     log(f"weights ready in {time.time() - t0:.1f}s")
     vp.setup_acceptance(synth, R)
 
-    step = vp.step
-    if args.graph:
+    def captured(fn):
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for _ in range(2):
-                vp.step()
+                fn()
         torch.cuda.current_stream().wait_stream(s)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            vp.step()
-        step = graph.replay
+            fn()
+        return graph
 
-    ms_step = time_region(torch, step, args.steps, args.warmup)
+    def captured_step():
+        return captured(vp.step)
+
+    graph = captured_step() if args.graph else None
+    step = graph.replay if args.graph else vp.step
+    ms_step = time_region(torch, step, args.steps, max(args.warmup, 30) if args.graph else args.warmup)
     step_bytes = vp.bytes_projections(R)
     log(f"step: {ms_step:.3f} ms")
+    # the other form of the same step: replayed as a HIP graph (or eager, under
+    # --graph).  The GPU idles while the host captures, and its clocks need
+    # ~30 steps to come back up, hence the longer warm-up.
+    if args.graph:
+        ms_step_other = time_region(torch, vp.step, args.steps, max(args.warmup, 30))
+    else:
+        graph = captured_step()
+        ms_step_other = time_region(torch, graph.replay, args.steps, max(args.warmup, 30))
+    del graph
+    log(f"step ({'eager' if args.graph else 'HIP graph'}): {ms_step_other:.3f} ms")
 
     # the projection kernel alone, for the roofline (same stream, HIP events)
     ms_proj = time_region(torch, lambda: vp.projections(R), args.steps, args.warmup)
@@ -709,12 +724,17 @@ def main():
     bytes_per_launch = step_bytes / vp.n_launches()
     achieved = bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
 
-    sweep, spread = {}, {}
+    sweep, spread, sweep_graph = {}, {}, {}
     if not args.no_sweep:
         for r in range(1, 25):
             ts = time_each(torch, lambda: vp.projections(r), max(10, args.steps // 2), 2)
             sweep[r] = float(np.median(ts))
             spread[r] = (float(np.min(ts)), float(np.max(ts)), len(ts))
+        # the same passes replayed as HIP graphs (launches recorded once)
+        for r in GRAPH_SWEEP_R:
+            g = captured(lambda: vp.projections(r))
+            sweep_graph[r] = float(np.median(time_each(torch, g.replay, 10, 30)))
+            del g
         log("sweep done")
     knee = None
     if sweep:
@@ -774,6 +794,7 @@ def main():
             "avg_launch_us": per_launch_ms * 1e3,
         },
         "ms_projections": ms_proj,
+        "ms_per_step_graph" if not args.graph else "ms_per_step_eager": ms_step_other,
         "ms_acceptance": ms_accept,
         "ms_acceptance_note": "verify_window, the whole acceptance stage of the window in two launches "
                               "(bit-identical to the separate calls, checked at setup); "
@@ -790,6 +811,7 @@ def main():
         "sweep_timing": "median of per-pass HIP-event times, "
                         f"{max(10, args.steps // 2)} passes after 2 warm-ups per R",
         "ms_per_pass_vs_R": {str(r): round(v, 4) for r, v in sweep.items()},
+        "ms_per_pass_graph_vs_R": {str(r): round(v, 4) for r, v in sweep_graph.items()},
         "ms_per_pass_min_max_vs_R": {str(r): [round(a, 4), round(b, 4)]
                                      for r, (a, b, _) in spread.items()},
         "gbs_vs_R": {str(r): round(vp.bytes_projections(r) / (v * 1e-3) / 1e9, 1)
