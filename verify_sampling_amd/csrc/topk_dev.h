@@ -508,11 +508,18 @@ __device__ __forceinline__ void merge_rank_write(MergeShared& sh, int c, int K, 
 // (keys >= v) are a prefix of its sorted list, so their positions in the
 // survivor list follow from one prefix sum of the per-lane counts over the
 // lanes (five ballots of the counts' bits), with no compaction rounds.
-// Returns false, having written only LDS, when a chunk may hold more
-// survivors than its entries read (all WIDE_READ survive, K > WIDE_READ) or
-// more than CAND survive; merge_row then takes its general path.
+// A chunk whose WIDE_READ entries all survive ("full") may hold more
+// survivors further down its list.  Only chunks with a maximum >= v can be
+// full, at most K of them, so when their unread entries fit WIDE_EXTRA loads
+// per lane (K (K - WIDE_READ) <= 64 WIDE_EXTRA: K <= 16) they are read in
+// one more round and their survivors appended.  This is what rows whose top
+// K crowds into the first chunks need (equal values, many -inf: ties go to
+// the lowest indices).  Returns false, having written only LDS, when full
+// chunks hold more than that or more than CAND keys survive; merge_row then
+// takes its general path.
 constexpr int WIDE_SLOTS = 3;
 constexpr int WIDE_READ = 8;
+constexpr int WIDE_EXTRA = 2;
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bool merge_row_wide(MergeShared& sh, const uint64_t* __restrict__ src, int chunks, int K,
@@ -545,7 +552,8 @@ __device__ __forceinline__ bool merge_row_wide(MergeShared& sh, const uint64_t* 
     total += n[s];
     full = full || n[s] == WIDE_READ;
   }
-  if (K > WIDE_READ && __ballot(full) != 0ull) return false;  // uniform
+  const bool any_full = K > WIDE_READ && __ballot(full) != 0ull;  // uniform
+  if (any_full && K * (K - WIDE_READ) > 64 * WIDE_EXTRA) return false;
   // exclusive prefix of total over the lanes (total <= 24: five bits)
   int pos = 0;
   count = 0;
@@ -561,6 +569,43 @@ __device__ __forceinline__ bool merge_row_wide(MergeShared& sh, const uint64_t* 
 #pragma unroll
     for (int j = 0; j < WIDE_READ; ++j)
       if (j < n[s]) sh.key[pos++] = e[s][j];
+  if (any_full) {
+    // the full chunks, in (slot, lane) order, listed in LDS (at most K)
+    int nf = 0;
+#pragma unroll
+    for (int s = 0; s < WIDE_SLOTS; ++s) {
+      const uint64_t bf = __ballot(n[s] == WIDE_READ);
+      if (n[s] == WIDE_READ) sh.cont[nf + static_cast<int>(lanes_below(bf))] = static_cast<uint32_t>(lane + 64 * s);
+      nf += __popcll(bf);
+    }
+    vs::wave_lds_sync();
+    // their entries WIDE_READ .. K - 1: entry q of the round is entry
+    // WIDE_READ + q % U of full chunk q / U
+    const int U = K - WIDE_READ;
+    if (nf * U > 64 * WIDE_EXTRA) return false;  // uniform; not reached while nf <= K
+    uint64_t x[WIDE_EXTRA];
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < WIDE_EXTRA; ++i) {
+      const int q = lane + 64 * i;
+      x[i] = 0ull;
+      if (q < nf * U) x[i] = src[static_cast<int64_t>(sh.cont[q / U]) * K + WIDE_READ + q % U];
+      t += x[i] != 0ull && x[i] >= v;
+    }
+    // appended after the first survivors: exclusive prefix of t (<= 2: two bits)
+    int pos2 = count, extra = 0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const uint64_t bb = __ballot((t >> b) & 1);
+      pos2 += static_cast<int>(lanes_below(bb)) << b;
+      extra += __popcll(bb) << b;
+    }
+    if (count + extra > CAND) return false;  // uniform
+#pragma unroll
+    for (int i = 0; i < WIDE_EXTRA; ++i)
+      if (x[i] != 0ull && x[i] >= v) sh.key[pos2++] = x[i];
+    count += extra;
+  }
   return true;
 }
 
