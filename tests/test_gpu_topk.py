@@ -225,3 +225,20 @@ def test_chunking_boundary(rows):
     x[1] = np.random.default_rng(1531).integers(0, 4, VOCAB).astype(np.float32)
     x[2, ::2] = np.nan
     compare_rows(x, 64, np.r_[0:4, rows - 2:rows])
+
+
+@pytest.mark.parametrize("K", [10, 12, 14, 16])
+def test_crowded_rows_read_full_chunks_to_the_end(K):
+    """Rows whose top K crowds into the first 1024-element chunks (equal
+    values, mostly -inf with a few numbers, a few distinct values over the
+    whole row): the merge reads those chunks past their first 8 entries in
+    one more round; the pool must still be the oracle's, byte for byte."""
+    V = VOCAB
+    g = np.random.default_rng(1540 + K)
+    x = logits(1541 + K, (4, V))
+    x[0, :] = np.float32(-3.5)
+    x[1, :] = -np.inf
+    x[1, g.choice(V, size=K // 2, replace=False)] = g.standard_normal(K // 2).astype(np.float32)
+    x[2] = g.integers(0, 3, V).astype(np.float32)
+    x[3, : 5 * 1024] = np.float32(1e4)   # five whole chunks of the row maximum
+    compare(x, K)
