@@ -42,6 +42,7 @@ __all__ = [
     "topk_planted_rows",
     "chain_greedy_case",
     "tree_greedy_case",
+    "tree_window",
     "torch_bf16_weights",
     "lookup_context",
     "LAYER_SHAPES",
@@ -143,6 +144,36 @@ def penalty_history(seed: int, vocab: int, prompt_len: int, emitted_len: int,
     if len(hot_tokens):
         ids[hot] = g.choice(np.asarray(hot_tokens, dtype=np.int64), size=int(hot.sum()))
     return ids.astype(np.int32)
+
+
+def tree_window(seed: int, vocab: int = VOCAB, branches: int = 3, depth: int = 8):
+    """A token tree's verify rows: branches x depth nodes under the root.
+
+    Node j = depth * b + d (branch b, depth d) hangs under the root (d = 0)
+    or node j - 1, and holds the b-th largest raw logit of its parent's row
+    (row 0 for the root, row j for node j - 1), raised by a random amount
+    that is larger on the lower branches, so that walks go deep.  Also a
+    2048 + 32 token history a quarter of which comes from the rows' top 64
+    ids, and uniforms [rows][2].  Returns (logits fp32 [n + 1][vocab],
+    ctx int32, tokens int32 [n], parent int32 [n], u fp32 [n + 1][2]).
+    """
+    g = rng(seed)
+    n = branches * depth
+    lg = logits(seed, (n + 1, vocab))
+    tokens = np.zeros(n, dtype=np.int32)
+    parent = np.zeros(n, dtype=np.int32)
+    for b in range(branches):
+        for d in range(depth):
+            j = depth * b + d
+            parent[j] = -1 if d == 0 else j - 1
+            prow = 0 if d == 0 else j
+            t = int(np.argsort(-lg[prow], kind="stable")[b])
+            tokens[j] = t
+            lg[prow, t] += np.float32(2.0 * (branches - b) * g.random())
+    hot = np.unique(np.argsort(-lg, axis=1)[:, :64])
+    ctx = penalty_history(seed + 1, vocab, 2048, 32, hot)
+    u = uniforms(seed + 2, (n + 1, 2))
+    return lg, ctx, tokens, parent, u
 
 
 def draft_candidates(seed: int, target_logits: np.ndarray, n_cand: int = 8, noise_std: float = 0.5):

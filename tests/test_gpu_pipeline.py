@@ -35,7 +35,8 @@ from oracle.penalty import penalize_dense, penalize_sparse
 from oracle.pipeline import acceptance_stage, draft_chain
 from oracle.policy import policy_row
 from oracle.topk import topk_rows as oracle_topk_rows
-from synth import LM_HEAD_SHAPE, draft_candidates, penalty_history, torch_bf16_weights, uniforms
+from synth import (LM_HEAD_SHAPE, draft_candidates, penalty_history, torch_bf16_weights, tree_window,
+                   uniforms)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -200,3 +201,52 @@ def decision_margin(want, drafts, u, temperature):
         margins.append(draw_margin(residual_weights(want["p_rows"][i], want["q_rows"][i]), u[i][1]))
     margins.append(draw_margin(want["p_rows"][-1][1], u[-1][1]))
     return min(margins)
+
+
+@pytest.mark.parametrize("seed,temperature", [(2050, 0.7), (2060, 0.7), (2070, 1.0), (2080, 0.0)])
+def test_lm_head_tree_window_stages(seed, temperature):
+    """The acceptance stage of a token tree through the C ABI: per-branch
+    penalties (penalize_tree_rows), the top-64 pool, the policy and the tree
+    walk (naive-sampling, or greedy at T = 0).  Every oracle stage fed the
+    GPU's output of the stage before must agree exactly, and the oracle's
+    composition (oracle.pipeline.tree_acceptance_stage) run on the same fp32
+    logits must emit the same tokens."""
+    from oracle.accept import accept_greedy_tree, accept_naive_tree
+    from oracle.penalty import penalize_tree_dense
+    from oracle.pipeline import tree_acceptance_stage
+
+    lg, ctx, tokens, parent, u = tree_window(seed, LM_HEAD_SHAPE[0])
+    cfg = dict(CFG, temperature=temperature)
+    L = torch.from_numpy(lg).to(DEV)
+    C, T, P = (torch.from_numpy(a).to(DEV) for a in (ctx, tokens, parent))
+    vs.penalize_tree_rows(L, C, T, P, **PEN)
+    pv, pi = vs.topk_rows(L, 64)
+    p = vs.sample_policy_rows(pv, pi, **cfg)
+    if temperature > 0:
+        tok, n = vs.spec_accept_rows(vs.ACCEPT_NAIVE_TREE, T[None, :], p[:3],
+                                     u=torch.from_numpy(u[None]).to(DEV), parent=P[None, :])
+    else:
+        tok, n = vs.spec_accept_rows(vs.ACCEPT_GREEDY_TREE, T[None, :], (pi, None, None), parent=P[None, :])
+    got_tokens = [int(t) for t in host(tok)[0, :int(host(n)[0])]]
+    pen, g_vals, g_ids = host(L), host(pv), host(pi)
+
+    want_pen = penalize_tree_dense(lg, ctx, tokens, parent, **PEN)
+    assert np.array_equal(want_pen.view(np.uint32), pen.view(np.uint32))
+    o_vals, o_ids = oracle_topk_rows(pen, 64)
+    assert np.array_equal(o_ids, g_ids)
+    assert np.array_equal(o_vals.view(np.uint32), g_vals.view(np.uint32))
+    d_ids, d_probs, d_len = (host(t) for t in p[:3])
+    rows = []
+    for r in range(25):
+        oi, op = policy_row(g_vals[r], g_ids[r], **cfg)
+        assert d_len[r] == len(oi), r
+        assert np.array_equal(d_ids[r, :len(oi)], oi), r
+        assert (ulp_diff_f32(d_probs[r, :len(oi)], op) <= 1).all(), r
+        rows.append((d_ids[r, :d_len[r]], d_probs[r, :d_len[r]]))
+    if temperature > 0:
+        assert got_tokens == accept_naive_tree(rows, tokens, parent, u)
+    else:
+        assert got_tokens == accept_greedy_tree(g_ids[:, 0], tokens, parent)
+    want = tree_acceptance_stage(lg, ctx, tokens, parent, u, **PEN, **cfg)
+    assert got_tokens == [int(t) for t in want["tokens"]], (got_tokens, want["tokens"])
+    print(f"seed {seed} T={temperature}: emitted {got_tokens}")

@@ -213,3 +213,124 @@ def test_control_drafter_ignores_its_drafts(monkeypatch):
     monkeypatch.setattr(pipeline, "penalize_sparse", ctx_only)
     d = pipeline.draft_chain(Q_IDS, Q_VALS, CTX, np.array([0.5, 0.5], np.float32), **draft_kw())
     assert [int(t) for t in d] != [1, 6]
+
+
+# ---- a token tree ([TREE] "Spend the budget on a tree, not a longer guess") ----
+#
+# Same vocabulary, penalties and context; three nodes: node 0 (token 1, under
+# the root), node 1 (token 6, under node 0), node 2 (token 3, under the root):
+# branches [1, 6] and [3].  Row histories (W = 4):
+#   row 0 (root)   H = [5, 2, 5, 7]
+#   row 1 (node 0) H = last 4 of ctx || [1]    = [2, 5, 7, 1]
+#   row 2 (node 1) H = last 4 of ctx || [1, 6] = [5, 7, 1, 6]
+#   row 3 (node 2) H = last 4 of ctx || [3]    = [2, 5, 7, 3]
+# Rows 0-2 are the chain's RAW rows with row 1's token-6 logit raised to 1,
+# so branch [1, 6] is the chain above; row 3 is penalised with its own
+# branch, not with the nodes numbered before it.
+
+TREE_TOKENS = np.array([1, 6, 3], dtype=np.int32)
+TREE_PARENT = np.array([-1, 0, -1], dtype=np.int32)
+TREE_RAW = np.array([
+    [0.5, 1.5, 1.0, 0.25, -1.0, 4.0, 0.0, 2.0],
+    [0.0, 3.0, 1.0, 0.25, -0.5, 0.5, 1.0, 0.0],
+    [1.0, 0.0, 0.0, 0.5, 0.25, 3.0, 2.0, -2.0],
+    [0.25, 0.5, 2.0, 1.0, 0.0, 0.75, -0.25, 0.5],
+], dtype=np.float32)
+# row 0: 5 (c=2): 2 - 1 = 1;  2: 1/2 - 3/4 = -1/4;  7: 1 - 3/4 = 1/4
+# row 1: 1: 3/2 - 3/4 = 3/4;  2: -1/4;  5: 1/4 - 3/4 = -1/2;  7: 0 - 3/4 = -3/4
+# row 2: 5: 3/4;  7: -4 - 3/4 = -19/4;  1: -3/4;  6: 1 - 3/4 = 1/4
+# row 3: 2: 1 - 3/4 = 1/4;  5: 3/8 - 3/4 = -3/8;  7: 1/4 - 3/4 = -1/2;  3: 1/2 - 3/4 = -1/4
+TREE_PENALIZED = np.array([
+    [0.5, 1.5, -0.25, 0.25, -1.0, 1.0, 0.0, 0.25],
+    [0.0, 0.75, -0.25, 0.25, -0.5, -0.5, 1.0, -0.75],
+    [1.0, -0.75, 0.0, 0.5, 0.25, 0.75, 0.25, -4.75],
+    [0.25, 0.5, 0.25, -0.25, 0.0, -0.375, -0.25, -0.5],
+], dtype=np.float32)
+TREE_POOL_IDS = np.array([[1, 5, 0, 3], [6, 1, 3, 0], [0, 5, 3, 4], [1, 0, 2, 4]], dtype=np.int32)
+
+
+def run_tree(temperature, u, top_k=2):
+    kw = dict(window=W, repeat=REP, presence=PRES, frequency=FREQ, top_k=top_k, top_p=1.0,
+              min_p=0.0, pool=POOL4)
+    return pipeline.tree_acceptance_stage(TREE_RAW, CTX, TREE_TOKENS, TREE_PARENT,
+                                          np.asarray(u, dtype=np.float32), temperature=temperature,
+                                          **kw)
+
+
+def check_tree(out):
+    np.testing.assert_array_equal(out["penalized"], TREE_PENALIZED)
+    np.testing.assert_array_equal(out["pool_ids"], TREE_POOL_IDS)
+
+
+def test_tree_greedy_by_hand():
+    out = run_tree(0.0, np.zeros((4, 2)))
+    check_tree(out)
+    # row argmax 1, 6, 0, 1: node 0 (1) agrees with the root, node 1 (6) with
+    # node 0's row, node 2 (3) does not; branch [1, 6], then row 2's argmax 0
+    assert [int(t) for t in out["tokens"]] == [1, 6, 0]
+    # on the raw rows the root's argmax (5) matches no child
+    assert int(np.argmax(TREE_RAW[0])) == 5
+
+
+# Naive-sampling walk at T = 1, top-2: root p = (1: 0.6225, 5: 0.3775),
+# node 0's row (6: 0.5622, 1: 0.4378), node 1's row (0: 0.5622, 5: 0.4378);
+# row r draws with u[r][1].
+TREE_WALKS = [
+    ([[0, 0.5], [0, 0.5], [0, 0.75], [0, 0]], [1, 6, 5]),   # down branch 0, then draw 5
+    ([[0, 0.5], [0, 0.5], [0, 0.25], [0, 0]], [1, 6, 0]),
+    ([[0, 0.7], [0, 0.0], [0, 0.0], [0, 0]], [5]),          # no child holds 5
+    ([[0, 0.5], [0, 0.9], [0, 0.0], [0, 0]], [1, 1]),       # node 0's row draws 1: no child
+]
+
+
+@pytest.mark.parametrize("u,want", TREE_WALKS)
+def test_tree_sampled_walk_by_hand(u, want):
+    out = run_tree(1.0, u)
+    check_tree(out)
+    assert [int(t) for t in out["tokens"]] == want
+
+
+def test_tree_second_branch_by_hand():
+    # top-4 at T = 1, root weights e^1.5, e^1, e^0.5, e^0.25 (cumulative 4.48,
+    # 7.20, 8.85, 10.13): u = 0.95 draws 3, node 2; its row (1: e^0.5, 0: e^0.25,
+    # 2: e^0.25, 4: 1) with u = 0.1 draws 1, which no child holds
+    out = run_tree(1.0, [[0, 0.95], [0, 0], [0, 0], [0, 0.1]], top_k=4)
+    check_tree(out)
+    assert [int(t) for t in out["tokens"]] == [3, 1]
+
+
+def test_tree_control_branches_as_one_chain(monkeypatch):
+    """Row r penalised with ctx || the nodes numbered before it (the tree read
+    as one chain) instead of its own branch's path: row 3 changes."""
+    def as_chain(logits, ctx, tokens, parent, window, repeat, presence, frequency):
+        return pipeline.penalize_dense(logits, ctx, tokens, window, repeat, presence, frequency)
+
+    monkeypatch.setattr(pipeline, "penalize_tree_dense", as_chain)
+    with pytest.raises(AssertionError):
+        check_tree(run_tree(0.0, np.zeros((4, 2))))
+
+
+def test_tree_control_pool_before_penalties(monkeypatch):
+    real_topk = pipeline.topk_rows
+
+    def pool_on_raw(pen, k):
+        _, ids = real_topk(TREE_RAW, k)
+        return np.take_along_axis(pen, ids, axis=1), ids
+
+    monkeypatch.setattr(pipeline, "topk_rows", pool_on_raw)
+    out = run_tree(0.0, np.zeros((4, 2)))
+    with pytest.raises(AssertionError):
+        check_tree(out)
+    assert [int(t) for t in out["tokens"]] != [1, 6, 0]
+
+
+def test_tree_control_walk_reads_the_wrong_rows(monkeypatch):
+    """The walk given node j's row where it should read row 1 + j."""
+    real = pipeline.accept_naive_tree
+
+    def shifted(p_rows, tokens, parent, u):
+        return real(p_rows[:1] + p_rows[2:] + p_rows[1:2], tokens, parent, u)
+
+    monkeypatch.setattr(pipeline, "accept_naive_tree", shifted)
+    u, want = TREE_WALKS[0]
+    assert [int(t) for t in run_tree(1.0, u)["tokens"]] != want
