@@ -54,7 +54,7 @@ enum vs_status {
                               fixed per-GPU area holds (topk_rows_noalloc)  */
 };
 
-#define VS_ABI_VERSION 4
+#define VS_ABI_VERSION 5
 #define VS_MAX_ROWS 24     /* verify rows R = k + 1 per projection call      */
 #define VS_POOL 64         /* width of the sampler's candidate pool          */
 #define VS_MAX_WINDOW 4096 /* longest penalty window                         */
@@ -358,6 +358,47 @@ int verify_window(float* logits, int64_t ld, int R, int V, const int32_t* ctx, i
                   int32_t* p_len, int32_t* q_dist_ids, float* q_dist_probs, int32_t* q_dist_len,
                   int32_t* out_tokens, int32_t* out_n, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * verify_tree_window: the acceptance stage of one token tree in two launches.
+ *   [TREE] "Spend the budget on a tree, not a longer guess": one verify pass
+ *   checks several branches sharing a prefix, each seeing only its
+ *   ancestors; [SD] §04 (each row penalised against its own history before
+ *   sampling), §03 (the pool and the policy); [PR] "Code map" (the
+ *   naive-sampling verify, walked down the tree).
+ *
+ * The same results, bit for bit, as the sequence
+ *   penalize_tree_rows(logits, NULL, ld, V, V, ctx, ctx_len, tokens, parent,
+ *                      R - 1, window, ...)
+ *   topk_rows(logits, ld, R, V, 64, pool_vals, pool_ids, 64, ...)
+ *   sample_policy_rows(pool_vals, pool_ids, 64, R, 64, policy..., p_ids,
+ *                      p_probs, p_len, 64, NULL, NULL)
+ *   spec_accept_rows(temperature > 0 ? VS_ACCEPT_NAIVE_TREE : VS_ACCEPT_GREEDY_TREE,
+ *                    1, R - 1, p_ids, p_probs, p_len, 64, R, NULL, NULL, NULL,
+ *                    1, 0, tokens, parent, u, out_tokens, out_n)
+ *   logits   fp32 [R][ld], penalised in place: row 0 (the root) against the
+ *            last `window` tokens of ctx, row 1 + j (node j) against the
+ *            last `window` of ctx followed by the tokens on the path from
+ *            the root down to node j (a parent outside [-1, child) ends the
+ *            path, as in penalize_tree_rows)
+ *   ctx      int32 [ctx_len]; tokens, parent int32 [R - 1] (device; parent
+ *            -1 = the root)
+ *   u        fp32 [R][2] in [0, 1) (sampled; may be NULL when greedy)
+ *   pool_vals, pool_ids [R][64]; p_ids, p_probs [R][64], p_len [R];
+ *   out_tokens [R] (entries past the count are -1), out_n [1].
+ *   1 <= R <= VS_MAX_DRAFTS + 1, 64 <= V <= VS_MAX_VOCAB, ld >= V; penalty
+ *   and policy parameters as for penalize_tree_rows and sample_policy_rows.
+ *   workspace: as for verify_window, verify_window_workspace_bytes(R, V)
+ *   bytes, 16-byte aligned, no initialisation needed, scratch after the call.
+ *   A VS_ERR_HIP from the second launch leaves the first one's writes in
+ *   place: the penalised logits and, for V <= 1024, the pools.
+ */
+int verify_tree_window(float* logits, int64_t ld, int R, int V, const int32_t* ctx, int ctx_len,
+                       const int32_t* tokens, const int32_t* parent, int window, float repeat,
+                       float presence, float frequency, float temperature, int top_k, float top_p,
+                       float min_p, const float* u, float* pool_vals, int32_t* pool_ids, int32_t* p_ids,
+                       float* p_probs, int32_t* p_len, int32_t* out_tokens, int32_t* out_n,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * tree_attention_rows: attention of a token tree's verify rows under the tree

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = vs.library()
-    assert lib.vs_abi_version() == 4
+    assert lib.vs_abi_version() == 5
     assert lib.vs_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.vs_status_string(code) != b"unknown status"
@@ -177,6 +177,33 @@ def test_tree_attention_rejects_before_launch():
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, FAKE, 11, 8, 128, None) == -2  # past the cache
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, FAKE, 3, 8, 12, None) == -2    # D % 8
     assert lib.tree_commit_kv(FAKE, FAKE, 100, 90, FAKE, FAKE, 25, None, 0, 8, 128, None) == 0    # nothing to copy
+
+
+def test_verify_tree_window_rejects_before_launch():
+    lib = vs.library()
+    V = 151936
+    ws = lib.verify_window_workspace_bytes(25, V)
+    base = dict(logits=FAKE, ld=V, R=25, V=V, ctx=FAKE, n_ctx=100, tokens=FAKE, parent=FAKE, window=64,
+                rep=1.1, pres=1.5, freq=0.2, T=0.7, top_k=20, top_p=0.95, min_p=0.05, u=FAKE, pv=FAKE, pi=FAKE,
+                di=FAKE, dp=FAKE, dl=FAKE, tok=FAKE, n=FAKE, ws=FAKE, nws=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.verify_tree_window(*a.values(), None)
+
+    assert call(logits=None) == -1
+    assert call(R=0) == -2
+    assert call(R=65) == -2                    # at most 64 rows (63 nodes)
+    assert call(V=63) == -2
+    assert call(ld=V - 1) == -2
+    assert call(parent=None) == -1             # nodes need their parents
+    assert call(tokens=None) == -1
+    assert call(u=None) == -1                  # sampled walk draws
+    assert call(window=5000) == -3
+    assert call(rep=0.0) == -3
+    assert call(T=float("nan")) == -3
+    assert call(nws=ws - 1) == -5
+    assert call(ctx=None) == -1
 
 
 def test_tree_attention_split_plan():

@@ -32,6 +32,7 @@ __all__ = [
     "spec_accept_rows",
     "verify_window",
     "verify_window_workspace_bytes",
+    "verify_tree_window",
     "choose_depth",
     "lookup_tree",
     "tree_attention_rows",
@@ -69,6 +70,7 @@ EXPORTED_SYMBOLS = (
     "spec_accept_rows",
     "verify_window_workspace_bytes",
     "verify_window",
+    "verify_tree_window",
     "tree_attention_rows_workspace_bytes",
     "tree_attention_rows",
     "tree_commit_kv",
@@ -106,6 +108,8 @@ _SIGNATURES = {
     "verify_window_workspace_bytes": ([I32, I32], SZ),
     "verify_window": ([P, I64, I32, I32, P, I32, P, I32, F32, F32, F32, P, P, I64, I32, P, F32, I32, F32,
                        F32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+    "verify_tree_window": ([P, I64, I32, I32, P, I32, P, P, I32, F32, F32, F32, F32, I32, F32, F32, P, P, P,
+                            P, P, P, P, P, P, SZ, P], I32),
     "tree_attention_rows_workspace_bytes": ([I32, I32, I32, I32], SZ),
     "tree_attention_rows": ([P, I32, I32, I32, P, P, I64, I32, P, P, I32, P, I32, F32, P, P, SZ, P], I32),
     "tree_commit_kv": ([P, P, I64, I32, P, P, I32, P, I32, I32, I32, P], I32),
@@ -617,6 +621,69 @@ def verify_window(logits, ctx, drafts, *, window, repeat, presence, frequency, t
                                  pv_ptr, pi_ptr, di_ptr, dp_ptr, dl_ptr, qdi_ptr, qdp_ptr, qdl_ptr,
                                  t_ptr, n_ptr, ws_ptr, ws_bytes, _stream(stream))
     _check(st, "verify_window")
+    return out
+
+
+def verify_tree_window(logits, ctx, tokens, parent, *, window, repeat, presence, frequency,
+                       temperature, top_k, top_p, min_p, u=None, out=None, workspace=None, stream=None):
+    """The acceptance stage of one token tree in two launches.
+
+    logits float32 [R][V] (row 0 the root, row 1 + j node j; penalised in
+    place, each row against the context and its own branch's path); ctx
+    int32 [n] and tokens, parent int32 [R - 1] 1-D device tensors (parent
+    -1 = the root).  Sampled (temperature > 0: the naive-sampling walk) also
+    needs u float32 [R][2]; greedy walks the tree by the rows' argmax.
+    Returns a dict: tokens int32 [R] (-1 past the count), n int32 [1],
+    pool_vals / pool_ids [R][64], p = (ids, probs, len).  out: an optional
+    dict of the same outputs, preallocated.
+    """
+    import torch
+
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise VerifySamplingError("logits must be a 2-D torch tensor [R][V]")
+    R, V = logits.shape
+    n = R - 1
+    dev = logits.device
+    l_ptr, ld = _mat(logits, "logits", R, V, torch.float32, dev)
+    c_ptr, n_ctx = _ids1d(ctx, "ctx", torch.int32, dev)
+    t_ptr, n_tok = _ids1d(tokens, "tokens", torch.int32, dev)
+    p_ptr, n_par = _ids1d(parent, "parent", torch.int32, dev)
+    if n_tok != n or n_par != n:
+        raise VerifySamplingError(f"a tree of {R} rows has {n} nodes: tokens {n_tok}, parent {n_par}")
+    sampled = float(temperature) > 0
+    u_ptr = _vec(u, "u", R * 2, torch.float32, dev) if sampled else None
+    if out is None:
+        out = dict(tokens=torch.empty((R,), dtype=torch.int32, device=dev),
+                   n=torch.empty((1,), dtype=torch.int32, device=dev),
+                   pool_vals=torch.empty((R, POOL), dtype=torch.float32, device=dev),
+                   pool_ids=torch.empty((R, POOL), dtype=torch.int32, device=dev),
+                   p=(torch.empty((R, POOL), dtype=torch.int32, device=dev),
+                      torch.empty((R, POOL), dtype=torch.float32, device=dev),
+                      torch.empty((R,), dtype=torch.int32, device=dev)))
+
+    def dense(t, name, rows, cols, dtype):
+        ptr = _vec(t, name, rows * cols, dtype, dev)
+        if tuple(t.shape) != (rows, cols):
+            raise VerifySamplingError(f"{name} must be [{rows}][{cols}], got {list(t.shape)}")
+        return ptr
+
+    to_ptr = _vec(out["tokens"], "tokens out", R, torch.int32, dev)
+    n_ptr = _vec(out["n"], "n", 1, torch.int32, dev)
+    pv_ptr = dense(out["pool_vals"], "pool_vals", R, POOL, torch.float32)
+    pi_ptr = dense(out["pool_ids"], "pool_ids", R, POOL, torch.int32)
+    p_ids, p_probs, p_len = out["p"]
+    di_ptr = dense(p_ids, "p_ids", R, POOL, torch.int32)
+    dp_ptr = dense(p_probs, "p_probs", R, POOL, torch.float32)
+    dl_ptr = _vec(p_len, "p_len", R, torch.int32, dev)
+    need = verify_window_workspace_bytes(R, V)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = _workspace(workspace, "workspace", dev)
+    st = library().verify_tree_window(l_ptr, ld, R, V, c_ptr, n_ctx, t_ptr, p_ptr, int(window), float(repeat),
+                                      float(presence), float(frequency), float(temperature), int(top_k),
+                                      float(top_p), float(min_p), u_ptr, pv_ptr, pi_ptr, di_ptr, dp_ptr, dl_ptr,
+                                      to_ptr, n_ptr, ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "verify_tree_window")
     return out
 
 

@@ -1,4 +1,5 @@
-// verify_window: the acceptance stage of one verify window in two launches.
+// verify_window: the acceptance stage of one verify window in two launches;
+// verify_tree_window: the same for a token tree.
 //
 // "Speculative decoding on RDNA": §04 (every verify row, and the draft's
 // candidates for it, penalised against H_i, the last W tokens of prompt ||
@@ -27,6 +28,15 @@
 // Both stages are latency-bound (one window is a few MB): the select stage's
 // cost is its waves' load latency and selection, the finish stage's a
 // single wave's dependent merge, policy and acceptance per row.
+//
+// A token tree ("One RDNA4 verify pass has slack for about two dozen
+// speculative tokens", "Spend the budget on a tree, not a longer guess":
+// several branches sharing a prefix, each attending only to its ancestors)
+// takes the same two launches as penalize_tree_rows, topk_rows,
+// sample_policy_rows and spec_accept_rows (naive-sampling or greedy tree
+// walk) would: row 0 is the root, row 1 + j node j, and each row's history
+// is the context followed by its own branch's path, which each select wave
+// builds in its lanes from the nodes' parents (loaded with the chunk).
 
 #include "accept_dev.h"
 #include "penalty_dev.h"
@@ -70,9 +80,12 @@ struct WinArgs {
   float* logits;  // [R][ld] target rows, penalised in place
   int64_t ld;
   int R;
-  History h;      // h.k = R - 1 drafts
+  History h;      // h.k = R - 1 drafts (a tree: its nodes' tokens)
+  const int32_t* parent;  // a tree: node j's parent (-1 = the root); null for a chain
   Penalty pen;
-  bool sampled;
+  int mode;       // the acceptance mode (VS_ACCEPT_*)
+  bool q_rows;    // the draft's candidates are penalised and scored (a sampled chain)
+  bool use_u;     // the acceptance draws
   const int32_t* q_ids;  // [k][q_ld], q_m candidates per row
   const float* q_vals;
   int64_t q_ld;
@@ -97,11 +110,55 @@ struct WinArgs {
   int chunks, lg_jp, lg_j2;
 };
 
-// The select stage's hook: the penalties of target row `row` on its history
-// tokens in [base, base + n).  Each distinct token is handled once, at its
-// first history position, with its count over the whole history, by the
-// lane that holds it (element j of lane l is chunk index 256 (j / 4) + 4 l +
-// j % 4), which also writes it back to the row with a device-coherent store.
+// The penalties of one row on its history tokens in [base, base + n).
+// tok(j0): the history token at position j0 + lane in each lane (-1 past the
+// history's hlen tokens); called with uniform j0 in uniform control flow.
+// Each distinct token is handled once, at its first history position, with
+// its count over the whole history, by the lane that holds it (element j of
+// lane l is chunk index 256 (j / 4) + 4 l + j % 4), which also writes it back
+// to the row with a device-coherent store.
+template <int NPL, class Tok>
+__device__ __forceinline__ void penalize_chunk(float (&x)[NPL], float* xrow, int base, int n, int hlen,
+                                               const Tok& tok, const Penalty& pen) {
+  const int lane = threadIdx.x & 63;
+  for (int h0 = 0; h0 < hlen; h0 += 64) {  // uniform
+    const int32_t t = tok(h0);
+    uint64_t inr = __ballot(t >= base && t < base + n);
+    while (inr) {  // uniform
+      const int src = __ffsll(static_cast<long long>(inr)) - 1;
+      inr &= inr - 1;
+      const int32_t tk = vs::bcast(t, src);
+      const int pos = h0 + src;
+      bool first = true;
+      int c = 0;
+      for (int g0 = 0; g0 < hlen; g0 += 64) {  // uniform
+        const int32_t tt = g0 == h0 ? t : tok(g0);
+        const uint64_t eq = __ballot(tt == tk);
+        c += __popcll(eq);
+        const int before = pos - g0;  // positions of this batch before pos
+        if (before > 0 && (before >= 64 ? eq : (eq & ((1ull << before) - 1ull))) != 0ull) first = false;
+      }
+      if (!first) continue;
+      const int li = tk - base;
+      const int owner = (li & 255) >> 2;
+      const int jreg = ((li >> 8) << 2) | (li & 3);
+      if (lane == owner) {
+        float nv = 0.f;
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) {
+          if (q == jreg) {  // uniform: no dynamic register index
+            x[q] = penalize_one(x[q], c, pen.rep, pen.pres, pen.freq);
+            nv = x[q];
+          }
+        }
+        __hip_atomic_store(xrow + tk, nv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before any reload of the chunk
+}
+
+// The select stage's hook for a chain: target row `row` against H_row.
 struct ChunkPenalty {
   History h;
   Penalty pen;
@@ -112,41 +169,56 @@ struct ChunkPenalty {
     const int lane = threadIdx.x & 63;
     int64_t start;
     const int hlen = h.span(row, start);
-    for (int h0 = 0; h0 < hlen; h0 += 64) {  // uniform
-      const int32_t t = h0 + lane < hlen ? h.token(start, h0 + lane) : -1;
-      uint64_t inr = __ballot(t >= base && t < base + n);
-      while (inr) {  // uniform
-        const int src = __ffsll(static_cast<long long>(inr)) - 1;
-        inr &= inr - 1;
-        const int32_t tk = vs::bcast(t, src);
-        const int pos = h0 + src;
-        bool first = true;
-        int c = 0;
-        for (int g0 = 0; g0 < hlen; g0 += 64) {  // uniform
-          const int32_t tt = g0 == h0 ? t : (g0 + lane < hlen ? h.token(start, g0 + lane) : -1);
-          const uint64_t eq = __ballot(tt == tk);
-          c += __popcll(eq);
-          const int before = pos - g0;  // positions of this batch before pos
-          if (before > 0 && (before >= 64 ? eq : (eq & ((1ull << before) - 1ull))) != 0ull) first = false;
-        }
-        if (!first) continue;
-        const int li = tk - base;
-        const int owner = (li & 255) >> 2;
-        const int jreg = ((li >> 8) << 2) | (li & 3);
-        if (lane == owner) {
-          float nv = 0.f;
-#pragma unroll
-          for (int q = 0; q < NPL; ++q) {
-            if (q == jreg) {  // uniform: no dynamic register index
-              x[q] = penalize_one(x[q], c, pen.rep, pen.pres, pen.freq);
-              nv = x[q];
-            }
-          }
-          __hip_atomic_store(xrow + tk, nv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    auto tok = [&](int j0) { return j0 + lane < hlen ? h.token(start, j0 + lane) : -1; };
+    penalize_chunk(x, xrow, base, n, hlen, tok, pen);
+  }
+};
+
+// The select stage's hook for a tree: row 0 against the context, row 1 + j
+// against the context followed by node j's path from the root.  parv, tokv:
+// lane i holds node i's parent and token (lanes past the nodes: -2, -1).
+// The path is walked up from node row - 1 while the parent index decreases
+// (a parent outside [-1, child) ends it, as in penalize_tree_rows), and its
+// tokens are placed root first in the lanes.
+struct ChunkPenaltyTree {
+  History h;
+  Penalty pen;
+  int row;
+  int32_t parv, tokv;
+  template <int NPL>
+  __device__ __forceinline__ void operator()(float (&x)[NPL], float* xrow, int base, int n) const {
+    if (h.window == 0) return;
+    const int lane = threadIdx.x & 63;
+    int len = 0;
+    if (row > 0) {  // uniform
+      int child = row - 1;
+      len = 1;
+      int q = __builtin_amdgcn_readlane(parv, child);
+      while (q > -1 && q < child) {  // indices strictly decrease: at most row steps
+        ++len;
+        child = q;
+        q = __builtin_amdgcn_readlane(parv, q);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before any reload of the chunk
+    int32_t pathv = -1;  // lane i: the path's token i
+    for (int s = len - 1, child = row - 1; s >= 0; --s) {
+      const int32_t tk = __builtin_amdgcn_readlane(tokv, child);
+      if (lane == s) pathv = tk;
+      child = __builtin_amdgcn_readlane(parv, child);
+    }
+    const int64_t total = static_cast<int64_t>(h.ctx_len) + len;
+    const int hlen = static_cast<int>(total < h.window ? total : h.window);
+    const int64_t start = total - hlen;
+    // every lane takes part in the shuffle: the path's tokens sit in other lanes
+    auto tok = [&](int j0) {
+      const int64_t pos = start + j0 + lane;
+      const int pi = static_cast<int>(pos - h.ctx_len);
+      const int32_t pt = __shfl(pathv, pi >= 0 && pi < 64 ? pi : 0, 64);
+      if (j0 + lane >= hlen) return -1;
+      const int32_t t = pos < h.ctx_len ? h.ctx[pos] : pt;
+      return (t >= 0 && t < h.V) ? t : -1;
+    };
+    penalize_chunk(x, xrow, base, n, hlen, tok, pen);
   }
 };
 
@@ -186,7 +258,7 @@ struct DraftShared {
   double run[64];
 };
 
-template <int NPL>
+template <int NPL, bool TREE>
 __global__ void __launch_bounds__(64 * WAVES)
 window_select_kernel(WinArgs a) {
   __shared__ union {
@@ -199,9 +271,18 @@ window_select_kernel(WinArgs a) {
   const int cunits = a.R * a.chunks;
   if (unit < cunits) {
     const int row = unit / a.chunks, chunk = unit - row * a.chunks;
-    chunk_unit<NPL, 4, true>(shared[w].chunk, a.logits, a.ld, row, chunk, a.h.V, WIN_K, a.chunks, a.ws,
-                             a.pool_vals, a.pool_ids, WIN_K, ChunkPenalty{a.h, a.pen, row});
-  } else if (a.sampled && unit < cunits + a.h.k) {
+    if constexpr (TREE) {
+      const int lane = threadIdx.x & 63;
+      const bool node = lane < a.h.k && a.h.window > 0;
+      const int32_t parv = node ? a.parent[lane] : -2;
+      const int32_t tokv = node ? a.h.drafts[lane] : -1;
+      chunk_unit<NPL, 4, true>(shared[w].chunk, a.logits, a.ld, row, chunk, a.h.V, WIN_K, a.chunks, a.ws,
+                               a.pool_vals, a.pool_ids, WIN_K, ChunkPenaltyTree{a.h, a.pen, row, parv, tokv});
+    } else {
+      chunk_unit<NPL, 4, true>(shared[w].chunk, a.logits, a.ld, row, chunk, a.h.V, WIN_K, a.chunks, a.ws,
+                               a.pool_vals, a.pool_ids, WIN_K, ChunkPenalty{a.h, a.pen, row});
+    }
+  } else if (a.q_rows && unit < cunits + a.h.k) {
     DraftShared& d = shared[w].draft;
     draft_row(a, unit - cunits, d.v, d.id, d.run);
   }
@@ -220,6 +301,7 @@ window_finish_kernel(WinArgs a) {
   __shared__ int32_t qlen[MAX_WIN_ROWS - 1];
   __shared__ float us[MAX_WIN_ROWS * 2];
   __shared__ int32_t dr[MAX_WIN_ROWS - 1];
+  __shared__ int32_t prt[MAX_WIN_ROWS - 1];  // a tree's parents
   __shared__ double run[FIN_WAVES][64];
   const int lane = threadIdx.x & 63;
   const int w = vs::wave_index();
@@ -234,19 +316,20 @@ window_finish_kernel(WinArgs a) {
   constexpr int QPRE = 2;
   int32_t qi_r[QPRE], ql_r[QPRE];
   float qp_r[QPRE];
-  const bool qm = a.sampled && lane < a.q_m;
+  const bool qm = a.q_rows && lane < a.q_m;
 #pragma unroll
   for (int t = 0; t < QPRE; ++t) {
     const int i = w + FIN_WAVES * t;
-    const bool live = a.sampled && i < k;
+    const bool live = a.q_rows && i < k;
     const int64_t off = static_cast<int64_t>(i) * a.q_ld + lane;
     qi_r[t] = live && qm ? a.q_dist_ids[off] : -1;
     qp_r[t] = live && qm ? a.q_dist_probs[off] : 0.f;
     ql_r[t] = live && lane == 0 ? a.q_dist_len[i] : 0;
   }
   const int tid = static_cast<int>(threadIdx.x);
-  const float u_r = a.sampled && tid < 2 * a.R ? a.u[tid] : 0.f;
+  const float u_r = a.use_u && tid < 2 * a.R ? a.u[tid] : 0.f;
   const int32_t d_r = tid < k ? a.h.drafts[tid] : 0;
+  const int32_t p_r = a.parent != nullptr && tid < k ? a.parent[tid] : -1;
 
   __shared__ int last;
   // one row per wave: the grid holds ceil(R / FIN_WAVES) workgroups
@@ -272,14 +355,17 @@ window_finish_kernel(WinArgs a) {
   }
   for (int t = 0; t < QSLOTS; ++t) {
     const int i = w + FIN_WAVES * t;
-    if (!(a.sampled && i < k)) break;  // uniform
+    if (!(a.q_rows && i < k)) break;  // uniform
     const int64_t off = static_cast<int64_t>(i) * a.q_ld + lane;
     qids[i][lane] = t < QPRE ? qi_r[t < QPRE ? t : 0] : (qm ? a.q_dist_ids[off] : -1);
     qprobs[i][lane] = t < QPRE ? qp_r[t < QPRE ? t : 0] : (qm ? a.q_dist_probs[off] : 0.f);
     if (lane == 0) qlen[i] = t < QPRE ? ql_r[t < QPRE ? t : 0] : a.q_dist_len[i];
   }
   if (tid < 2 * a.R) us[tid] = u_r;
-  if (tid < k) dr[tid] = d_r;
+  if (tid < k) {
+    dr[tid] = d_r;
+    prt[tid] = p_r;
+  }
   if (gridDim.x > 1) {  // uniform
     // More than one workgroup: each publishes its rows to the device and is
     // counted; the last to arrive reads the others' rows and accepts.  Each
@@ -306,8 +392,8 @@ window_finish_kernel(WinArgs a) {
   __syncthreads();
   if (w == 0) {
     const Dists d{&dids[0][0], &dprobs[0][0], dlen, WIN_K, k + 1, &qids[0][0], &qprobs[0][0], qlen, WIN_K, k};
-    accept_window(a.sampled ? VS_ACCEPT_SAMPLED : VS_ACCEPT_GREEDY, 0, k, d, dr, nullptr, us, a.out_tokens,
-                  a.out_n, run[0]);
+    accept_window(a.mode, 0, k, d, dr, a.parent != nullptr ? prt : nullptr, us, a.out_tokens, a.out_n,
+                  run[0]);
   }
 }
 
@@ -317,6 +403,20 @@ window_finish_kernel(WinArgs a) {
 size_t lists_bytes(int R, int V) {
   const Plan p = plan_for(R, V);
   return p.chunks <= 1 ? 0 : static_cast<size_t>(R) * p.chunks * WIN_K * sizeof(uint64_t);
+}
+
+template <bool TREE>
+int launch_window(const WinArgs& a, const Plan& p, int units, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((units + WAVES - 1) / WAVES)), block(64 * WAVES);
+  if (p.small)
+    window_select_kernel<16, TREE><<<grid, block, 0, stream>>>(a);
+  else
+    window_select_kernel<64, TREE><<<grid, block, 0, stream>>>(a);
+  int st = vs::check_launch();
+  if (st != VS_OK) return st;
+  window_finish_kernel<<<dim3(static_cast<unsigned>((a.R + FIN_WAVES - 1) / FIN_WAVES)), dim3(64 * FIN_WAVES), 0,
+                         stream>>>(a);
+  return vs::check_launch();
 }
 
 }  // namespace
@@ -367,8 +467,11 @@ extern "C" int verify_window(float* logits, int64_t ld, int R, int V, const int3
   a.R = R;
   // nothing to penalise without a window or a history (as penalize_rows)
   a.h = History{ctx, drafts, ctx_len, k, V, (ctx_len == 0 && k == 0) ? 0 : window};
+  a.parent = nullptr;
   a.pen = Penalty{repeat, presence, frequency};
-  a.sampled = sampled;
+  a.mode = sampled ? VS_ACCEPT_SAMPLED : VS_ACCEPT_GREEDY;
+  a.q_rows = sampled;
+  a.use_u = sampled;
   a.q_ids = q_ids;
   a.q_vals = q_vals;
   a.q_ld = q_ld;
@@ -398,13 +501,64 @@ extern "C" int verify_window(float* logits, int64_t ld, int R, int V, const int3
 
   const int units = R * p.chunks + (sampled ? k : 0);
   const dim3 grid(static_cast<unsigned>((units + WAVES - 1) / WAVES)), block(64 * WAVES);
-  if (p.small)
-    window_select_kernel<16><<<grid, block, 0, stream>>>(a);
-  else
-    window_select_kernel<64><<<grid, block, 0, stream>>>(a);
-  int st = vs::check_launch();
-  if (st != VS_OK) return st;
-  window_finish_kernel<<<dim3(static_cast<unsigned>((R + FIN_WAVES - 1) / FIN_WAVES)), dim3(64 * FIN_WAVES), 0,
-                         stream>>>(a);
-  return vs::check_launch();
+  return launch_window<false>(a, p, units, stream);
+}
+
+extern "C" int verify_tree_window(float* logits, int64_t ld, int R, int V, const int32_t* ctx, int ctx_len,
+                                  const int32_t* tokens, const int32_t* parent, int window, float repeat,
+                                  float presence, float frequency, float temperature, int top_k, float top_p,
+                                  float min_p, const float* u, float* pool_vals, int32_t* pool_ids,
+                                  int32_t* p_ids, float* p_probs, int32_t* p_len, int32_t* out_tokens,
+                                  int32_t* out_n, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!logits || !pool_vals || !pool_ids || !p_ids || !p_probs || !p_len || !out_tokens || !out_n)
+    return VS_ERR_NULL;
+  if (R < 1 || R > MAX_WIN_ROWS || V < WIN_K || V > VS_MAX_VOCAB || ld < V) return VS_ERR_SHAPE;
+  const int n = R - 1;  // tree nodes
+  if (ctx_len < 0) return VS_ERR_SHAPE;
+  if ((ctx_len > 0 && !ctx) || (n > 0 && (!tokens || !parent))) return VS_ERR_NULL;
+  if (window < 0 || window > VS_MAX_WINDOW) return VS_ERR_PARAM;
+  if (!(repeat > 0.f) || !__builtin_isfinite(repeat) || !__builtin_isfinite(presence) ||
+      !__builtin_isfinite(frequency))
+    return VS_ERR_PARAM;
+  if (__builtin_isnan(temperature) || __builtin_isinf(temperature) || __builtin_isnan(top_p) ||
+      __builtin_isnan(min_p))
+    return VS_ERR_PARAM;
+  const bool sampled = temperature > 0.f;
+  if (sampled && !u) return VS_ERR_NULL;
+  const size_t need = verify_window_workspace_bytes(R, V);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return VS_ERR_WORKSPACE;
+  if (need > 0 && !vs::aligned16(workspace)) return VS_ERR_ALIGN;
+
+  const Plan p = plan_for(R, V);
+  WinArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.R = R;
+  // nothing to penalise without a window or a history (as penalize_tree_rows)
+  a.h = History{ctx, tokens, ctx_len, n, V, (ctx_len == 0 && n == 0) ? 0 : window};
+  a.parent = parent != nullptr && n > 0 ? parent : nullptr;
+  a.pen = Penalty{repeat, presence, frequency};
+  a.mode = sampled ? VS_ACCEPT_NAIVE_TREE : VS_ACCEPT_GREEDY_TREE;
+  a.q_rows = false;
+  a.use_u = sampled;
+  a.q_ld = 1;
+  a.temperature = temperature;
+  a.k_eff = policy_k_eff(top_k);
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.u = u;
+  a.pool_vals = pool_vals;
+  a.pool_ids = pool_ids;
+  a.p_ids = p_ids;
+  a.p_probs = p_probs;
+  a.p_len = p_len;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n;
+  a.ws = static_cast<uint64_t*>(workspace);
+  a.counter = R > FIN_WAVES
+                  ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + lists_bytes(R, V))
+                  : nullptr;
+  a.chunks = p.chunks;
+  merge_reads(p.chunks, WIN_K, a.lg_jp, a.lg_j2);
+  return launch_window<true>(a, p, R * p.chunks, stream);
 }
