@@ -569,54 +569,76 @@ def tree_window_leg(torch, vs, synth, dev):
     """The acceptance stage of one token tree on LM-head rows: a 3 x 8 tree
     (25 rows of 151936 logits, branch tokens planted so that walks go deep),
     per-branch penalties over a 2048 + 32 token history (window 64), the
-    top-64 pool, the policy, and the naive-sampling tree walk: four C-ABI
-    calls with cached arguments, the mean of back-to-back calls (HIP
-    events).  The penalties work in place, so later calls see rows already
-    penalised; the work per call is the same."""
+    top-64 pool, the policy, and the naive-sampling tree walk, through
+    verify_tree_window (two launches) and as the four separate calls, both
+    with cached C-ABI arguments; the two give the same bits (checked here
+    once).  Times are the mean of back-to-back calls (HIP events).  The
+    penalties work in place, so later calls see rows already penalised; the
+    work per call is the same."""
     V = synth.LM_HEAD_SHAPE[0]
     lg, ctx, tokens, parent, u = synth.tree_window(8200, V)
     R, n = lg.shape[0], len(tokens)
-    L = torch.from_numpy(lg).to(dev)
+    src = torch.from_numpy(lg).to(dev)
     C, T, P = (torch.from_numpy(a).to(dev) for a in (ctx, tokens, parent))
     U = torch.from_numpy(u[None]).to(dev)
-    pv = torch.empty((R, 64), device=dev)
-    pi = torch.empty((R, 64), dtype=torch.int32, device=dev)
-    d_ids = torch.empty((R, 64), dtype=torch.int32, device=dev)
-    d_probs = torch.empty((R, 64), device=dev)
-    d_len = torch.empty((R,), dtype=torch.int32, device=dev)
-    tok = torch.empty((1, n + 1), dtype=torch.int32, device=dev)
-    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
-    nws = vs.topk_rows_workspace_bytes(R, V, 64)
-    ws = torch.empty(max(16, nws), dtype=torch.uint8, device=dev)
     lib = vs.library()
     pen = (PEN["window"], PEN["repeat"], PEN["presence"], PEN["frequency"])
     cfg = (CFG["temperature"], CFG["top_k"], CFG["top_p"], CFG["min_p"])
-    calls = [
-        (lib.penalize_tree_rows, (L.data_ptr(), None, V, V, V, C.data_ptr(), int(C.numel()), T.data_ptr(),
-                                  P.data_ptr(), n, *pen)),
-        (lib.topk_rows, (L.data_ptr(), V, R, V, 64, pv.data_ptr(), pi.data_ptr(), 64, ws.data_ptr(), nws)),
-        (lib.sample_policy_rows, (pv.data_ptr(), pi.data_ptr(), 64, R, 64, *cfg, d_ids.data_ptr(),
-                                  d_probs.data_ptr(), d_len.data_ptr(), 64, None, None)),
-        (lib.spec_accept_rows, (vs.ACCEPT_NAIVE_TREE, 1, n, d_ids.data_ptr(), d_probs.data_ptr(),
-                                d_len.data_ptr(), 64, R, None, None, None, 1, 0, T.data_ptr(), P.data_ptr(),
-                                U.data_ptr(), tok.data_ptr(), cnt.data_ptr())),
-    ]
 
-    def stage():
+    def buffers():
+        return dict(L=src.clone(), pv=torch.empty((R, 64), device=dev),
+                    pi=torch.empty((R, 64), dtype=torch.int32, device=dev),
+                    di=torch.empty((R, 64), dtype=torch.int32, device=dev), dp=torch.empty((R, 64), device=dev),
+                    dl=torch.empty((R,), dtype=torch.int32, device=dev),
+                    tok=torch.full((1, n + 1), -1, dtype=torch.int32, device=dev),
+                    cnt=torch.empty((1,), dtype=torch.int32, device=dev))
+
+    nws = max(vs.topk_rows_workspace_bytes(R, V, 64), vs.verify_window_workspace_bytes(R, V))
+    ws = torch.empty(max(16, nws), dtype=torch.uint8, device=dev)
+    b1, b2 = buffers(), buffers()
+    sep_calls = [
+        (lib.penalize_tree_rows, (b1["L"].data_ptr(), None, V, V, V, C.data_ptr(), int(C.numel()), T.data_ptr(),
+                                  P.data_ptr(), n, *pen)),
+        (lib.topk_rows, (b1["L"].data_ptr(), V, R, V, 64, b1["pv"].data_ptr(), b1["pi"].data_ptr(), 64,
+                         ws.data_ptr(), nws)),
+        (lib.sample_policy_rows, (b1["pv"].data_ptr(), b1["pi"].data_ptr(), 64, R, 64, *cfg, b1["di"].data_ptr(),
+                                  b1["dp"].data_ptr(), b1["dl"].data_ptr(), 64, None, None)),
+        (lib.spec_accept_rows, (vs.ACCEPT_NAIVE_TREE, 1, n, b1["di"].data_ptr(), b1["dp"].data_ptr(),
+                                b1["dl"].data_ptr(), 64, R, None, None, None, 1, 0, T.data_ptr(), P.data_ptr(),
+                                U.data_ptr(), b1["tok"].data_ptr(), b1["cnt"].data_ptr())),
+    ]
+    fused_args = (b2["L"].data_ptr(), V, R, V, C.data_ptr(), int(C.numel()), T.data_ptr(), P.data_ptr(), *pen,
+                  *cfg, U.data_ptr(), b2["pv"].data_ptr(), b2["pi"].data_ptr(), b2["di"].data_ptr(),
+                  b2["dp"].data_ptr(), b2["dl"].data_ptr(), b2["tok"].data_ptr(), b2["cnt"].data_ptr(),
+                  ws.data_ptr(), nws)
+
+    def separate():
         st = torch.cuda.current_stream().cuda_stream
-        for fn, a in calls:
+        for fn, a in sep_calls:
             status = fn(*a, st)
             if status != 0:
                 raise RuntimeError(f"tree acceptance call failed with status {status}")
 
-    stage()
+    def fused():
+        status = lib.verify_tree_window(*fused_args, torch.cuda.current_stream().cuda_stream)
+        if status != 0:
+            raise RuntimeError(f"verify_tree_window failed with status {status}")
+
+    separate()
+    fused()
     torch.cuda.synchronize()
-    emitted = int(cnt.item())
-    us = time_region(torch, stage, ACCEPT_REPS, 5) * 1e3
+    for key in ("L", "pv", "pi", "di", "dp", "dl", "tok", "cnt"):
+        if not torch.equal(b1[key].view(torch.int32), b2[key].view(torch.int32)):
+            raise RuntimeError(f"verify_tree_window differs from the separate calls in {key}")
+    emitted = int(b2["cnt"].item())
+    us = time_region(torch, fused, ACCEPT_REPS, 5) * 1e3
+    us_sep = time_region(torch, separate, ACCEPT_REPS, 5) * 1e3
     return {"config": f"3 x 8 tree ({R} rows of {V}), window {PEN['window']}, top-64 pool, "
                       f"T{CFG['temperature']}/top-k{CFG['top_k']}/top-p{CFG['top_p']}/min-p{CFG['min_p']}, "
                       "naive-sampling walk",
-            "us": round(us, 2), "us_note": f"mean of {ACCEPT_REPS} back-to-back stages of four calls (HIP events)",
+            "us": round(us, 2), "us_separate_calls": round(us_sep, 2),
+            "us_note": f"verify_tree_window (two launches) and the four separate calls, each the mean of "
+                       f"{ACCEPT_REPS} back-to-back stages (HIP events); same bits, checked at setup",
             "emitted_first_call": emitted}
 
 
@@ -805,7 +827,7 @@ def main():
     tree_attn = tree_attention_leg(torch, vs, synth, dev)
     log(f"tree attention: {tree_attn['us']} us ({tree_attn['frac_of_hbm_peak']} of peak)")
     tree_win = tree_window_leg(torch, vs, synth, dev)
-    log(f"tree acceptance stage: {tree_win['us']} us")
+    log(f"tree acceptance stage: {tree_win['us']} us ({tree_win['us_separate_calls']} us as four calls)")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -161,3 +161,60 @@ def test_fused_window_and_tree_attention_replay_equal_eager(window_state):
         for k in eager:
             assert np.array_equal(eager[k].view(np.uint8), got[k].view(np.uint8)), (rep, k)
         assert 1 <= int(eager["n"][0]) <= K_DRAFT + 1
+
+
+def test_tree_window_replays_equal_eager():
+    """verify_tree_window on a 2 x 4 tree (9 rows of 151936 logits: two
+    finish workgroups, so the arrival counter too) captured once and
+    replayed on fresh inputs: every replay equals the eager run bit for bit."""
+    from synth import tree_window
+
+    V = 151936
+    pen = dict(window=64, repeat=1.1, presence=1.5, frequency=0.2)
+    cfg = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
+
+    def inputs(seed):
+        lg, ctx, tokens, parent, u = tree_window(seed, V, branches=2, depth=4)
+        return dict(logits=lg, ctx=ctx, tokens=tokens, parent=parent, u=u)
+
+    bufs = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in inputs(2900).items()}
+    work = torch.empty_like(bufs["logits"])
+    R = work.shape[0]
+    ws = torch.empty(vs.verify_window_workspace_bytes(R, V), dtype=torch.uint8, device=DEV)
+    out = dict(tokens=torch.empty((R,), dtype=torch.int32, device=DEV),
+               n=torch.empty((1,), dtype=torch.int32, device=DEV),
+               pool_vals=torch.empty((R, 64), device=DEV),
+               pool_ids=torch.empty((R, 64), dtype=torch.int32, device=DEV),
+               p=(torch.empty((R, 64), dtype=torch.int32, device=DEV), torch.empty((R, 64), device=DEV),
+                  torch.empty((R,), dtype=torch.int32, device=DEV)))
+
+    def run():
+        work.copy_(bufs["logits"])  # penalised in place: every run starts from the inputs
+        vs.verify_tree_window(work, bufs["ctx"], bufs["tokens"], bufs["parent"], u=bufs["u"], out=out,
+                              workspace=ws, **pen, **cfg)
+
+    def snapshot():
+        flat = dict(work=work, tokens=out["tokens"], n=out["n"], pool_vals=out["pool_vals"],
+                    pool_ids=out["pool_ids"], p_ids=out["p"][0], p_probs=out["p"][1], p_len=out["p"][2])
+        return {k: host(v) for k, v in flat.items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+
+    for rep, seed in enumerate([2910, 2920, 2930]):
+        for k, v in inputs(seed).items():
+            bufs[k].copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        run()
+        eager = snapshot()
+        graph.replay()
+        got = snapshot()
+        for k in eager:
+            assert np.array_equal(eager[k].view(np.uint8), got[k].view(np.uint8)), (rep, k)
+        assert 1 <= int(eager["n"][0]) <= R
