@@ -45,6 +45,27 @@ def test_sizes_and_ragged_chunks(V, K):
     compare(x, K)
 
 
+@pytest.mark.parametrize("K", [64, 16, 1])
+def test_narrow_bands_and_minus_inf_thresholds(K):
+    """Rows whose thresholds take the search's corner cases: distinct values
+    packed within 2^-6 of each other (the first threshold's coarse bits
+    leave most of a chunk above it, so its search goes on to the low bits),
+    and chunks whose K-th largest group maximum is -inf (a threshold with
+    cleared low bits would fall among NaN patterns below -inf's key)."""
+    V = VOCAB
+    rng = np.random.default_rng(1510 + K)
+    x = np.empty((5, V), dtype=np.float32)
+    band = (np.float32(1.0) + rng.permutation(V).astype(np.float32) * np.float32(2.0 ** -23))
+    x[0] = band                                   # 1 + i * 2^-23, distinct, in [1, 1.02)
+    x[1] = -band                                  # the same band, negative
+    x[2] = -np.inf                                # a few finite values per 1024, the rest -inf
+    x[2, rng.choice(V, V // 200, replace=False)] = rng.standard_normal(V // 200).astype(np.float32)
+    x[3] = np.where(rng.random(V) < 0.5, np.float32(np.nan), np.float32(-np.inf))
+    x[3, rng.choice(V, 40, replace=False)] = np.float32(2.0)
+    x[4] = np.where(rng.random(V) < 0.5, band, np.float32(-np.inf))
+    compare(x, K)
+
+
 def test_special_rows():
     V = 5000
     x = logits(1504, (5, V))

@@ -13,6 +13,9 @@ constexpr int SMALL_CHUNK = 1024;    // elements per chunk for a few rows
 constexpr int LARGE_CHUNK = 4096;    // elements per chunk for batches
 constexpr int MAX_CHUNKS = VS_MAX_VOCAB / SMALL_CHUNK;
 constexpr int MERGE_LOADS = 24;      // candidates a merge lane reads in one round
+constexpr int COARSE_BIT = 16;      // first threshold searches: low value-key bits searched only
+constexpr int COARSE_SLACK = 8;     // while more than K + COARSE_SLACK keys are at or above
+constexpr uint32_t NEG_INF_KEY = 0x007fffffu;  // value key of -inf, the smallest of a number
 constexpr int SMALL_BATCH_UNITS = 2048;  // fewer 4096-chunks than this: small chunks
 
 struct WaveShared {
@@ -238,9 +241,16 @@ __device__ __forceinline__ void chunk_unit(WaveShared& sh, const float* __restri
     if ((GL - 3) % 2) m = max3f(m, x[GL * g + GL - 1], x[GL * g + GL - 1]);
     mk[g] = vs::value_key(__builtin_bit_cast(uint32_t, m));
   }
-  // two bits per step: the three candidates' counts are independent
+  // two bits per step: the three candidates' counts are independent.  Below
+  // bit COARSE_BIT the search goes on only while more than K + COARSE_SLACK
+  // maxima are at or above v: the threshold may stay a lower bound of the
+  // K-th largest maximum (at least K maxima at or above it), so the
+  // survivors still hold the top K, ranked exactly below, plus the few
+  // elements just under the K-th maximum, at about half the search.
   uint32_t v = 0;
+  int nv = 64 * GROUPS;  // maxima at or above v
   for (int bit = 30; bit >= 0; bit -= 2) {
+    if (bit < COARSE_BIT && nv <= K + COARSE_SLACK) break;  // uniform
     const uint32_t c1 = v | (1u << bit), c2 = v | (2u << bit), c3 = v | (3u << bit);
     int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
@@ -251,8 +261,20 @@ __device__ __forceinline__ void chunk_unit(WaveShared& sh, const float* __restri
       n2 += __popcll(b2);
       n3 += __popcll(b3);
     }
-    v = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : v));
+    if (n3 >= K) {
+      v = c3;
+      nv = n3;
+    } else if (n2 >= K) {
+      v = c2;
+      nv = n2;
+    } else if (n1 >= K) {
+      v = c1;
+      nv = n1;
+    }
   }
+  // below -inf's key only NaN patterns (no value key) lie: a cleared
+  // threshold there stands for -inf, which the same maxima reach
+  if (v != 0u && v < NEG_INF_KEY) v = NEG_INF_KEY;
 
   // 3: compaction: the elements above t and, of those equal to t, the ones
   // with the lowest chunk indices, until K are taken
@@ -366,7 +388,15 @@ __device__ __forceinline__ void chunk_unit(WaveShared& sh, const float* __restri
 // share the value key found, over the index halves of those ties.  When
 // the ties are exactly as many as needed the result is the value key with
 // a zero index half: the same keys, exactly K, are at or above it.
-template <int N>
+//
+// COARSE: below bit COARSE_BIT the search over the value keys goes on only
+// while more than K + COARSE_SLACK keys are at or above it; if it stops
+// there, the result is that value key with a zero index half: a lower bound
+// of the K-th largest key with at least K keys at or above it (0 if fewer
+// than K keys are non-zero), for callers that rank their survivors exactly.
+// Otherwise (every value bit searched: ties, or keys crowded within 2^-7)
+// the index halves are searched as without COARSE.
+template <int N, bool COARSE = false>
 __device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int K) {
   uint32_t hi[N], lo[N];
 #pragma unroll
@@ -387,7 +417,17 @@ __device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int
   }
   int top;
   uint32_t vh = common_prefix(la, lo_or, top);
+  int nv = 0;  // COARSE: non-zero keys at or above vh (at first all, which share its bits)
+  if constexpr (COARSE) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) nv += __popcll(__ballot(k[i] != 0ull));
+  }
+  bool stopped = false;  // COARSE: the search ended above bit 0
   for (int bit = (top | 1) - 1; bit >= 0; bit -= 2) {
+    if (COARSE && bit < COARSE_BIT && nv <= K + COARSE_SLACK) {  // uniform
+      stopped = true;
+      break;
+    }
     const uint32_t c1 = vh | (1u << bit), c2 = vh | (2u << bit), c3 = vh | (3u << bit);
     int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
@@ -400,8 +440,18 @@ __device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int
       n2 += __popcll(b2);
       n3 += __popcll(b3);
     }
-    vh = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : vh));
+    if (n3 >= K) {
+      vh = c3;
+      nv = n3;
+    } else if (n2 >= K) {
+      vh = c2;
+      nv = n2;
+    } else if (n1 >= K) {
+      vh = c1;
+      nv = n1;
+    }
   }
+  if (COARSE && stopped) return nv >= K ? static_cast<uint64_t>(vh) << 32 : 0ull;
   // index halves of the ties, 0 for the other keys (an index half is the
   // complement of an index below 2^31, so a real one is never 0)
   int above = 0, ties = 0;
@@ -540,7 +590,7 @@ __device__ __forceinline__ bool merge_row_wide(MergeShared& sh, const uint64_t* 
   uint64_t m[WIDE_SLOTS];
 #pragma unroll
   for (int s = 0; s < WIDE_SLOTS; ++s) m[s] = e[s][0];  // 0 for chunks past the row's
-  const uint64_t v = wave_kth_largest<WIDE_SLOTS>(m, K);
+  const uint64_t v = wave_kth_largest<WIDE_SLOTS, true>(m, K);
   int n[WIDE_SLOTS];
   int total = 0;
   bool full = false;
