@@ -51,6 +51,14 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // compares that make them issue back to back instead of queueing on one
 // condition register.
 __device__ __forceinline__ void pin3(uint64_t a, uint64_t b, uint64_t c) { asm volatile("" ::"s"(a), "s"(b), "s"(c)); }
+template <int N>
+__device__ __forceinline__ void pin_ballots(const uint64_t (&b)[N]) {
+  static_assert(N >= 1 && N <= 4, "ballots");
+  if constexpr (N == 1) asm volatile("" ::"s"(b[0]));
+  if constexpr (N == 2) asm volatile("" ::"s"(b[0]), "s"(b[1]));
+  if constexpr (N == 3) asm volatile("" ::"s"(b[0]), "s"(b[1]), "s"(b[2]));
+  if constexpr (N == 4) asm volatile("" ::"s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(b[3]));
+}
 
 // The bits every valid lane's value shares, as (prefix, top): prefix holds
 // the common bits above the highest bit in which two valid values differ,
@@ -241,35 +249,28 @@ __device__ __forceinline__ void chunk_unit(WaveShared& sh, const float* __restri
     if ((GL - 3) % 2) m = max3f(m, x[GL * g + GL - 1], x[GL * g + GL - 1]);
     mk[g] = vs::value_key(__builtin_bit_cast(uint32_t, m));
   }
-  // two bits per step: the three candidates' counts are independent.  Below
-  // bit COARSE_BIT the search goes on only while more than K + COARSE_SLACK
-  // maxima are at or above v: the threshold may stay a lower bound of the
-  // K-th largest maximum (at least K maxima at or above it), so the
-  // survivors still hold the top K, ranked exactly below, plus the few
-  // elements just under the K-th maximum, at about half the search.
+  // one bit per step, unrolled (a single wave runs this search, so its
+  // instruction count is its time).  Below bit COARSE_BIT the search goes on
+  // only while more than K + COARSE_SLACK maxima are at or above v: the
+  // threshold may stay a lower bound of the K-th largest maximum (at least
+  // K maxima at or above it), so the survivors still hold the top K, ranked
+  // exactly below, plus the few elements just under the K-th maximum.
   uint32_t v = 0;
   int nv = 64 * GROUPS;  // maxima at or above v
-  for (int bit = 30; bit >= 0; bit -= 2) {
-    if (bit < COARSE_BIT && nv <= K + COARSE_SLACK) break;  // uniform
-    const uint32_t c1 = v | (1u << bit), c2 = v | (2u << bit), c3 = v | (3u << bit);
-    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-    for (int g = 0; g < GROUPS; ++g) {
-      const uint64_t b1 = __ballot(mk[g] >= c1), b2 = __ballot(mk[g] >= c2), b3 = __ballot(mk[g] >= c3);
-      pin3(b1, b2, b3);
-      n1 += __popcll(b1);
-      n2 += __popcll(b2);
-      n3 += __popcll(b3);
-    }
-    if (n3 >= K) {
-      v = c3;
-      nv = n3;
-    } else if (n2 >= K) {
-      v = c2;
-      nv = n2;
-    } else if (n1 >= K) {
-      v = c1;
-      nv = n1;
+  for (int bit = 31; bit >= 0; --bit) {
+    if (bit < COARSE_BIT && nv <= K + COARSE_SLACK) break;  // uniform
+    const uint32_t c = v | (1u << bit);
+    uint64_t b[GROUPS];
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) b[g] = __ballot(mk[g] >= c);
+    pin_ballots(b);
+    int n = 0;
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) n += __popcll(b[g]);
+    if (n >= K) {
+      v = c;
+      nv = n;
     }
   }
   // below -inf's key only NaN patterns (no value key) lie: a cleared
@@ -423,32 +424,25 @@ __device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&k)[N], int
     for (int i = 0; i < N; ++i) nv += __popcll(__ballot(k[i] != 0ull));
   }
   bool stopped = false;  // COARSE: the search ended above bit 0
-  for (int bit = (top | 1) - 1; bit >= 0; bit -= 2) {
+  // one bit per step, unrolled, from the highest bit in which keys differ
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    if (bit > top) continue;  // uniform: a bit every key shares
     if (COARSE && bit < COARSE_BIT && nv <= K + COARSE_SLACK) {  // uniform
       stopped = true;
       break;
     }
-    const uint32_t c1 = vh | (1u << bit), c2 = vh | (2u << bit), c3 = vh | (3u << bit);
-    int n1 = 0, n2 = 0, n3 = 0;
+    const uint32_t c = vh | (1u << bit);
+    uint64_t b[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      uint32_t h = hi[i];
-      asm volatile("" : "+v"(h));  // keeps the compares of key i after those of key i - 1
-      const uint64_t b1 = __ballot(h >= c1), b2 = __ballot(h >= c2), b3 = __ballot(h >= c3);
-      pin3(b1, b2, b3);
-      n1 += __popcll(b1);
-      n2 += __popcll(b2);
-      n3 += __popcll(b3);
-    }
-    if (n3 >= K) {
-      vh = c3;
-      nv = n3;
-    } else if (n2 >= K) {
-      vh = c2;
-      nv = n2;
-    } else if (n1 >= K) {
-      vh = c1;
-      nv = n1;
+    for (int i = 0; i < N; ++i) b[i] = __ballot(hi[i] >= c);
+    pin_ballots(b);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) n += __popcll(b[i]);
+    if (n >= K) {
+      vh = c;
+      nv = n;
     }
   }
   if (COARSE && stopped) return nv >= K ? static_cast<uint64_t>(vh) << 32 : 0ull;
