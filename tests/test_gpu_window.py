@@ -30,12 +30,17 @@ CFG = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
 PEN = dict(window=64, repeat=1.1, presence=1.5, frequency=0.2)
 
 
-def make_case(seed, V, R, *, q_m=8, q_ld=None, ld=None, ctx_len=2080, planted=False, bad_ids=False):
+def make_case(seed, V, R, *, q_m=8, q_ld=None, ld=None, ctx_len=2080, planted=False, bad_ids=False,
+              plateau=False):
     """Seeded window inputs: target logits [R][ld] (V valid), history, drafts,
-    draft candidates [R-1][q_ld] (q_m valid), uniforms [R][2]."""
+    draft candidates [R-1][q_ld] (q_m valid), uniforms [R][2].  plateau: the
+    first 2048 logits of every row equal 100.0 (so the history's hot tokens
+    fall in chunks whose top K is selected by the exact path)."""
     k = R - 1
     ld = ld or V
     x = topk_planted_rows(seed, rows=R, vocab=V, K=64) if planted else logits(seed, (R, V))
+    if plateau:
+        x[:, :2048] = np.float32(100.0)
     lg = np.zeros((R, ld), dtype=np.float32)
     lg[:, :V] = x
     hot = np.unique(np.argsort(-np.nan_to_num(x, nan=-np.inf), axis=1)[:, :64])
@@ -133,6 +138,9 @@ CASES = {
     "planted_hard_rows": (3110, 151936, 4, dict(planted=True, bad_ids=True), {}, {}),
     "q_stride": (3120, 32000, 4, dict(q_m=5, q_ld=12, bad_ids=True), dict(window=2000), {}),
     "negative_penalties": (3130, 151936, 4, {}, dict(presence=-0.5, frequency=-0.25, repeat=0.8), {}),
+    # penalised history tokens lifted above a plateau: the chunk's exact path
+    # reads the survivors' bits back from the row after the penalties' stores
+    "plateau_lifted_history": (3140, 151936, 4, dict(plateau=True), dict(presence=-2.0, frequency=0.0, repeat=1.0), {}),
 }
 
 

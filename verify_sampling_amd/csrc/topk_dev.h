@@ -197,7 +197,8 @@ __device__ __forceinline__ void rank_and_write(WaveShared& sh, int c, int K, int
 //
 // pre(x, xrow, base, n) runs once the lane's values are loaded: a hook that
 // may change values of the chunk in the registers (and in X); CO: a hook
-// wrote into X, so the exact path's reload of survivors reads X coherently.
+// wrote into X, so the exact path waits for those stores and its reload of
+// survivors reads X coherently.
 struct NoPre {
   template <int NPL>
   __device__ __forceinline__ void operator()(float (&)[NPL], float*, int, int) const {}
@@ -323,6 +324,9 @@ __device__ __forceinline__ void chunk_unit(WaveShared& sh, const float* __restri
 
   const bool exact = count > CAND;
   if (exact) {
+    // CO: the hook's stores into X are complete before the survivors' bits
+    // are read back from it
+    if constexpr (CO) __builtin_amdgcn_s_waitcnt(0);
     // the exact K-th largest value key of the chunk, by the same bitwise
     // search over every element's value key (padding is NaN, value key 0,
     // and ranks after every valid element of that key), then the same

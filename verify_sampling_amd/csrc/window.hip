@@ -151,11 +151,11 @@ __device__ __forceinline__ void penalize_chunk(float (&x)[NPL], float* xrow, int
             nv = x[q];
           }
         }
+        // (chunk_unit waits for these stores before its exact path reloads the chunk)
         __hip_atomic_store(xrow + tk, nv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before any reload of the chunk
 }
 
 // The select stage's hook for a chain: target row `row` against H_row.
@@ -163,13 +163,14 @@ struct ChunkPenalty {
   History h;
   Penalty pen;
   int row;
+  int32_t t0;  // this lane's token of the history's first 64, loaded with the chunk
   template <int NPL>
   __device__ __forceinline__ void operator()(float (&x)[NPL], float* xrow, int base, int n) const {
     if (h.window == 0) return;
     const int lane = threadIdx.x & 63;
     int64_t start;
     const int hlen = h.span(row, start);
-    auto tok = [&](int j0) { return j0 + lane < hlen ? h.token(start, j0 + lane) : -1; };
+    auto tok = [&](int j0) { return j0 == 0 ? t0 : (j0 + lane < hlen ? h.token(start, j0 + lane) : -1); };
     penalize_chunk(x, xrow, base, n, hlen, tok, pen);
   }
 };
@@ -185,6 +186,7 @@ struct ChunkPenaltyTree {
   Penalty pen;
   int row;
   int32_t parv, tokv;
+  int32_t ctxv;  // lane i: context token ctx_len - 64 + i (-1 before the context), loaded with the chunk
   template <int NPL>
   __device__ __forceinline__ void operator()(float (&x)[NPL], float* xrow, int base, int n) const {
     if (h.window == 0) return;
@@ -209,13 +211,18 @@ struct ChunkPenaltyTree {
     const int64_t total = static_cast<int64_t>(h.ctx_len) + len;
     const int hlen = static_cast<int>(total < h.window ? total : h.window);
     const int64_t start = total - hlen;
-    // every lane takes part in the shuffle: the path's tokens sit in other lanes
+    // every lane takes part in the shuffles: the path's tokens sit in other
+    // lanes, and so does the context's tail when the history fits in 64
+    // tokens (all of its context tokens are then among the last 64)
+    const bool tail = hlen <= 64;  // uniform
     auto tok = [&](int j0) {
       const int64_t pos = start + j0 + lane;
       const int pi = static_cast<int>(pos - h.ctx_len);
       const int32_t pt = __shfl(pathv, pi >= 0 && pi < 64 ? pi : 0, 64);
+      const int ci = pi + 64;  // in [0, 64) for the context's last 64 positions
+      const int32_t ct = tail ? __shfl(ctxv, ci >= 0 && ci < 64 ? ci : 0, 64) : -1;
       if (j0 + lane >= hlen) return -1;
-      const int32_t t = pos < h.ctx_len ? h.ctx[pos] : pt;
+      const int32_t t = pos < h.ctx_len ? (tail ? ct : h.ctx[pos]) : pt;
       return (t >= 0 && t < h.V) ? t : -1;
     };
     penalize_chunk(x, xrow, base, n, hlen, tok, pen);
@@ -271,16 +278,21 @@ window_select_kernel(WinArgs a) {
   const int cunits = a.R * a.chunks;
   if (unit < cunits) {
     const int row = unit / a.chunks, chunk = unit - row * a.chunks;
+    const int lane = threadIdx.x & 63;
     if constexpr (TREE) {
-      const int lane = threadIdx.x & 63;
       const bool node = lane < a.h.k && a.h.window > 0;
       const int32_t parv = node ? a.parent[lane] : -2;
       const int32_t tokv = node ? a.h.drafts[lane] : -1;
+      const int ci = a.h.ctx_len - 64 + lane;
+      const int32_t ctxv = a.h.window > 0 && ci >= 0 ? a.h.ctx[ci] : -1;
       chunk_unit<NPL, 4, true>(shared[w].chunk, a.logits, a.ld, row, chunk, a.h.V, WIN_K, a.chunks, a.ws,
-                               a.pool_vals, a.pool_ids, WIN_K, ChunkPenaltyTree{a.h, a.pen, row, parv, tokv});
+                               a.pool_vals, a.pool_ids, WIN_K, ChunkPenaltyTree{a.h, a.pen, row, parv, tokv, ctxv});
     } else {
+      int64_t start = 0;
+      const int hlen = a.h.window > 0 ? a.h.span(row, start) : 0;
+      const int32_t t0 = lane < hlen ? a.h.token(start, lane) : -1;
       chunk_unit<NPL, 4, true>(shared[w].chunk, a.logits, a.ld, row, chunk, a.h.V, WIN_K, a.chunks, a.ws,
-                               a.pool_vals, a.pool_ids, WIN_K, ChunkPenalty{a.h, a.pen, row});
+                               a.pool_vals, a.pool_ids, WIN_K, ChunkPenalty{a.h, a.pen, row, t0});
     }
   } else if (a.q_rows && unit < cunits + a.h.k) {
     DraftShared& d = shared[w].draft;
