@@ -66,6 +66,63 @@ def test_narrow_bands_and_minus_inf_thresholds(K):
     compare(x, K)
 
 
+def random_rows(rng, rows, V):
+    """Rows of mixed kinds for the randomized parity test: ordinary logits,
+    narrow bands of distinct values, integers (many exact ties),
+    bf16-rounded values, mostly -inf, NaN mixes, plateaus with a few values
+    above them, and all-equal rows."""
+    x = np.empty((rows, V), dtype=np.float32)
+    for r in range(rows):
+        kind = int(rng.integers(0, 8))
+        if kind == 0:
+            row = rng.standard_normal(V).astype(np.float32) * np.float32(rng.uniform(0.5, 8.0))
+        elif kind == 1:
+            row = (np.float32(rng.uniform(-4, 4)) + rng.permutation(V).astype(np.float32)
+                   * np.float32(2.0 ** -int(rng.integers(16, 24))))
+        elif kind == 2:
+            row = rng.integers(-20, 20, size=V).astype(np.float32)
+        elif kind == 3:
+            b = rng.standard_normal(V).astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+            row = b.view(np.float32)
+        elif kind == 4:
+            row = np.full(V, -np.inf, dtype=np.float32)
+            n = int(rng.integers(0, min(V, 200) + 1))
+            row[rng.choice(V, n, replace=False)] = rng.standard_normal(n).astype(np.float32)
+        elif kind == 5:
+            row = rng.standard_normal(V).astype(np.float32)
+            row[rng.random(V) < rng.uniform(0.1, 0.9)] = np.nan
+            row[rng.random(V) < 0.05] = -np.inf
+        elif kind == 6:
+            row = np.full(V, np.float32(rng.uniform(-2, 2)), dtype=np.float32)
+            n = int(rng.integers(0, min(V, 100)))
+            row[rng.choice(V, n, replace=False)] += np.abs(rng.standard_normal(n)).astype(np.float32) + 1
+        else:
+            row = np.full(V, np.float32(rng.choice([0.0, -0.0, 1.5, -3.25])), dtype=np.float32)
+        x[r] = row
+    return x
+
+
+@pytest.mark.parametrize("seed", range(1520, 1544))
+def test_random_rows_against_oracle(seed):
+    """Seeded random sizes, K and row kinds; exact ids and value bits."""
+    rng = np.random.default_rng(seed)
+    V = int(rng.choice([64, 1000, 4096, 5000, 50257, 151936, 151936, 262144]))
+    K = int(rng.integers(1, min(V, 64) + 1))
+    rows = int(rng.integers(1, 16))
+    x = random_rows(rng, rows, V)
+    print(f"seed {seed}: rows={rows} V={V} K={K}", flush=True)
+    compare(x, K)
+
+
+@pytest.mark.parametrize("K", [64, 23])
+def test_random_rows_batched_against_oracle(K):
+    """64 rows of 151936 in mixed kinds: enough chunks for the 4096-element
+    chunk stage."""
+    rng = np.random.default_rng(1550 + K)
+    x = random_rows(rng, 64, VOCAB)
+    compare(x, K)
+
+
 def test_special_rows():
     V = 5000
     x = logits(1504, (5, V))
