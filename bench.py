@@ -187,8 +187,11 @@ class VerifyPass:
                                                    u=ud[i], **CFG)
             drafts[i] = drawn[0]
         self.drafts = drafts
-        self.ws = torch.empty(vs.topk_rows_workspace_bytes(R, self.vocab, 64), dtype=torch.uint8,
-                              device=dev)
+        # one workspace for the separate top-K call and for verify_window
+        # (which also needs an arrival counter above 8 rows)
+        self.ws = torch.empty(max(vs.topk_rows_workspace_bytes(R, self.vocab, 64),
+                                  vs.verify_window_workspace_bytes(R, self.vocab)),
+                              dtype=torch.uint8, device=dev)
         self.pool_v = torch.empty((R, 64), device=dev, dtype=torch.float32)
         self.pool_i = torch.empty((R, 64), device=dev, dtype=torch.int32)
         self.p_out = (torch.empty((R, 64), dtype=torch.int32, device=dev),
