@@ -358,7 +358,7 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
     return {"bytes": nbytes, "ms": round(ms, 4), "gbs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, warmup=1):
+def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=20, warmup=3):
     """Batched acceptance stage, one set of rows per window (config: vocab 4096, k = 3)."""
     R = k + 1
     g = torch.Generator(device=dev)
@@ -382,8 +382,9 @@ def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, war
              torch.empty((B * k,), dtype=torch.int32, device=dev),
              torch.empty((B * k,), dtype=torch.int32, device=dev))
     acc = (torch.empty((B, R), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+    acc_f = (torch.empty((B, R), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
 
-    def run():
+    def separate():
         vs.topk_rows(p_log, 64, pv, pi, ws_p)
         vs.sample_policy_rows(pv, pi, out=p_out, **CFG)
         vs.topk_rows(q_log, 64, qv, qi, ws_q)
@@ -391,10 +392,25 @@ def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=5, war
         drafts = q_out[3].view(B, k)
         vs.spec_accept_rows(vs.ACCEPT_SAMPLED, drafts, p_out[:3], q_out[:3], u=u, out=acc)
 
-    ms = time_region(torch, run, steps, warmup)
-    mean_emitted = float(acc[1].float().mean().item())
+    def fused():
+        vs.verify_windows(p_log, q_log, k, u_draft=ud, u=u, out=acc_f, **CFG)
+
+    # the one-launch stage gives the five calls' bits
+    separate()
+    fused()
+    torch.cuda.synchronize()
+    if not (torch.equal(acc[0], acc_f[0]) and torch.equal(acc[1], acc_f[1])):
+        raise RuntimeError("verify_windows differs from the separate calls")
+    ms = time_region(torch, fused, steps, warmup)
+    ms_sep = time_region(torch, separate, steps, warmup)
+    mean_emitted = float(acc_f[1].float().mean().item())
+    nbytes = (B * R + B * k) * vocab * 4  # every target and draft row read once
     return {"windows": B, "k": k, "vocab": vocab, "ms": ms,
             "rows_per_s": B * R / (ms * 1e-3), "windows_per_s": B / (ms * 1e-3),
+            "logit_bytes": nbytes, "gb_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel": "verify_windows (one launch)",
+            "ms_separate_calls": ms_sep, "rows_per_s_separate_calls": B * R / (ms_sep * 1e-3),
             "mean_emitted_per_window": mean_emitted}
 
 

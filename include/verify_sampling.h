@@ -54,7 +54,7 @@ enum vs_status {
                               fixed per-GPU area holds (topk_rows_noalloc)  */
 };
 
-#define VS_ABI_VERSION 5
+#define VS_ABI_VERSION 6
 #define VS_MAX_ROWS 24     /* verify rows R = k + 1 per projection call      */
 #define VS_POOL 64         /* width of the sampler's candidate pool          */
 #define VS_MAX_WINDOW 4096 /* longest penalty window                         */
@@ -304,6 +304,52 @@ int spec_accept_rows(int mode, int B, int k,
                      int q_ld, int64_t q_win_stride,
                      const int32_t* drafts, const int32_t* parent, const float* u,
                      int32_t* out_tokens, int32_t* out_n, hipStream_t stream);
+
+/*
+ * verify_windows: the sampled acceptance stage of B windows in one call,
+ * each window with its own k + 1 target rows and k full draft rows over a
+ * vocabulary of at most 4096 tokens (the batched sampling workload).
+ *   [SD] §03 "how hipfire does it": the 64-wide pool, then temperature,
+ *   top-k, min-p and top-p, the same policy for p and q; §03 steps 1-4: the
+ *   drafts are draws from q, each accepted with min(1, p/q), else the window
+ *   ends with a draw from the renormalised residual (p - q)+, and after k
+ *   acceptances comes a bonus draw from p.
+ *
+ * The same results, bit for bit, as the sequence
+ *   topk_rows(p_logits, ldp, B (k + 1), V, 64, pv, pi, 64, ...)
+ *   sample_policy_rows(pv, pi, 64, B (k + 1), 64, policy..., p_ids, p_probs,
+ *                      p_len, 64, NULL, NULL)
+ *   topk_rows(q_logits, ldq, B k, V, 64, qv, qi, 64, ...)
+ *   sample_policy_rows(qv, qi, 64, B k, 64, policy..., q_ids, q_probs,
+ *                      q_len, 64, u_draft, drafts)
+ *   spec_accept_rows(VS_ACCEPT_SAMPLED, B, k, p_ids, p_probs, p_len, 64,
+ *                    k + 1, q_ids, q_probs, q_len, 64, k, drafts, NULL, u,
+ *                    out_tokens, out_n)
+ * with the pools kept on chip: one launch for up to 1024 windows of k <= 3,
+ * else two (every row's distribution, then the acceptance).
+ *   p_logits fp32 [B (k + 1)][ldp]: window b's target row i is row
+ *            b (k + 1) + i; q_logits fp32 [B k][ldq], draft row i of window
+ *            b is row b k + i (may be NULL when k = 0).
+ *   u_draft  fp32 [B k] in [0, 1): the draw of each draft from its q row
+ *            (may be NULL when k = 0); u fp32 [B][k + 1][2] in [0, 1) as
+ *            for spec_accept_rows.
+ *   Outputs: drafts int32 [B k], the drafts drawn; p_ids, p_probs
+ *            [B (k + 1)][64], p_len [B (k + 1)], the target distributions;
+ *            q_ids, q_probs [B k][64], q_len [B k], the draft ones (the q
+ *            outputs and drafts may be NULL when k = 0); out_tokens int32
+ *            [B][k + 1] (entries past the count are -1), out_n int32 [B],
+ *            1 <= out_n[b] <= k + 1.
+ *   1 <= B <= 2^22, 0 <= k <= 15, 64 <= V <= 4096, ldp >= V, ldq >= V
+ *   (k > 0); policy parameters as for sample_policy_rows.  Needs no
+ *   workspace.  A VS_ERR_HIP from the second launch leaves the first one's
+ *   outputs (distributions and drafts) in place.
+ */
+int verify_windows(const float* p_logits, int64_t ldp, const float* q_logits, int64_t ldq,
+                   int B, int k, int V, float temperature, int top_k, float top_p, float min_p,
+                   const float* u_draft, const float* u, int32_t* drafts,
+                   int32_t* p_ids, float* p_probs, int32_t* p_len,
+                   int32_t* q_ids, float* q_probs, int32_t* q_len,
+                   int32_t* out_tokens, int32_t* out_n, hipStream_t stream);
 
 /*
  * verify_window: the whole acceptance stage of one chain window in two

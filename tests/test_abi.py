@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = vs.library()
-    assert lib.vs_abi_version() == 5
+    assert lib.vs_abi_version() == 6
     assert lib.vs_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.vs_status_string(code) != b"unknown status"
@@ -204,6 +204,38 @@ def test_verify_tree_window_rejects_before_launch():
     assert call(T=float("nan")) == -3
     assert call(nws=ws - 1) == -5
     assert call(ctx=None) == -1
+
+
+def test_verify_windows_rejects_before_launch():
+    lib = vs.library()
+    base = dict(p=FAKE, ldp=4096, q=FAKE, ldq=4096, B=16, k=3, V=4096, T=0.7, top_k=20, top_p=0.95,
+                min_p=0.05, ud=FAKE, u=FAKE, drafts=FAKE, pi=FAKE, pp=FAKE, pl=FAKE, qi=FAKE, qp=FAKE,
+                ql=FAKE, tok=FAKE, n=FAKE)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.verify_windows(*a.values(), None)
+
+    assert call(p=None) == -1
+    assert call(u=None) == -1
+    assert call(tok=None) == -1
+    assert call(q=None) == -1                  # drafts are drawn from q
+    assert call(ud=None) == -1
+    assert call(pi=None) == -1                 # every distribution output is required
+    assert call(ql=None) == -1
+    assert call(drafts=None) == -1
+    # without drafts the q side may be NULL (the shape is still checked first)
+    assert call(k=0, q=None, ud=None, drafts=None, qi=None, qp=None, ql=None, V=63) == -2
+    assert call(B=0) == -2
+    assert call(k=16) == -2                    # at most 15 drafts
+    assert call(k=-1) == -2
+    assert call(V=63) == -2                    # the pool needs 64 candidates
+    assert call(V=4097) == -2                  # one top-K chunk per row
+    assert call(ldp=4095) == -2
+    assert call(ldq=4095) == -2
+    assert call(T=float("nan")) == -3
+    assert call(T=float("inf")) == -3
+    assert call(top_p=float("nan")) == -3
 
 
 def test_tree_attention_split_plan():

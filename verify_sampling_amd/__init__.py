@@ -33,6 +33,7 @@ __all__ = [
     "verify_window",
     "verify_window_workspace_bytes",
     "verify_tree_window",
+    "verify_windows",
     "choose_depth",
     "lookup_tree",
     "tree_attention_rows",
@@ -71,6 +72,7 @@ EXPORTED_SYMBOLS = (
     "verify_window_workspace_bytes",
     "verify_window",
     "verify_tree_window",
+    "verify_windows",
     "tree_attention_rows_workspace_bytes",
     "tree_attention_rows",
     "tree_commit_kv",
@@ -110,6 +112,8 @@ _SIGNATURES = {
                        F32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
     "verify_tree_window": ([P, I64, I32, I32, P, I32, P, P, I32, F32, F32, F32, F32, I32, F32, F32, P, P, P,
                             P, P, P, P, P, P, SZ, P], I32),
+    "verify_windows": ([P, I64, P, I64, I32, I32, I32, F32, I32, F32, F32, P, P, P, P, P, P, P, P, P, P, P,
+                        P], I32),
     "tree_attention_rows_workspace_bytes": ([I32, I32, I32, I32], SZ),
     "tree_attention_rows": ([P, I32, I32, I32, P, P, I64, I32, P, P, I32, P, I32, F32, P, P, SZ, P], I32),
     "tree_commit_kv": ([P, P, I64, I32, P, P, I32, P, I32, I32, I32, P], I32),
@@ -444,6 +448,82 @@ def sample_policy_rows(vals, ids, *, temperature, top_k, top_p, min_p, u=None, o
                                       u_ptr, dr_ptr, _stream(stream))
     _check(st, "sample_policy_rows")
     return d_ids, d_probs, d_len, drawn
+
+
+def verify_windows(p_logits, q_logits, k, *, temperature, top_k, top_p, min_p, u_draft, u,
+                   drafts=None, p_dist=None, q_dist=None, out=None, stream=None):
+    """The sampled acceptance stage of B windows in one launch.
+
+    p_logits float32 [B * (k + 1)][V] (window b's target row i is row
+    b * (k + 1) + i), q_logits float32 [B * k][V] (draft row i of window b is
+    row b * k + i; None when k = 0), 64 <= V <= 4096, 0 <= k <= 15.
+    u_draft float32 [B * k] draws the drafts from q; u float32 [B][k + 1][2]
+    as for spec_accept_rows.  Outputs, allocated here when not given:
+    drafts int32 [B * k]; p_dist (ids int32, probs float32 [B * (k + 1)][64],
+    len int32 [B * (k + 1)]); q_dist likewise [B * k]; out (tokens int32
+    [B][k + 1], n int32 [B]).  Returns (tokens, n).
+    """
+    import torch
+
+    if not isinstance(p_logits, torch.Tensor) or p_logits.dim() != 2:
+        raise VerifySamplingError("p_logits must be a 2-D torch tensor")
+    k = int(k)
+    if k < 0 or k > 15:
+        raise VerifySamplingError(f"k must be in [0, 15], got {k}")
+    rows_p, V = p_logits.shape
+    if rows_p % (k + 1) != 0:
+        raise VerifySamplingError(f"p_logits rows ({rows_p}) must be a multiple of k + 1 = {k + 1}")
+    B = rows_p // (k + 1)
+    dev = p_logits.device
+    p_ptr, ldp = _mat(p_logits, "p_logits", B * (k + 1), V, torch.float32, dev)
+    if p_logits.shape[1] != V:
+        raise VerifySamplingError("p_logits must hold exactly V columns")
+    q_ptr, ldq = None, V
+    if k > 0:
+        if q_logits is None:
+            raise VerifySamplingError("q_logits is required when k > 0")
+        q_ptr, ldq = _mat(q_logits, "q_logits", B * k, V, torch.float32, dev)
+        if q_logits.shape[1] != V:
+            raise VerifySamplingError("q_logits must have as many columns as p_logits")
+    ud_ptr = _vec(u_draft, "u_draft", B * k, torch.float32, dev, allow_none=k == 0)
+    u_ptr = _vec(u, "u", B * (k + 1) * 2, torch.float32, dev)
+    if drafts is None:
+        drafts = torch.empty((B * k,), dtype=torch.int32, device=dev)
+    dr_ptr = _vec(drafts, "drafts", B * k, torch.int32, dev) if k > 0 else None
+
+    # outputs the caller leaves out are allocated here and held until the
+    # launch is enqueued (a freed block could be handed to the next output)
+    if p_dist is None:
+        p_dist = (torch.empty((B * (k + 1), POOL), dtype=torch.int32, device=dev),
+                  torch.empty((B * (k + 1), POOL), dtype=torch.float32, device=dev),
+                  torch.empty((B * (k + 1),), dtype=torch.int32, device=dev))
+    if q_dist is None and k > 0:
+        q_dist = (torch.empty((B * k, POOL), dtype=torch.int32, device=dev),
+                  torch.empty((B * k, POOL), dtype=torch.float32, device=dev),
+                  torch.empty((B * k,), dtype=torch.int32, device=dev))
+
+    def dist(d, name, rows):
+        if rows == 0:
+            return None, None, None
+        ids, probs, length = d
+        i_ptr = _vec(ids, f"{name}_ids", rows * POOL, torch.int32, dev)
+        p_ptr_ = _vec(probs, f"{name}_probs", rows * POOL, torch.float32, dev)
+        l_ptr = _vec(length, f"{name}_len", rows, torch.int32, dev)
+        return i_ptr, p_ptr_, l_ptr
+
+    pi, pp, pl = dist(p_dist, "p", B * (k + 1))
+    qi, qp, ql = dist(q_dist, "q", B * k)
+    if out is None:
+        out = (torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    tokens, n = out
+    t_ptr = _vec(tokens, "out_tokens", B * (k + 1), torch.int32, dev)
+    n_ptr = _vec(n, "out_n", B, torch.int32, dev)
+    st = library().verify_windows(p_ptr, ldp, q_ptr, ldq, B, k, V, float(temperature), int(top_k),
+                                  float(top_p), float(min_p), ud_ptr, u_ptr, dr_ptr, pi, pp, pl,
+                                  qi, qp, ql, t_ptr, n_ptr, _stream(stream))
+    _check(st, "verify_windows")
+    return tokens, n
 
 
 _TREE_MODES = (ACCEPT_GREEDY_TREE, ACCEPT_NAIVE_TREE)
