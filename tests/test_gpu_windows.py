@@ -219,3 +219,36 @@ def test_first_token_follows_p():
     qv, qi = topk_rows(q1[:1], 64)
     qids, qprobs = policy_row(qv[0], qi[0], **CFG)
     assert chi2_pvalue(first, qids, qprobs) < 1e-6
+
+
+def test_full_batch_sampled_windows_against_oracle():
+    """The bench's batch (16384 windows, k = 3, 4096 tokens, two launches):
+    byte-identical to the separate calls, and 40 seeded windows against the
+    oracle stage by stage."""
+    B, k, V = 16384, 3, 4096
+    print(f"verify_windows: full batch B {B} k {k} V {V}", flush=True)
+    p, q, u, ud = case(150, B, k, V, special=False)
+    P, Q, U, UD = dev(p), dev(q), dev(u), dev(ud)
+    want = separate(P, Q, k, V, U, UD, CFG)
+    got = fused(P, Q, k, V, U, UD, CFG)
+    for a, b in ((got[0], want[0]), (got[1], want[1]), (got[2], want[2])):
+        assert same(a, b)
+    for a, b in zip(got[3] + got[4], want[3] + want[4]):
+        assert same(a, b)
+    tok, n, drafts = host(got[0]), host(got[1]), host(got[2])
+    pd, qd = [tuple(host(t) for t in d) for d in (got[3], got[4])]
+    for b in rng(151).choice(B, size=40, replace=False):
+        p_rows, q_rows = [], []
+        for rows, dist, logit_rows in ((p_rows, pd, p[b * (k + 1):(b + 1) * (k + 1)]),
+                                       (q_rows, qd, q[b * k:(b + 1) * k])):
+            base = b * (k + 1) if rows is p_rows else b * k
+            vals, ids = topk_rows(logit_rows, 64)
+            for i in range(len(logit_rows)):
+                o_ids, o_probs = policy_row(vals[i], ids[i], **CFG)
+                L = int(dist[2][base + i])
+                assert L == len(o_ids) and np.array_equal(dist[0][base + i, :L], o_ids), (b, i)
+                assert ulp_diff_f32(dist[1][base + i, :L], o_probs).max() <= 1, (b, i)
+                rows.append((dist[0][base + i, :L], dist[1][base + i, :L]))
+        for i in range(k):
+            assert drafts[b * k + i] == q_rows[i][0][draw(q_rows[i][1], ud[b * k + i])], (b, i)
+        assert list(tok[b, :n[b]]) == accept_sampled(p_rows, q_rows, drafts[b * k:(b + 1) * k], u[b]), b
