@@ -218,3 +218,55 @@ def test_tree_window_replays_equal_eager():
         for k in eager:
             assert np.array_equal(eager[k].view(np.uint8), got[k].view(np.uint8)), (rep, k)
         assert 1 <= int(eager["n"][0]) <= R
+
+
+@pytest.mark.parametrize("B", [64, 2048])
+def test_batched_windows_replay_equal_eager(B):
+    """verify_windows (one launch at 64 windows, two at 2048) captured once
+    and replayed on fresh target and draft rows and uniforms: every replay
+    equals the eager run bit for bit."""
+    k, V = 3, 4096
+    cfg = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
+
+    def inputs(seed):
+        return dict(p=logits(seed, (B * (k + 1), V)), q=logits(seed + 1, (B * k, V)),
+                    u=uniforms(seed + 2, (B, k + 1, 2)), ud=uniforms(seed + 3, (B * k,)))
+
+    bufs = {n: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for n, v in inputs(3000).items()}
+    outs = dict(drafts=torch.empty((B * k,), dtype=torch.int32, device=DEV),
+                p=(torch.empty((B * (k + 1), 64), dtype=torch.int32, device=DEV),
+                   torch.empty((B * (k + 1), 64), device=DEV),
+                   torch.empty((B * (k + 1),), dtype=torch.int32, device=DEV)),
+                q=(torch.empty((B * k, 64), dtype=torch.int32, device=DEV), torch.empty((B * k, 64), device=DEV),
+                   torch.empty((B * k,), dtype=torch.int32, device=DEV)),
+                out=(torch.empty((B, k + 1), dtype=torch.int32, device=DEV),
+                     torch.empty((B,), dtype=torch.int32, device=DEV)))
+
+    def run():
+        vs.verify_windows(bufs["p"], bufs["q"], k, u_draft=bufs["ud"], u=bufs["u"], drafts=outs["drafts"],
+                          p_dist=outs["p"], q_dist=outs["q"], out=outs["out"], **cfg)
+
+    def snapshot():
+        flat = [outs["drafts"], *outs["p"], *outs["q"], *outs["out"]]
+        return [host(t) for t in flat]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+
+    for rep, seed in enumerate([3010, 3020, 3030]):
+        for n, v in inputs(seed).items():
+            bufs[n].copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        run()
+        eager = snapshot()
+        graph.replay()
+        got = snapshot()
+        for i, (a, b) in enumerate(zip(eager, got)):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (rep, i)
+        assert eager[-1].min() >= 1
