@@ -182,3 +182,26 @@ def test_tree_attention_rejects(T):
     raises(lambda: vs.tree_commit_kv(kc, kc, n - 3, ks, ks, z(2)))              # float path
     raises(lambda: vs.tree_commit_kv(kc, z(Hkv, n + 1, D, dtype=torch.bfloat16), n - 3, ks, ks,
                                      i(2)))                                     # cache shapes
+
+
+def test_batched_windows_reject(T):
+    torch, vs, z, i = T
+    B, k, V = 4, 3, 256
+    P, Q = z(B * (k + 1), V), z(B * k, V)
+    U, UD = z(B, k + 1, 2), z(B * k)
+    cfg = dict(temperature=0.7, top_k=20, top_p=0.95, min_p=0.05)
+    raises(lambda: vs.verify_windows(P[:-1], Q, k, u_draft=UD, u=U, **cfg))          # rows not B (k + 1)
+    raises(lambda: vs.verify_windows(P, Q[:-1], k, u_draft=UD, u=U, **cfg))          # draft rows short
+    raises(lambda: vs.verify_windows(P, z(B * k, V + 1), k, u_draft=UD, u=U, **cfg))  # vocab mismatch
+    raises(lambda: vs.verify_windows(P, None, k, u_draft=UD, u=U, **cfg))            # q needed
+    raises(lambda: vs.verify_windows(P, Q, k, u_draft=UD[:-1], u=U, **cfg))          # u_draft short
+    raises(lambda: vs.verify_windows(P, Q, k, u_draft=UD, u=U[:-1], **cfg))          # u short
+    raises(lambda: vs.verify_windows(P.double(), Q, k, u_draft=UD, u=U, **cfg))      # dtype
+    raises(lambda: vs.verify_windows(P, Q, 16, u_draft=UD, u=U, **cfg))              # k > 15
+    raises(lambda: vs.verify_windows(P, Q, k, u_draft=UD, u=U, drafts=i(B * k - 1), **cfg))
+    raises(lambda: vs.verify_windows(P, Q, k, u_draft=UD, u=U, p_dist=(i(B * (k + 1), 32), z(B * (k + 1), 64),
+                                                                     i(B * (k + 1))), **cfg))  # ids too small
+    raises(lambda: vs.verify_windows(P, Q, k, u_draft=UD, u=U, q_dist=(i(B * k, 64), z(B * k, 64), i(B * k - 1)),
+                                     **cfg))                                           # len too short
+    raises(lambda: vs.verify_windows(P, Q, k, u_draft=UD, u=U, out=(i(B, k), i(B)), **cfg))  # tokens short
+    raises(lambda: vs.verify_windows(P.cpu(), Q, k, u_draft=UD, u=U, **cfg))         # host tensor
