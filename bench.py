@@ -570,6 +570,7 @@ def cpu_baseline(synth, R, budget_s=8.0):
     t0 = time.perf_counter()
     oracle.pipeline.acceptance_stage(lg, ctx, drafts, u, q_ids=q_ids, q_vals=q_vals, **PEN, **CFG)
     acc_s = time.perf_counter() - t0
+    batched = oracle_batched_leg(synth)
     return {"value": allc["gbs"], "unit": "GB/s", "cores": allc["threads"], "kind": "oracle",
             "sample": f"fp64 projection oracle on one fused 8B-class layer (qkv, o, gate|up, "
                       f"down), repeated for ~{budget_s:.0f} s per leg ({allc['calls']} calls, "
@@ -581,7 +582,35 @@ def cpu_baseline(synth, R, budget_s=8.0):
             "single_thread": {"value": one["gbs"], "unit": "GB/s", "threads": one["threads"]},
             "seconds": allc["seconds"] + one["seconds"] + acc_s,
             "accept_window_ms": acc_s * 1e3,
-            "accept_rows_per_s": R / acc_s}
+            "accept_rows_per_s": R / acc_s,
+            "batched_sampling": batched}
+
+
+def oracle_batched_leg(synth, k=3, vocab=4096, budget_s=4.0):
+    """The oracle on windows of the batched sampling workload (k + 1 target
+    and k draft rows of `vocab` logits each: top-64 pool, policy, the
+    drafts' draws, sampled acceptance), single-threaded, for ~budget_s."""
+    import oracle
+
+    R = k + 1
+    windows, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        p = synth.logits(8200 + windows, (R, vocab))
+        q = synth.logits(8300 + windows, (k, vocab))
+        u = synth.uniforms(8400 + windows, (R, 2))
+        ud = synth.uniforms(8500 + windows, (k,))
+        pv, pi = oracle.topk.topk_rows(p, 64)
+        qv, qi = oracle.topk.topk_rows(q, 64)
+        p_rows = [oracle.policy.policy_row(pv[i], pi[i], **CFG) for i in range(R)]
+        q_rows = [oracle.policy.policy_row(qv[i], qi[i], **CFG) for i in range(k)]
+        drafts = [int(q_rows[i][0][oracle.policy.draw(q_rows[i][1], ud[i])]) for i in range(k)]
+        oracle.accept.accept_sampled(p_rows, q_rows, drafts, u)
+        windows += 1
+    secs = time.perf_counter() - t0
+    return {"windows": windows, "seconds": secs, "rows_per_s": windows * R / secs,
+            "windows_per_s": windows / secs, "threads": 1,
+            "sample": f"{windows} windows of k = {k} over {vocab} tokens (the GPU leg's `sampling` workload), "
+                      f"single-threaded Python"}
 
 
 def tree_window_leg(torch, vs, synth, dev):
