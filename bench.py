@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sampling", action="store_true")
+    ap.add_argument("--projections-only", action="store_true",
+                    help="time the step and the projection pass, then stop (profiler runs: "
+                         "the other legs add thousands of dispatches)")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -828,6 +831,12 @@ def main():
     ms_step = time_region(torch, step, args.steps, max(args.warmup, 30) if args.graph else args.warmup)
     step_bytes = vp.bytes_projections(R)
     log(f"step: {ms_step:.3f} ms")
+    if args.projections_only:
+        ms_proj = time_region(torch, lambda: vp.projections(R), args.steps, args.warmup)
+        print(json.dumps({"metric": "verify pass (projections only, a profiling run)", "rows": R,
+                          "layers": args.layers, "ms_per_step": ms_step, "ms_projections": ms_proj,
+                          "projection_gb_per_s": step_bytes / (ms_proj * 1e-3) / 1e9}), flush=True)
+        return
     # the other form of the same step: replayed as a HIP graph (or eager, under
     # --graph).  The GPU idles while the host captures, and its clocks need
     # ~30 steps to come back up, hence the longer warm-up.
