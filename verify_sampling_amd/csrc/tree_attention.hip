@@ -405,8 +405,12 @@ tree_attention_combine_kernel(const float* __restrict__ part_o, const float* __r
   __shared__ float lf[MAX_SPLITS];  // l_s * e^(m_s - M)
   __shared__ float wmax[HD / 64];
   const int M = G * R;
-  const int gm = blockIdx.x;  // g * M + m
-  const int g = gm / M, m = gm % M;
+  // query-major numbering: workgroup m * Hkv + g.  The split kernel's grid
+  // (Hkv, splits) puts every split of KV head g on XCD (g + Hkv s) % 8, g % 8
+  // when Hkv % 8 == 0 (workgroups are dealt to the eight XCDs round robin in
+  // launch order), and so does this numbering: the partial results are read
+  // from the L2 of the XCD that wrote them
+  const int g = static_cast<int>(blockIdx.x) % Hkv, m = static_cast<int>(blockIdx.x) / Hkv;
   const int d = threadIdx.x;
   auto stat = [&](int s) { return (static_cast<int64_t>(s) * Hkv + g) * M + m; };
   float pre[PRE];
