@@ -22,9 +22,8 @@
 //    as soon as their row is done.
 //  * Larger batches, and longer windows: two launches.  The rows: one wave
 //    per row in workgroups of four independent waves (no barrier), pool in
-//    LDS, distribution (and draft) to memory, each window's rows on the XCD
-//    of the workgroup that accepts it.  The acceptance: one wave per window,
-//    as spec_accept_rows.
+//    LDS, distribution (and draft) to memory.  The acceptance: one wave per
+//    window, as spec_accept_rows.
 // Why both (MI355X, k = 3, vocabulary 4096, back-to-back calls): one launch
 // took 28-32 us for 1-256 windows against 29-35 us for two, but 0.148 ms
 // against 0.116 for 4096 windows and 0.485-0.520 against 0.403-0.406 for
@@ -122,31 +121,19 @@ windows_kernel(WwArgs a) {
                 a.out_n + b, run[w]);
 }
 
-// Two launches, rows: one wave per target or draft row, four independent
-// waves per workgroup (no barrier).  The acceptance kernel's workgroup a
-// takes windows 4a .. 4a + 3, whose 4 (2k + 1) rows are exactly 2k + 1 row
-// workgroups; those are numbered so that they run on the same XCD as
-// acceptance workgroup a (XCD a % 8: workgroups are dealt to the eight XCDs
-// round robin in launch order), and the acceptance reads the distributions
-// and drafts from the L2 that they were written to.  Row workgroup id:
-// (8 (a / 8) (2k + 1) + 8 c + a % 8) for its chunk c of 4 rows; within a
-// window the rows are its k + 1 target rows, then its k draft rows.
+// Two launches, rows: one wave per target or draft row (target rows first),
+// four independent waves per workgroup (no barrier).
 __global__ void __launch_bounds__(64 * ROW_WAVES)
-windows_rows_kernel(WwArgs a, int B) {
+windows_rows_kernel(WwArgs a, int64_t p_rows, int64_t units) {
   __shared__ WaveShared sh[ROW_WAVES];
   __shared__ float pv[ROW_WAVES][WW_POOL];
   __shared__ int32_t pi[ROW_WAVES][WW_POOL];
   __shared__ double run[ROW_WAVES][64];
   const int w = vs::wave_index();
-  const int rows = 2 * a.k + 1;
-  const int j = static_cast<int>(blockIdx.x >> 3);
-  const int ag = (j / rows) * 8 + static_cast<int>(blockIdx.x & 7);  // acceptance workgroup
-  const int u = (j % rows) * ROW_WAVES + w;                           // row of its 4 windows
-  const int64_t b = static_cast<int64_t>(ag) * ROW_WAVES + u / rows;
-  if (b >= B) return;  // whole wave; no block-wide barriers
-  const int i = u % rows;
-  const bool draft = i > a.k;
-  const int64_t row = draft ? b * a.k + (i - a.k - 1) : b * (a.k + 1) + i;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * ROW_WAVES + w;
+  if (unit >= units) return;  // whole wave; no block-wide barriers
+  const bool draft = unit >= p_rows;
+  const int64_t row = draft ? unit - p_rows : unit;
   const float* xrow = draft ? a.q + row * a.ldq : a.p + row * a.ldp;
   chunk_unit<64, 4, false>(sh[w], xrow, 0, 0, 0, a.V, WW_POOL, 1, nullptr, pv[w], pi[w], WW_POOL, NoPre{});
   vs::wave_lds_sync();
@@ -192,9 +179,9 @@ extern "C" int verify_windows(const float* p_logits, int64_t ldp, const float* q
     windows_kernel<<<dim3(static_cast<unsigned>(B)), dim3(64 * rows), 0, stream>>>(a);
     return vs::check_launch();
   }
-  const int64_t groups = (static_cast<int64_t>(B) + ROW_WAVES - 1) / ROW_WAVES;  // acceptance workgroups
-  windows_rows_kernel<<<dim3(static_cast<unsigned>(((groups + 7) / 8) * 8 * rows)), dim3(64 * ROW_WAVES), 0,
-                        stream>>>(a, B);
+  const int64_t p_rows = static_cast<int64_t>(B) * (k + 1), units = p_rows + static_cast<int64_t>(B) * k;
+  windows_rows_kernel<<<dim3(static_cast<unsigned>((units + ROW_WAVES - 1) / ROW_WAVES)), dim3(64 * ROW_WAVES), 0,
+                        stream>>>(a, p_rows, units);
   int st = vs::check_launch();
   if (st != VS_OK) return st;
   windows_accept_kernel<<<dim3(static_cast<unsigned>((B + ROW_WAVES - 1) / ROW_WAVES)), dim3(64 * ROW_WAVES), 0,
