@@ -361,7 +361,7 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
     return {"bytes": nbytes, "ms": round(ms, 4), "gbs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=20, warmup=3):
+def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=10, warmup=2):
     """Batched acceptance stage, one set of rows per window (config: vocab 4096, k = 3)."""
     R = k + 1
     g = torch.Generator(device=dev)
@@ -404,8 +404,15 @@ def sampling_batch(torch, vs, synth, dev, B=16384, k=3, vocab=4096, steps=20, wa
     torch.cuda.synchronize()
     if not (torch.equal(acc[0], acc_f[0]) and torch.equal(acc[1], acc_f[1])):
         raise RuntimeError("verify_windows differs from the separate calls")
-    ms = time_region(torch, fused, steps, warmup)
-    ms_sep = time_region(torch, separate, steps, warmup)
+    # the two forms in alternating rounds (medians), after a long warm-up: in
+    # a fresh process the first timed steps run several percent slow
+    for _ in range(10):
+        fused()
+        separate()
+    rounds = [(time_region(torch, fused, steps, warmup), time_region(torch, separate, steps, warmup))
+              for _ in range(5)]
+    ms = float(np.median([r[0] for r in rounds]))
+    ms_sep = float(np.median([r[1] for r in rounds]))
     mean_emitted = float(acc_f[1].float().mean().item())
     nbytes = (B * R + B * k) * vocab * 4  # every target and draft row read once
     return {"windows": B, "k": k, "vocab": vocab, "ms": ms,
