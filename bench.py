@@ -861,6 +861,15 @@ def main():
     # latency before the first launch is not spread over only a few calls
     ms_accept = time_region(torch, vp.acceptance, ACCEPT_REPS, args.warmup)
     ms_accept_sep = time_region(torch, vp.acceptance_separate, ACCEPT_REPS, args.warmup)
+    # the same 200 calls replayed as one HIP graph: the GPU's time per stage
+    # without the host's per-call launch work (the eager figure above can be
+    # bound by the host issuing 200 calls of 34 arguments each)
+    def accept_batch():
+        for _ in range(ACCEPT_REPS):
+            vp.acceptance()
+    g_acc = captured(accept_batch)
+    ms_accept_graph = float(np.median(time_each(torch, g_acc.replay, 10, 30))) / ACCEPT_REPS
+    del g_acc
     per_launch_ms = ms_proj / vp.n_launches()
     bytes_per_launch = step_bytes / vp.n_launches()
     achieved = bytes_per_launch / (per_launch_ms * 1e-3) / 1e9
@@ -942,8 +951,10 @@ def main():
         "ms_acceptance_note": "verify_window, the whole acceptance stage of the window in two launches "
                               "(bit-identical to the separate calls, checked at setup); "
                               "ms_acceptance_separate_calls: the same stage as seven library calls; "
-                              f"both the mean of {ACCEPT_REPS} back-to-back calls (HIP events)",
+                              f"both the mean of {ACCEPT_REPS} back-to-back calls (HIP events); "
+                              "ms_acceptance_graph: the same calls replayed as one HIP graph (no host launch work)",
         "ms_acceptance_separate_calls": ms_accept_sep,
+        "ms_acceptance_graph": ms_accept_graph,
         "verify_rows_per_s": R / (ms_step * 1e-3),
         "emitted_tokens_per_s": (sampling["mean_emitted_per_window"] / (ms_step * 1e-3)
                                  if sampling else None),
